@@ -1,0 +1,204 @@
+"""fp64 CPU oracle of the TriAttention online KV-eviction pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product library never links,
+loads or calls it, and it shares no code with the HIP path: the arithmetic
+lives in ``tri_oracle.c`` (plain C99, fp64, literal steps) and this module only
+marshals numpy arrays into it.
+
+Sources: the "TriAttention" paper review on romaanj.github.io (section
+"Method", figure 4 caption) and the "TriAttention ... Review" on
+dimensionstp.github.io (sections 2-2 and 3-2).  The C file's header lists
+the readings taken where the pages leave a step open.
+
+Pinned by ``tests/test_oracle_pins.py`` against brute-force RoPE dot products,
+the pages' polar per-band form, closed-form special cases, hand-worked
+fixtures, library sorts, brute-force subset search and invariants;
+``tests/test_oracle_mutants.py`` checks that planted mistakes fail those pins.
+Whole-score parity with the authors' own implementation is unpinned (the
+pages print no worked example, and the norm-term weight is a reading).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "tri_oracle.c")
+LIBRARY = os.path.join(_HERE, "libtri_oracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def compile_c(src: str, out: str) -> str:
+    """gcc, plain C99, -O2, no fast-math."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-std=c99", "-O2", "-fPIC", "-shared",
+                           "-Wall", "-Wextra", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+        compile_c(SOURCE, LIBRARY)
+    return LIBRARY
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i64(a):
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        lib = ctypes.CDLL(path)
+        lib.tri_oracle_omega.restype = ctypes.c_double
+        lib.tri_oracle_omega.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double]
+        lib.tri_oracle_unrotate.restype = None
+        lib.tri_oracle_unrotate.argtypes = [ctypes.c_int, _dp, ctypes.c_int64, _dp, _dp, _dp]
+        lib.tri_oracle_score_head.restype = None
+        lib.tri_oracle_score_head.argtypes = [
+            ctypes.c_int, ctypes.c_int, _dp, _i64p, ctypes.c_int64, _dp, _i64p,
+            ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.tri_oracle_bound_head.restype = None
+        lib.tri_oracle_bound_head.argtypes = [
+            ctypes.c_int, ctypes.c_int, _dp, _dp, _i64p, ctypes.c_int,
+            _dp, _dp, _dp, _dp, _dp]
+        lib.tri_oracle_select_head.restype = ctypes.c_int
+        lib.tri_oracle_select_head.argtypes = [
+            ctypes.c_int, _dp, _i64p, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.tri_oracle_gather_rows.restype = None
+        lib.tri_oracle_gather_rows.argtypes = [
+            ctypes.c_int, _i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        self.lib = lib
+        self.path = path
+
+    def omega(self, head_dim: int, rope_theta: float) -> np.ndarray:
+        """Band frequencies w_f = theta^(-2f/d), f < d/2 (standard RoPE; reading)."""
+        return np.array([self.lib.tri_oracle_omega(f, head_dim, float(rope_theta))
+                         for f in range(head_dim // 2)], dtype=np.float64)
+
+    def unrotate(self, K_row, p: int, om) -> np.ndarray:
+        """Pre-RoPE complex bands of one stored key row at position ``p``."""
+        K_row = _f64(K_row)
+        om = _f64(om)
+        d = K_row.shape[0]
+        re = np.empty(d // 2)
+        im = np.empty(d // 2)
+        self.lib.tri_oracle_unrotate(d, _ptr(K_row, _dp), int(p), _ptr(om, _dp),
+                                     _ptr(re, _dp), _ptr(im, _dp))
+        return re + 1j * im
+
+    def score_head(self, K, pos, p_now, om, offsets, qc_re, qc_im, q_mean_norm, q_mrl):
+        """Returns (trig, norm, score), each fp64 [n], for one (layer, KV head).
+
+        ``K`` is [n][d] stored post-RoPE key rows (any float dtype; upcast
+        exactly to fp64), ``pos`` [n] their positions.
+        """
+        K = _f64(K)
+        n, d = K.shape
+        pos = _i64(pos)
+        om = _f64(om)
+        offsets = _i64(offsets)
+        qc_re, qc_im, q_mean_norm, q_mrl = (_f64(x) for x in (qc_re, qc_im, q_mean_norm, q_mrl))
+        assert pos.shape == (n,) and om.shape == (d // 2,)
+        for x in (qc_re, qc_im, q_mean_norm, q_mrl):
+            assert x.shape == (d // 2,)
+        trig = np.empty(n)
+        norm = np.empty(n)
+        score = np.empty(n)
+        self.lib.tri_oracle_score_head(
+            d, n, _ptr(K, _dp), _ptr(pos, _i64p), int(p_now), _ptr(om, _dp),
+            _ptr(offsets, _i64p), len(offsets), _ptr(qc_re, _dp), _ptr(qc_im, _dp),
+            _ptr(q_mean_norm, _dp), _ptr(q_mrl, _dp),
+            _ptr(trig, _dp), _ptr(norm, _dp), _ptr(score, _dp))
+        return trig, norm, score
+
+    def bound_head(self, K, om, offsets, qc_re, qc_im, q_mean_norm, q_mrl):
+        """Per-key magnitude bound M_i (tolerance scale; |score_i| <= M_i)."""
+        K = _f64(K)
+        n, d = K.shape
+        om = _f64(om)
+        offsets = _i64(offsets)
+        qc_re, qc_im, q_mean_norm, q_mrl = (_f64(x) for x in (qc_re, qc_im, q_mean_norm, q_mrl))
+        out = np.empty(n)
+        self.lib.tri_oracle_bound_head(
+            d, n, _ptr(K, _dp), _ptr(om, _dp), _ptr(offsets, _i64p), len(offsets),
+            _ptr(qc_re, _dp), _ptr(qc_im, _dp), _ptr(q_mean_norm, _dp), _ptr(q_mrl, _dp),
+            _ptr(out, _dp))
+        return out
+
+    def select_head(self, score, pos, budget: int, window: int):
+        """Kept slots (ascending) of one head, or None when the head does not fire."""
+        score = _f64(score)
+        pos = _i64(pos)
+        n = score.shape[0]
+        kept = np.empty(max(budget, 1), dtype=np.int32)
+        r = self.lib.tri_oracle_select_head(n, _ptr(score, _dp), _ptr(pos, _i64p),
+                                            int(budget), int(window), _ptr(kept, _i32p))
+        if r < 0:
+            raise ValueError("bad arguments to the oracle's select")
+        if r == 0:
+            return None
+        return kept[:r].copy()
+
+    def gather_rows(self, kept, rows: np.ndarray) -> np.ndarray:
+        """dst[r] = rows[kept[r]] (bytes copied exactly)."""
+        kept = np.ascontiguousarray(kept, dtype=np.int32)
+        rows = np.ascontiguousarray(rows)
+        row_bytes = rows.strides[0] if rows.ndim > 1 else rows.itemsize
+        out = np.empty((len(kept),) + rows.shape[1:], dtype=rows.dtype)
+        self.lib.tri_oracle_gather_rows(len(kept), _ptr(kept, _i32p), int(row_bytes),
+                                        rows.ctypes.data, out.ctypes.data)
+        return out
+
+    def prune_head(self, K, V, pos, p_now, om, offsets, qc_re, qc_im, q_mean_norm, q_mrl,
+                   budget, window):
+        """One head's full prune step: score, top-B, gather.
+
+        Returns dict(score, kept, K, V, pos); kept/K/V/pos are None when the
+        head does not fire.
+        """
+        _, _, score = self.score_head(K, pos, p_now, om, offsets, qc_re, qc_im,
+                                      q_mean_norm, q_mrl)
+        kept = self.select_head(score, pos, budget, window)
+        if kept is None:
+            return dict(score=score, kept=None, K=None, V=None, pos=None)
+        return dict(score=score, kept=kept, K=self.gather_rows(kept, K),
+                    V=self.gather_rows(kept, V), pos=self.gather_rows(kept, np.asarray(pos)))
+
+    def prune_heads_parallel(self, jobs, threads: int):
+        """Runs ``prune_head(**job)`` for every job on ``threads`` host threads
+        (the C calls release the GIL).  Returns the results in job order."""
+        if threads <= 1:
+            return [self.prune_head(**j) for j in jobs]
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            return list(ex.map(lambda j: self.prune_head(**j), jobs))
+
+
+_default = None
+
+
+def load() -> Oracle:
+    """The oracle built from ``tri_oracle.c`` (compiled on first use)."""
+    global _default
+    if _default is None:
+        build()
+        _default = Oracle(LIBRARY)
+    return _default

@@ -1,0 +1,223 @@
+/*
+ * tri_oracle.c -- plain, slow fp64 CPU oracle of the TriAttention online
+ * KV-eviction pass: score every cached key, keep the top-B keys per KV head,
+ * gather the kept rows.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may use it.  It shares no code, header, table or constant
+ * with the HIP path.
+ *
+ * Sources (cited by page title and section; no code exists on the pages):
+ *   [R1] "TriAttention" paper review, romaanj.github.io, section "Method":
+ *        the per-band trigonometric term ||E[q_f]||*||k_f||*cos(w_f*D + phi_f),
+ *        the norm term weighted by (1 - R_f), averaging over geometrically
+ *        spaced future offsets {1,2,4,...,2^16}, pruning to the budget every
+ *        128 decoded tokens; figure 4 caption ("only top-scoring keys survive
+ *        the prune").
+ *   [R2] "TriAttention ... Review", dimensionstp.github.io, section 2-2
+ *        (RoPE logit as a sum over bands of r_q*r_k*cos((i-j)*theta_f+phi_f)),
+ *        section 3-2 items 2)-5) (cached key has a known position and
+ *        pre-RoPE form; score = S_tri + S_norm; window-based pruning keeps
+ *        the top-budget keys).
+ *
+ * Readings taken where the pages leave a step open (each is listed in the
+ * design notes of the repository):
+ *   - band f of a head_dim-d vector x is the complex number
+ *     x[f] + i*x[f + d/2] (half-split pairing), and RoPE at position p
+ *     multiplies band f by exp(i*w_f*p);
+ *   - w_f = theta^(-2f/d) unless the caller gives explicit frequencies;
+ *   - the norm-term weight of band f is (1 - R_f) * E|q_f|;
+ *   - the average over offsets is the plain arithmetic mean;
+ *   - the trig and norm terms are added unscaled;
+ *   - a head fires iff n > budget + window; top-B orders keys by
+ *     (score descending, position ascending), NaN below every number,
+ *     -0 equal to +0; kept slots are returned in ascending slot order.
+ *
+ * Everything is computed literally in the order the pages state it:
+ * un-rotate the stored key, then average the per-band trigonometric term
+ * over every future offset, then add the norm term.
+ */
+#include <complex.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* RoPE band frequency w_f = theta^(-2f/d) (standard RoPE; reading). */
+double tri_oracle_omega(int f, int d, double theta)
+{
+    return pow(theta, -2.0 * (double)f / (double)d);
+}
+
+/* Pre-RoPE band f of one stored (post-RoPE) key row K at position p:
+ * k_f = (K[f] + i*K[f+d/2]) * exp(-i*w_f*p).  [R2 3-2 item 2: the cached key
+ * has a known position and a pre-RoPE representation.] */
+static double complex unrotate_band(const double* K, int d, int f,
+                                    int64_t p, const double* omega)
+{
+    double complex stored = K[f] + I * K[f + d / 2];
+    return stored * cexp(-I * omega[f] * (double)p);
+}
+
+/* Writes the d/2 pre-RoPE bands of one stored key row. */
+void tri_oracle_unrotate(int d, const double* K, int64_t p,
+                         const double* omega, double* k_re, double* k_im)
+{
+    for (int f = 0; f < d / 2; ++f) {
+        double complex k = unrotate_band(K, d, f, p, omega);
+        k_re[f] = creal(k);
+        k_im[f] = cimag(k);
+    }
+}
+
+/*
+ * Scores the n keys of one (layer, KV head).
+ *   K       [n][d] stored post-RoPE key rows, upcast to fp64
+ *   pos     [n]    position of each key
+ *   p_now          position of the newest cached token; future queries
+ *                  sit at p_now + delta for each delta in offsets
+ *   omega   [d/2]  band frequencies
+ *   offsets [n_off]
+ *   qc_re, qc_im [d/2]  calibrated pre-RoPE query centre E[q_f]
+ *   q_mean_norm  [d/2]  E|q_f|
+ *   q_mrl        [d/2]  mean resultant length R_f
+ * Outputs trig[n], norm[n], score[n] (any may be NULL).
+ *
+ * trig_i = mean over delta of  sum_f Re( qc_f * conj(k_f) *
+ *                                         exp(i*w_f*(p_now + delta - p_i)) )
+ *   which is, band by band, |qc_f|*|k_f|*cos(w_f*dist + phase difference)
+ *   [R1 Method; R2 2-2, 3-2 item 2];
+ * norm_i = sum_f (1 - R_f) * E|q_f| * |k_f|      [R1 Method; R2 3-2 items 3-4];
+ * score_i = trig_i + norm_i                       [R2 3-2 item 4].
+ */
+void tri_oracle_score_head(int d, int n, const double* K, const int64_t* pos,
+                           int64_t p_now, const double* omega,
+                           const int64_t* offsets, int n_off,
+                           const double* qc_re, const double* qc_im,
+                           const double* q_mean_norm, const double* q_mrl,
+                           double* trig, double* norm, double* score)
+{
+    const int half = d / 2;
+    double complex* k = (double complex*)malloc(sizeof(double complex) * (size_t)half);
+    for (int i = 0; i < n; ++i) {
+        const double* row = K + (size_t)i * (size_t)d;
+        for (int f = 0; f < half; ++f)
+            k[f] = unrotate_band(row, d, f, pos[i], omega);
+
+        /* trigonometric distance-preference series, averaged over offsets */
+        double trig_sum = 0.0;
+        for (int o = 0; o < n_off; ++o) {
+            int64_t dist = p_now + offsets[o] - pos[i];
+            double at_offset = 0.0;
+            for (int f = 0; f < half; ++f) {
+                double complex q = qc_re[f] + I * qc_im[f];
+                at_offset += creal(q * conj(k[f]) * cexp(I * omega[f] * (double)dist));
+            }
+            trig_sum += at_offset;
+        }
+        double t = trig_sum / (double)n_off;
+
+        /* concentration-weighted norm term */
+        double nm = 0.0;
+        for (int f = 0; f < half; ++f)
+            nm += (1.0 - q_mrl[f]) * q_mean_norm[f] * cabs(k[f]);
+
+        if (trig) trig[i] = t;
+        if (norm) norm[i] = nm;
+        if (score) score[i] = t + nm;
+    }
+    free(k);
+}
+
+/*
+ * Per-key magnitude bound M_i = sum_f (|qc_f| * |A_f| + w_f) * |k_f| with
+ * A_f = mean over delta of exp(i*w_f*delta) and w_f = (1 - R_f) * E|q_f|.
+ * |score_i| <= M_i, and M_i is the scale of the rounding error of any
+ * evaluation of the score, so parity tolerances are stated relative to it.
+ * This is a tolerance scale, not part of the score.
+ */
+void tri_oracle_bound_head(int d, int n, const double* K, const double* omega,
+                           const int64_t* offsets, int n_off,
+                           const double* qc_re, const double* qc_im,
+                           const double* q_mean_norm, const double* q_mrl,
+                           double* bound)
+{
+    const int half = d / 2;
+    double* coef = (double*)malloc(sizeof(double) * (size_t)half);
+    for (int f = 0; f < half; ++f) {
+        double complex a = 0.0;
+        for (int o = 0; o < n_off; ++o)
+            a += cexp(I * omega[f] * (double)offsets[o]);
+        a /= (double)n_off;
+        coef[f] = cabs(qc_re[f] + I * qc_im[f]) * cabs(a)
+                + (1.0 - q_mrl[f]) * q_mean_norm[f];
+    }
+    for (int i = 0; i < n; ++i) {
+        const double* row = K + (size_t)i * (size_t)d;
+        double m = 0.0;
+        for (int f = 0; f < half; ++f)
+            m += coef[f] * hypot(row[f], row[f + half]);   /* |k_f| = |K_f| */
+        bound[i] = m;
+    }
+    free(coef);
+}
+
+/* ---- top-B selection ---------------------------------------------------- */
+
+typedef struct { double s; int64_t p; int32_t slot; } ranked;
+
+/* Order: score descending, NaN below every number, then position ascending,
+ * then slot ascending (positions are distinct in a cache, the slot only makes
+ * the order total). -0 and +0 compare equal under C's ordinary comparison. */
+static int by_rank(const void* a_, const void* b_)
+{
+    const ranked* a = (const ranked*)a_;
+    const ranked* b = (const ranked*)b_;
+    int an = isnan(a->s), bn = isnan(b->s);
+    if (an != bn) return an ? 1 : -1;
+    if (!an) {
+        if (a->s > b->s) return -1;
+        if (a->s < b->s) return 1;
+    }
+    if (a->p != b->p) return a->p < b->p ? -1 : 1;
+    return a->slot < b->slot ? -1 : (a->slot > b->slot ? 1 : 0);
+}
+
+static int by_int32(const void* a_, const void* b_)
+{
+    int32_t a = *(const int32_t*)a_, b = *(const int32_t*)b_;
+    return (a > b) - (a < b);
+}
+
+/*
+ * Top-B of one head [R1 Method and figure 4 caption; R2 3-2 item 5].
+ * The head fires iff n > budget + window.  When it fires, writes the budget
+ * kept slots in ascending slot order to kept[] and returns budget; otherwise
+ * returns 0 and writes nothing.  Returns -1 on bad arguments.
+ */
+int tri_oracle_select_head(int n, const double* score, const int64_t* pos,
+                           int budget, int window, int32_t* kept)
+{
+    if (n < 0 || budget <= 0 || window < 0) return -1;
+    if ((int64_t)n <= (int64_t)budget + (int64_t)window) return 0;
+    ranked* r = (ranked*)malloc(sizeof(ranked) * (size_t)n);
+    for (int i = 0; i < n; ++i) { r[i].s = score[i]; r[i].p = pos[i]; r[i].slot = i; }
+    qsort(r, (size_t)n, sizeof(ranked), by_rank);
+    for (int j = 0; j < budget; ++j) kept[j] = r[j].slot;
+    qsort(kept, (size_t)budget, sizeof(int32_t), by_int32);
+    free(r);
+    return budget;
+}
+
+/* Gathers rows: dst[r] = src[kept[r]] for r < n_kept (row_bytes each).
+ * The eviction keeps exactly the selected rows, in ascending slot order. */
+void tri_oracle_gather_rows(int n_kept, const int32_t* kept, int64_t row_bytes,
+                            const void* src, void* dst)
+{
+    const unsigned char* s = (const unsigned char*)src;
+    unsigned char* o = (unsigned char*)dst;
+    for (int r = 0; r < n_kept; ++r)
+        memcpy(o + (size_t)r * (size_t)row_bytes,
+               s + (size_t)kept[r] * (size_t)row_bytes, (size_t)row_bytes);
+}

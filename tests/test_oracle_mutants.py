@@ -1,0 +1,94 @@
+"""Planted mistakes in the oracle must fail its pins.
+
+Each mutant is a copy of ``oracle/tri_oracle.c`` with one plausible mistake
+(a flipped conjugate or sign, interleaved band pairing, a dropped term, a
+wrong weight, a wrong tie-break or fire rule, ...), compiled with gcc into a
+temporary directory.  The pins of ``test_oracle_pins.py`` run against it and
+at least one must fail.  CPU only; the real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = {
+    "conjugate on the query": ("q * conj(k[f])", "conj(q) * k[f]"),
+    "interleaved band pairing": ("K[f] + I * K[f + d / 2]", "K[2 * f] + I * K[2 * f + 1]"),
+    "inverse RoPE rotates forward": ("cexp(-I * omega[f] * (double)p)", "cexp(I * omega[f] * (double)p)"),
+    "offsets look backwards": ("p_now + offsets[o] - pos[i]", "p_now - offsets[o] - pos[i]"),
+    "distance ignores key position": ("p_now + offsets[o] - pos[i]", "p_now + offsets[o]"),
+    "norm term dropped": ("score[i] = t + nm", "score[i] = t"),
+    "trig term dropped": ("score[i] = t + nm", "score[i] = nm"),
+    "norm weighted by R instead of 1-R": ("(1.0 - q_mrl[f]) * q_mean_norm[f] * cabs(k[f])",
+                                          "q_mrl[f] * q_mean_norm[f] * cabs(k[f])"),
+    "norm not weighted by mean query norm": ("(1.0 - q_mrl[f]) * q_mean_norm[f] * cabs(k[f])",
+                                             "(1.0 - q_mrl[f]) * cabs(k[f])"),
+    "sum over offsets instead of mean": ("trig_sum / (double)n_off", "trig_sum"),
+    "omega with d in place of d/2 pairing": ("-2.0 * (double)f / (double)d", "-1.0 * (double)f / (double)d"),
+    "ties go to the later position": ("if (a->p != b->p) return a->p < b->p ? -1 : 1;",
+                                      "if (a->p != b->p) return a->p < b->p ? 1 : -1;"),
+    "ties by slot instead of position": ("if (a->p != b->p) return a->p < b->p ? -1 : 1;", ""),
+    "NaN ranks highest": ("if (an != bn) return an ? 1 : -1;", "if (an != bn) return an ? -1 : 1;"),
+    "keeps the lowest scores": ("if (a->s > b->s) return -1;\n        if (a->s < b->s) return 1;",
+                                "if (a->s > b->s) return 1;\n        if (a->s < b->s) return -1;"),
+    "fire rule off by one": ("if ((int64_t)n <= (int64_t)budget + (int64_t)window) return 0;",
+                             "if ((int64_t)n < (int64_t)budget + (int64_t)window) return 0;"),
+    "kept list left in rank order": ("qsort(kept, (size_t)budget, sizeof(int32_t), by_int32);", ""),
+    "gather copies the wrong row": ("s + (size_t)kept[r] * (size_t)row_bytes", "s + (size_t)r * (size_t)row_bytes"),
+}
+
+
+def _pin_calls():
+    calls = [
+        (pins.test_omega_matches_standard_rope, {}),
+        (pins.test_unrotate_inverts_a_dense_rotation, {"d": 64}),
+        (pins.test_unrotate_composes_and_preserves_band_norms, {}),
+        (pins.test_trig_equals_bruteforce_rope_dot_products, {"d": 8, "n": 40, "theta": 10.0}),
+        (pins.test_trig_equals_bruteforce_rope_dot_products, {"d": 64, "n": 64, "theta": 1e4}),
+        (pins.test_single_offset_is_the_rope_attention_logit, {}),
+        (pins.test_key_equal_to_centre_at_zero_distance_gives_squared_norm, {}),
+        (pins.test_zero_query_centre_gives_zero_trig, {}),
+        (pins.test_polar_per_band_form, {}),
+        (pins.test_trig_swapping_query_and_key_roles_is_detected, {}),
+        (pins.test_norm_term_special_cases_and_direct_sum, {}),
+        (pins.test_norm_term_is_position_invariant, {}),
+        (pins.test_score_is_sum_and_bounded, {}),
+        (pins.test_folded_form_agrees, {}),
+        (pins.test_select_matches_numpy_lexsort, {}),
+        (pins.test_select_invariants_and_fire_rule, {}),
+        (pins.test_gather_matches_numpy_take_and_identity, {}),
+    ]
+    for ex in pins._golden()["score_examples"]:
+        calls.append((pins.test_golden_score_examples, {"ex": ex}))
+    for i in range(len(pins._golden()["select_examples"])):
+        calls.append((pins.test_golden_select_examples, {"i": i}))
+    for seed in range(12):
+        calls.append((pins.test_select_equals_bruteforce_subset_search, {"seed": seed}))
+    return calls
+
+
+def test_pins_pass_on_the_real_oracle():
+    lib = oracle.load()
+    for fn, kw in _pin_calls():
+        fn(lib, **kw)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation site not found: %r" % old
+    mutant_c = os.path.join(tmp_path, "mutant.c")
+    with open(mutant_c, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.Oracle(oracle.compile_c(mutant_c, os.path.join(tmp_path, "libmutant.so")))
+    failed = []
+    for fn, kw in _pin_calls():
+        try:
+            fn(lib, **kw)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            failed.append(fn.__name__)
+    assert failed, "mutant '%s' passed every pin" % name
