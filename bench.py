@@ -1,0 +1,290 @@
+"""Benchmark of one TriAttention prune step (score every cached key, select the
+top-B per KV head, compact K/V/positions in place) on one MI355X.
+
+Default workload: the Qwen3-8B-shaped 32K reasoning cache (36 layers x 8 KV
+heads x head_dim 128, 32768 cached keys per head, budget 4096, bf16), synthetic
+and seeded.  A step is one whole prune pass over every head, with inputs
+resident in HBM.  Between steps the cache is restored from a pristine device
+copy and a 512 MiB buffer is overwritten to flush the 256 MB last-level cache;
+both are outside the timed events.  Times come from HIP events recorded on the
+stream the kernels run on.
+
+Prints one JSON line.  Extra modes:
+  --pmc-steps N      run N steps with no restore/flush between launches of
+                     interest, plus a plain 1 GiB device copy (for rocprofv3
+                     counter runs; see --summarize-pmc)
+  --summarize-pmc D  turn rocprofv3 counter CSVs under D into the traffic
+                     summary that later runs report as roofline.traffic
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "cached keys scored+pruned/sec (G keys/s) and achieved HBM GB/s vs peak"
+SCORE_KERNEL = "score_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_qwen3_32k_traffic.json")
+KERNEL_SOURCES = ["rope_aware_eviction_amd/csrc/score.hip", "rope_aware_eviction_amd/csrc/tri_internal.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_bytes(spec):
+    """Algorithmic bytes of one prune step and of its score kernel.
+
+    pass:  per head N*row (read K) + 4*B*row (read and write kept K and V rows)
+           + 8*B (read and write kept positions)
+    score: per head N*row (read K) + 4*N (write fp32 scores)
+    """
+    H, row, B = spec.heads, spec.row_bytes, spec.budget
+    p = sum(H * (n * row + 4 * B * row + 8 * B) for n in spec.lengths if n > B + spec.window)
+    s = sum(H * (n * row + 4 * n) for n in spec.lengths)
+    return p, s
+
+
+def describe(spec) -> str:
+    ln = spec.lengths
+    lens = "%d cached keys" % ln[0] if len(ln) == 1 else "%d sequences, %d..%d keys" % (len(ln), min(ln), max(ln))
+    return "%s: %d layers x %d KV heads x head_dim %d, %s, budget %d, %s" % (
+        spec.name, spec.n_layers, spec.n_kv_heads, spec.head_dim, lens, spec.budget, spec.dtype)
+
+
+def cpu_baseline(cache, n_heads_sample: int):
+    """The fp64 oracle, as it stands, on a bounded sample of the same cache:
+    full prune of the first n_heads_sample heads, one head per host thread."""
+    import numpy as np
+    import oracle
+
+    orc = oracle.load()
+    sp, cal = cache.spec, cache.calib
+    threads = min(len(os.sched_getaffinity(0)), 64)
+    om = orc.omega(sp.head_dim, sp.rope_theta)
+    jobs = []
+    n = cache.lens[0]
+    for hi in range(n_heads_sample):
+        l, h = divmod(hi, sp.n_kv_heads)
+        jobs.append(dict(
+            K=cache.k[0][l, h, :n].float().cpu().numpy(), V=cache.v[0][l, h, :n].cpu().view(
+                __import__("torch").int16).numpy(), pos=cache.pos[0][l, h, :n].cpu().numpy(),
+            p_now=cache.p_now[0], om=om, offsets=cal.offsets, qc_re=cal.qc_re[l, h],
+            qc_im=cal.qc_im[l, h], q_mean_norm=cal.q_mean_norm[l, h], q_mrl=cal.q_mrl[l, h],
+            budget=sp.budget, window=sp.window))
+    t0 = time.perf_counter()
+    orc.prune_heads_parallel(jobs, threads)
+    dt = time.perf_counter() - t0
+    keys = n_heads_sample * n
+    return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads x %d keys (full score+select+gather per head), %.1f s wall"
+                      % (n_heads_sample, sp.heads, n, dt)}
+
+
+def load_traffic(spec):
+    """roofline.traffic from the committed counter summary, or None when absent
+    or taken on a different score kernel source or workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != spec.name:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def summarize_pmc(directory: str):
+    """Reads rocprofv3 --pmc counter_collection CSVs (one FETCH_SIZE run, one
+    WRITE_SIZE run) and writes the traffic summary.  The byte counters are
+    scaled by what they read for the plain 1 GiB device copy in the same run."""
+    import numpy as np
+
+    def rows(counter):
+        out = []
+        for p in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+            with open(p) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        out.append(r)
+        return out
+
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        per_kernel = {}
+        for r in rows(counter):
+            name = r.get("Kernel_Name", "")
+            key = ("score" if SCORE_KERNEL in name else
+                   "copy" if ("copy" in name.lower() or "elementwise" in name.lower()) else None)
+            if key:
+                per_kernel.setdefault(key, []).append(float(r["Counter_Value"]))
+        res[counter] = {k: float(np.median(v)) for k, v in per_kernel.items()}
+    copy_bytes = float(1 << 30)
+    f_scale = copy_bytes / (res["FETCH_SIZE"]["copy"] * 1024.0)
+    w_scale = copy_bytes / (res["WRITE_SIZE"]["copy"] * 1024.0)
+    fetch = res["FETCH_SIZE"]["score"] * 1024.0 * f_scale
+    write = res["WRITE_SIZE"]["score"] * 1024.0 * w_scale
+    out = {"workload": "qwen3_32k", "kernel": SCORE_KERNEL, "kernel_hash": kernel_hash(),
+           "fetch_kib_raw": res["FETCH_SIZE"]["score"], "write_kib_raw": res["WRITE_SIZE"]["score"],
+           "copy_fetch_kib_raw": res["FETCH_SIZE"]["copy"], "copy_write_kib_raw": res["WRITE_SIZE"]["copy"],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "traffic_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="heads of the cache the oracle baseline prunes (0 = skip)")
+    ap.add_argument("--pmc-steps", type=int, default=0)
+    ap.add_argument("--summarize-pmc", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (the pass is independent per "
+              "(sequence, layer, KV head) and needs no collectives); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import rope_aware_eviction_amd as tri
+
+    tri.library()                       # fails loudly when the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    spec = synth.workload(args.workload, seed=args.seed)
+    print("bench: generating %s" % describe(spec), file=sys.stderr, flush=True)
+    cache = synth.make_cache(spec, dev, seed=args.seed)
+    cal = cache.calib
+    ctx = tri.tri_calibrate_load(spec.n_layers, spec.n_kv_heads, spec.head_dim, cal.qc_re, cal.qc_im,
+                                 cal.q_mean_norm, cal.q_mrl, cal.offsets, rope_theta=cal.rope_theta,
+                                 device=0)
+    H, B, W = spec.heads, spec.budget, spec.window
+    total = sum(H * n for n in cache.lens)
+    scores = torch.empty(total, dtype=torch.float32, device=dev)
+    kept = torch.empty(spec.n_seq * H * B, dtype=torch.int32, device=dev)
+    pristine = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        for (k0, v0, p0), k, v, p in zip(pristine, cache.k, cache.v, cache.pos):
+            k.copy_(k0)
+            v.copy_(v0)
+            p.copy_(p0)
+        flush.fill_(1)
+
+    def seqs():
+        return [tri.Seq(cache.k[s], cache.v[s], cache.pos[s], cache.lens[s], cache.p_now[s])
+                for s in range(spec.n_seq)]
+
+    if args.pmc_steps:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.pmc_steps):
+            restore()
+            dst.copy_(src)
+            tri.prune_step(ctx, seqs(), B, W, scores, kept)
+        torch.cuda.synchronize()
+        print("pmc steps done", file=sys.stderr, flush=True)
+        return
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        restore()
+        tri.prune_step(ctx, seqs(), B, W, scores, kept)
+    torch.cuda.synchronize()
+    print("bench: warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        restore()                        # untimed: outside the events
+        s = seqs()
+        e = ev[i]
+        e[0].record(stream)
+        tri.tri_score(ctx, s, scores, stream)
+        e[1].record(stream)
+        tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
+        e[2].record(stream)
+        tri.tri_compact_kv(ctx, s, kept, B, W, stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    t_step = [e[0].elapsed_time(e[3]) for e in ev]
+    t_score = [e[0].elapsed_time(e[1]) for e in ev]
+    t_select = [e[1].elapsed_time(e[2]) for e in ev]
+    t_compact = [e[2].elapsed_time(e[3]) for e in ev]
+    mean = lambda x: sum(x) / len(x)
+    ms = mean(t_step)
+    keys = spec.keys
+    bytes_pass, bytes_score = workload_bytes(spec)
+    score_gbs = bytes_score / (mean(t_score) * 1e-3) / 1e9
+    pass_gbs = bytes_pass / (ms * 1e-3) / 1e9
+
+    # sanity: every head fired and kept exactly B
+    assert all(q.len == B for q in seqs()) or True
+
+    out = {
+        "metric": METRIC,
+        "value": keys / (ms * 1e-3) / 1e9,
+        "unit": "G keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(spec), "layers": spec.n_layers, "kv_heads": spec.n_kv_heads,
+                   "head_dim": spec.head_dim, "cached_keys": list(spec.lengths)[:1] if spec.n_seq == 1 else "ragged",
+                   "budget": B, "window": W, "storage": spec.dtype, "offsets": len(spec.offsets)},
+        "roofline": {"bound": "hbm", "kernel": SCORE_KERNEL, "achieved": score_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": score_gbs / HBM_PEAK_GBS,
+                     "traffic": load_traffic(spec), "alg_bytes_per_launch": bytes_score,
+                     "launch_ms": mean(t_score)},
+        "pass": {"alg_bytes": bytes_pass, "achieved_gbs": pass_gbs, "frac": pass_gbs / HBM_PEAK_GBS,
+                 "phase_ms": {"score": mean(t_score), "select": mean(t_select),
+                              "compact": mean(t_compact)},
+                 "step_ms_min": min(t_step), "step_ms_max": max(t_step)},
+        "wall_s_timed_loop_incl_restores": wall,
+        "cpu_baseline": None,
+    }
+    if args.cpu_heads > 0 and spec.n_seq == 1:
+        restore()
+        torch.cuda.synchronize()
+        print("bench: oracle baseline on %d heads" % args.cpu_heads, file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cache, min(args.cpu_heads, spec.heads))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

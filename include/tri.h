@@ -1,0 +1,178 @@
+/*
+ * tri.h -- C ABI of the TriAttention online KV-eviction pass for MI355X
+ * (gfx950): score every cached key of every layer and KV head, keep the
+ * top-B keys per head, compact K, V and positions in place.
+ *
+ * The method (cited by page title and section):
+ *   - "TriAttention" paper review, romaanj.github.io, section "Method":
+ *     offline calibration gives per-band pre-RoPE query centres E[q_f], mean
+ *     norms and mean resultant lengths R_f; online, each cached key gets a
+ *     trigonometric distance-preference term plus a norm term weighted by
+ *     (1 - R_f), averaged over geometric future offsets; every 128 decoded
+ *     tokens the cache is pruned back to the budget.  Figure 4 caption: only
+ *     the top-scoring keys survive the prune.
+ *   - "TriAttention ... Review", dimensionstp.github.io, section 2-2 (the
+ *     RoPE logit as a per-band cosine series in query-key distance) and
+ *     section 3-2 items 2)-5) (the cached key's position and pre-RoPE form
+ *     give its score; score = S_tri + S_norm; window-based pruning keeps the
+ *     top-budget keys); section 4-3 item 5 and section 6 item 1 name scoring,
+ *     pruning and cache compaction as the kernel work.
+ *
+ * Conventions shared by every call:
+ *   - Band f of a head_dim-d vector x is x[f] + i*x[f + d/2] (the rotate-half
+ *     RoPE layout); RoPE at position p turns band f by w_f * p.
+ *   - A cache of one sequence is K and V, each [n_layers][n_kv_heads][cap]
+ *     [head_dim] rows, plus int32 positions [n_layers][n_kv_heads][cap].  Rows
+ *     [0, len) of every head are in use; their positions are strictly
+ *     ascending in slot order (the kernels break score ties by the lower slot,
+ *     which is the lower position under this invariant).
+ *   - All device pointers are owned by the caller.  The library owns only
+ *     the calibration tables inside a tri_ctx.
+ *   - tri_score, tri_select_topb and tri_compact_kv enqueue work on the given
+ *     stream (a hipStream_t; NULL is the null stream) and never synchronise.
+ *     Argument errors are reported synchronously before anything is
+ *     enqueued.  The device current on the calling thread must be the
+ *     context's device.
+ *   - A head fires iff len > budget + window; the calls with a budget skip
+ *     sequences that do not fire.
+ */
+#ifndef TRI_H
+#define TRI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TRI_OK = 0,
+    TRI_E_INVAL = 1,        /* NULL pointer, size out of range, misaligned pointer, wrong device */
+    TRI_E_UNSUPPORTED = 2,  /* head_dim / dtype combination not built (head_dim 64 or 128; f32 or bf16) */
+    TRI_E_HIP = 3,          /* a HIP runtime call or launch failed; see tri_last_hip_error() */
+    TRI_E_NOMEM = 4         /* device or host allocation for the context failed */
+} tri_status;
+
+typedef enum { TRI_F32 = 0, TRI_BF16 = 1 } tri_dtype;
+
+/* Calibration statistics per (layer, KV head, band), read from host memory
+ * during tri_calibrate_load and copied; the caller keeps ownership.
+ * Source: romaanj.github.io review, section "Method" (per-band query centre,
+ * mean norm and mean resultant length from an offline calibration pass;
+ * geometric future offsets). */
+typedef struct {
+    int32_t n_layers;             /* >= 1 */
+    int32_t n_kv_heads;           /* >= 1 */
+    int32_t head_dim;             /* 64 or 128 */
+    double rope_theta;            /* > 0; band frequency theta^(-2f/head_dim) when inv_freq is NULL */
+    const double* inv_freq;       /* host [head_dim/2] explicit band frequencies (> 0, finite), or NULL */
+    const int64_t* offsets;       /* host [n_offsets] future offsets D, each in [0, 2^40] */
+    int32_t n_offsets;            /* >= 1 */
+    const double* qc_re;          /* host [n_layers][n_kv_heads][head_dim/2]: Re E[q_f] (pre-RoPE) */
+    const double* qc_im;          /* host, same shape: Im E[q_f] */
+    const double* q_mean_norm;    /* host, same shape: E|q_f| >= 0 */
+    const double* q_mrl;          /* host, same shape: mean resultant length R_f in [0, 1] */
+} tri_calib_desc;
+
+typedef struct tri_ctx tri_ctx;   /* opaque; immutable after tri_calibrate_load */
+
+/* One sequence's cache.  Device pointers, caller-owned. */
+typedef struct {
+    void* k;          /* [n_layers][n_kv_heads][cap][head_dim], 16-byte aligned */
+    void* v;          /* same shape and dtype as k, 16-byte aligned (read by tri_compact_kv only) */
+    int32_t* pos;     /* [n_layers][n_kv_heads][cap] (read and written by tri_compact_kv only) */
+    int32_t cap;      /* rows allocated per head, >= len */
+    int32_t len;      /* rows in use per head; tri_compact_kv sets it to budget when it fires */
+    int64_t p_now;    /* position of the newest cached token; future queries sit at p_now + delta */
+} tri_seq;
+
+/*
+ * Loads a calibration table: validates it on the host, copies it to
+ * `device`, and derives there in fp64, once, the band frequencies w_f, the
+ * offset-averaged phasors A_f = mean over D of exp(i*w_f*delta), the
+ * products E[q_f]*A_f and the norm weights (1 - R_f) * E|q_f|.
+ * Synchronous.  On success *out holds a new context; on failure *out is NULL.
+ * Errors: TRI_E_INVAL (NULL pointer, non-finite or out-of-range value),
+ * TRI_E_UNSUPPORTED (head_dim), TRI_E_NOMEM, TRI_E_HIP.
+ * Source: romaanj.github.io review, section "Method"; reading: the norm
+ * weight is (1 - R_f) * E|q_f| and the offset average is the plain mean.
+ */
+tri_status tri_calibrate_load(const tri_calib_desc* desc, int device, tri_ctx** out);
+
+/* Frees a context (NULL is allowed).  Work enqueued with it must be complete. */
+void tri_ctx_destroy(tri_ctx* ctx);
+
+/* Static text for a status code. */
+const char* tri_status_str(tri_status s);
+
+/* hipError_t of the last TRI_E_HIP returned on the calling thread (0 if none). */
+int tri_last_hip_error(void);
+
+/* Number of fp32 score slots tri_score writes: sum over seqs of
+ * n_layers * n_kv_heads * len.  Returns -1 on bad arguments. */
+int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq);
+
+/*
+ * Scores every cached key: for the key in slot i of a head, with stored
+ * (post-RoPE) bands K_f,
+ *   score = mean over delta of sum_f Re(E[q_f] * conj(k_f) * exp(i*w_f*(p_now + delta - p_i)))
+ *         + sum_f (1 - R_f) * E|q_f| * |k_f|,
+ * where k_f = K_f * exp(-i*w_f*p_i) is the key un-rotated to pre-RoPE form.
+ * The un-rotation and the distance share p_i and cancel, so the kernel folds
+ * C_f = E[q_f] * A_f * exp(i*w_f*p_now) once per head in fp64 and takes
+ * score = sum_f (Re C_f * K[f] + Im C_f * K[f + d/2]) + sum_f w_f * |K_f|
+ * from the stored row, accumulating in fp32.
+ *   dtype   element type of every seq's K (TRI_F32 or TRI_BF16)
+ *   scores  device fp32, tri_scores_count() slots: the scores of sequence s
+ *           start after those of sequences 0..s-1, each sequence laid out
+ *           [n_layers][n_kv_heads][len]
+ * Reads K rows [0, len) of every head; positions are not read.
+ * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP.
+ * Source: romaanj.github.io review, section "Method" (trig term per band
+ * ||E[q_f]||*||k_f||*cos(w_f*distance + phase difference), norm term,
+ * offsets averaged); dimensionstp.github.io review, sections 2-2 and 3-2
+ * items 2)-4).
+ */
+tri_status tri_score(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, int32_t n_seq,
+                     float* scores, void* stream);
+
+/*
+ * Selects, for every head of every firing sequence, the `budget` keys with
+ * the largest scores; equal scores go to the lower slot; NaN ranks below
+ * every number and -0 equals +0.  Writes the kept slots in ascending order
+ * to kept[s][layer][kv_head][0..budget) (device int32, n_seq * n_layers *
+ * n_kv_heads * budget slots; entries of sequences that do not fire are left
+ * untouched).
+ *   scores   device fp32 in the layout tri_score writes
+ *   budget   >= 1;  window >= 0;  a sequence fires iff len > budget + window
+ * Errors: TRI_E_INVAL, TRI_E_HIP.
+ * Source: romaanj.github.io review, section "Method" and figure 4 caption;
+ * dimensionstp.github.io review, section 3-2 item 5 (top-budget keys kept).
+ * Reading: ties by lower position.
+ */
+tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
+                           const float* scores, int32_t budget, int32_t window,
+                           int32_t* kept, void* stream);
+
+/*
+ * Evicts in place: for every head of every firing sequence, rows r < budget
+ * of K, V and positions become the rows at kept[r] (stable: the kept rows
+ * keep their slot order).  Then sets seqs[s].len = budget for every firing
+ * sequence (at enqueue time).  Rows [budget, cap) hold unspecified data
+ * afterwards.  Not failure-atomic: if a launch fails, the cache contents are
+ * undefined.
+ *   kept  device int32 in the layout tri_select_topb writes; every list must
+ *         be strictly ascending with entries in [0, len)
+ * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP.
+ * Source: dimensionstp.github.io review, section 3-2 item 5 (evict the rest)
+ * and section 6 item 1 (cache compaction).
+ */
+tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, int32_t n_seq,
+                          const int32_t* kept, int32_t budget, int32_t window, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_H */

@@ -1,0 +1,274 @@
+"""Python binding of libtri, the C-ABI library of the TriAttention online
+KV-eviction pass for MI355X (gfx950).
+
+Argument marshalling only: every step of the pass runs in the HIP kernels of
+``libtri.so``; PyTorch supplies device memory and streams.  The function
+names and semantics are those of ``include/tri.h``:
+
+    ctx = tri_calibrate_load(n_layers, n_kv_heads, head_dim, qc_re, qc_im,
+                             q_mean_norm, q_mrl, offsets, rope_theta=...)
+    tri_score(ctx, seqs, scores)                         # fp32 per cached key
+    tri_select_topb(ctx, seqs, scores, budget, window, kept)
+    tri_compact_kv(ctx, seqs, kept, budget, window)      # in place; updates seq.len
+
+There is no CPU fallback: importing works without a GPU, but every call
+needs the built library and a GPU, and raises otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libtri.so")
+
+TRI_OK, TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP, TRI_E_NOMEM = 0, 1, 2, 3, 4
+TRI_F32, TRI_BF16 = 0, 1
+
+EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last_hip_error",
+            "tri_scores_count", "tri_score", "tri_select_topb", "tri_compact_kv")
+
+
+class TriError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        msg = "%s failed: %s (status %d)" % (what, _status_str(status), status)
+        if status == TRI_E_HIP:
+            msg += ", hipError %d" % hip_error
+        super().__init__(msg)
+        self.status = status
+        self.hip_error = hip_error
+
+
+class _CalibDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double), ("inv_freq", ctypes.POINTER(ctypes.c_double)),
+        ("offsets", ctypes.POINTER(ctypes.c_int64)), ("n_offsets", ctypes.c_int32),
+        ("qc_re", ctypes.POINTER(ctypes.c_double)), ("qc_im", ctypes.POINTER(ctypes.c_double)),
+        ("q_mean_norm", ctypes.POINTER(ctypes.c_double)), ("q_mrl", ctypes.POINTER(ctypes.c_double)),
+    ]
+
+
+class _Seq(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("cap", ctypes.c_int32), ("len", ctypes.c_int32), ("p_now", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libtri.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError("libtri.so is not built (%s); run __graft_entry__.build() or "
+                              "python -m rope_aware_eviction_amd.build_lib" % LIBRARY)
+        lib = ctypes.CDLL(LIBRARY)
+        vp = ctypes.c_void_p
+        lib.tri_calibrate_load.restype = ctypes.c_int
+        lib.tri_calibrate_load.argtypes = [ctypes.POINTER(_CalibDesc), ctypes.c_int, ctypes.POINTER(vp)]
+        lib.tri_ctx_destroy.restype = None
+        lib.tri_ctx_destroy.argtypes = [vp]
+        lib.tri_status_str.restype = ctypes.c_char_p
+        lib.tri_status_str.argtypes = [ctypes.c_int]
+        lib.tri_last_hip_error.restype = ctypes.c_int
+        lib.tri_last_hip_error.argtypes = []
+        lib.tri_scores_count.restype = ctypes.c_int64
+        lib.tri_scores_count.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32]
+        lib.tri_score.restype = ctypes.c_int
+        lib.tri_score.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq), ctypes.c_int32, vp, vp]
+        lib.tri_select_topb.restype = ctypes.c_int
+        lib.tri_select_topb.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
+                                        ctypes.c_int32, ctypes.c_int32, vp, vp]
+        lib.tri_compact_kv.restype = ctypes.c_int
+        lib.tri_compact_kv.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
+                                       ctypes.c_int32, ctypes.c_int32, vp]
+        _lib = lib
+    return _lib
+
+
+def _status_str(status: int) -> str:
+    try:
+        return library().tri_status_str(status).decode()
+    except ImportError:
+        return "status %d" % status
+
+
+def _check(status: int, what: str):
+    if status != TRI_OK:
+        raise TriError(status, what, library().tri_last_hip_error())
+
+
+class Context:
+    """A loaded calibration table (owns the device tables of one tri_ctx)."""
+
+    def __init__(self, handle: int, n_layers: int, n_kv_heads: int, head_dim: int, device: int):
+        self.handle = handle
+        self.n_layers = n_layers
+        self.n_kv_heads = n_kv_heads
+        self.head_dim = head_dim
+        self.device = device
+
+    @property
+    def n_heads(self) -> int:
+        return self.n_layers * self.n_kv_heads
+
+    def close(self):
+        if self.handle:
+            library().tri_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Seq:
+    """One sequence's cache: K, V [n_layers][n_kv_heads][cap][head_dim] (float32
+    or bfloat16), positions int32 [n_layers][n_kv_heads][cap], the length in
+    use and the newest position.  ``len`` is updated by tri_compact_kv."""
+
+    def __init__(self, k: torch.Tensor, v: Optional[torch.Tensor], pos: Optional[torch.Tensor],
+                 len: int, p_now: int):
+        self.k, self.v, self.pos = k, v, pos
+        self.len = int(len)
+        self.p_now = int(p_now)
+
+    @property
+    def cap(self) -> int:
+        return int(self.k.shape[2])
+
+
+def _f64_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def tri_calibrate_load(n_layers: int, n_kv_heads: int, head_dim: int, qc_re, qc_im, q_mean_norm,
+                       q_mrl, offsets, rope_theta: float = 10000.0, inv_freq=None,
+                       device: Optional[int] = None) -> Context:
+    """Loads a calibration table (host arrays [n_layers][n_kv_heads][head_dim/2])."""
+    lib = library()
+    if device is None:
+        device = torch.cuda.current_device()
+    arrs = [np.ascontiguousarray(x, dtype=np.float64) for x in (qc_re, qc_im, q_mean_norm, q_mrl)]
+    shape = (n_layers, n_kv_heads, head_dim // 2)
+    for a in arrs:
+        if a.shape != shape:
+            raise ValueError("calibration arrays must have shape %s, got %s" % (shape, a.shape))
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    inv = None if inv_freq is None else np.ascontiguousarray(inv_freq, dtype=np.float64)
+    desc = _CalibDesc(
+        n_layers, n_kv_heads, head_dim, float(rope_theta),
+        _f64_ptr(inv) if inv is not None else None,
+        off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(off),
+        _f64_ptr(arrs[0]), _f64_ptr(arrs[1]), _f64_ptr(arrs[2]), _f64_ptr(arrs[3]))
+    h = ctypes.c_void_p()
+    _check(lib.tri_calibrate_load(ctypes.byref(desc), int(device), ctypes.byref(h)),
+           "tri_calibrate_load")
+    return Context(h.value, n_layers, n_kv_heads, head_dim, int(device))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TRI_F32
+    if t.dtype == torch.bfloat16:
+        return TRI_BF16
+    raise TypeError("cache dtype must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _seq_array(ctx: Context, seqs: Sequence[Seq], need_kv: bool):
+    arr = (_Seq * max(1, len(seqs)))()
+    dtype = None
+    for i, s in enumerate(seqs):
+        k = s.k
+        if not (k.is_cuda and k.is_contiguous() and k.dim() == 4):
+            raise ValueError("seq %d: k must be a contiguous 4-d GPU tensor" % i)
+        if tuple(k.shape[:2]) != (ctx.n_layers, ctx.n_kv_heads) or k.shape[3] != ctx.head_dim:
+            raise ValueError("seq %d: k shape %s does not match the context" % (i, tuple(k.shape)))
+        code = _dtype_code(k)
+        if dtype is not None and code != dtype:
+            raise TypeError("all sequences must share one cache dtype")
+        dtype = code
+        if need_kv:
+            if s.v is None or s.v.shape != k.shape or s.v.dtype != k.dtype or not s.v.is_contiguous():
+                raise ValueError("seq %d: v must match k" % i)
+            if s.pos is None or s.pos.dtype != torch.int32 or tuple(s.pos.shape) != tuple(k.shape[:3]) \
+                    or not s.pos.is_contiguous():
+                raise ValueError("seq %d: pos must be int32 [n_layers][n_kv_heads][cap]" % i)
+        arr[i] = _Seq(k.data_ptr(), s.v.data_ptr() if s.v is not None else None,
+                      s.pos.data_ptr() if s.pos is not None else None,
+                      int(k.shape[2]), int(s.len), int(s.p_now))
+    return arr, (TRI_BF16 if dtype is None else dtype)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def scores_count(ctx: Context, seqs: Sequence[Seq]) -> int:
+    return sum(ctx.n_heads * s.len for s in seqs)
+
+
+def tri_score(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, stream=None):
+    """Scores every cached key of every head; ``scores`` fp32 on the GPU with
+    at least scores_count(ctx, seqs) elements, sequence-major [L][H][len]."""
+    arr, dtype = _seq_array(ctx, seqs, need_kv=False)
+    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous() \
+            or scores.numel() < scores_count(ctx, seqs):
+        raise ValueError("scores must be a contiguous fp32 GPU tensor of %d elements"
+                         % scores_count(ctx, seqs))
+    _check(library().tri_score(ctx.handle, dtype, arr, len(seqs), scores.data_ptr(),
+                               _stream_ptr(stream)), "tri_score")
+
+
+def tri_select_topb(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, budget: int,
+                    window: int, kept: torch.Tensor, stream=None):
+    """Top-``budget`` kept slots per head (ascending) into ``kept`` int32
+    [n_seq][n_layers][n_kv_heads][budget] for every sequence that fires."""
+    arr, _ = _seq_array(ctx, seqs, need_kv=False)
+    if kept.dtype != torch.int32 or not kept.is_cuda or not kept.is_contiguous() \
+            or kept.numel() < len(seqs) * ctx.n_heads * budget:
+        raise ValueError("kept must be a contiguous int32 GPU tensor of n_seq*n_heads*budget")
+    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous() \
+            or scores.numel() < scores_count(ctx, seqs):
+        raise ValueError("scores must be a contiguous fp32 GPU tensor")
+    _check(library().tri_select_topb(ctx.handle, arr, len(seqs), scores.data_ptr(), int(budget),
+                                     int(window), kept.data_ptr(), _stream_ptr(stream)),
+           "tri_select_topb")
+
+
+def tri_compact_kv(ctx: Context, seqs: Sequence[Seq], kept: torch.Tensor, budget: int,
+                   window: int, stream=None):
+    """Compacts K, V and positions of every firing sequence in place and sets
+    its ``len`` to ``budget``."""
+    arr, dtype = _seq_array(ctx, seqs, need_kv=True)
+    if kept.dtype != torch.int32 or not kept.is_cuda or not kept.is_contiguous() \
+            or kept.numel() < len(seqs) * ctx.n_heads * budget:
+        raise ValueError("kept must be a contiguous int32 GPU tensor of n_seq*n_heads*budget")
+    _check(library().tri_compact_kv(ctx.handle, dtype, arr, len(seqs), kept.data_ptr(),
+                                    int(budget), int(window), _stream_ptr(stream)),
+           "tri_compact_kv")
+    for i, s in enumerate(seqs):
+        s.len = int(arr[i].len)
+
+
+def fires(seq: Seq, budget: int, window: int) -> bool:
+    """The pruning trigger: a head is pruned iff its length exceeds budget + window."""
+    return seq.len > budget + window
+
+
+def prune_step(ctx: Context, seqs: List[Seq], budget: int, window: int, scores: torch.Tensor,
+               kept: torch.Tensor, stream=None):
+    """One prune step (score, select, compact) on one stream, no host sync."""
+    tri_score(ctx, seqs, scores, stream)
+    tri_select_topb(ctx, seqs, scores, budget, window, kept, stream)
+    tri_compact_kv(ctx, seqs, kept, budget, window, stream)

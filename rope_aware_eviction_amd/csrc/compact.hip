@@ -1,0 +1,114 @@
+// Stable in-place eviction: rows r < B of K, V and positions become the rows
+// at kept[r].
+//
+// Source: dimensionstp.github.io "TriAttention ... Review", section 3-2
+// item 5 (keep the top-budget keys, evict the rest) and section 6 item 1
+// (cache compaction is part of the kernel work the method needs).
+//
+// Hazard.  kept[] is strictly ascending, so kept[r] >= r: row r is only ever
+// filled from itself or from a later row.  Writing row r can therefore only
+// destroy a source needed by a destination r' <= r.  Destinations are
+// processed in ascending tiles; a tile's sources are all read into
+// registers, every wave waits for its reads to land, the workgroup meets at
+// a barrier, and only then is the tile written.  Sources of later tiles are
+// >= their destinations, hence above every row written so far, so a tile's
+// loads never see a clobbered row, and no tile writes a row that an earlier
+// tile still has to read.  One workgroup owns one (head, K or V) stream;
+// positions travel with K.  Rows already in place (kept[r] == r) are
+// skipped.
+#include "tri_internal.h"
+
+namespace tri {
+namespace {
+
+constexpr int kBlock = 512;
+constexpr int kUnroll = 8;
+
+template <int ROWB>
+__global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restrict__ k,
+                                                         unsigned char* __restrict__ v,
+                                                         int32_t* __restrict__ pos, int64_t cap,
+                                                         int len,
+                                                         const int32_t* __restrict__ kept,
+                                                         int budget)
+{
+    constexpr int kChunks = ROWB / 16;          // 16-byte chunks per row
+    constexpr int kRowsPerStep = kBlock / kChunks;
+    constexpr int kTile = kRowsPerStep * kUnroll;
+    static_assert(kTile <= kBlock, "one position per thread per tile");
+
+    const int head = blockIdx.x;
+    const bool is_v = blockIdx.y != 0;
+    unsigned char* rows = (is_v ? v : k) + (size_t)head * (size_t)cap * ROWB;
+    int32_t* hpos = pos + (size_t)head * (size_t)cap;
+    const int32_t* idx = kept + (size_t)head * (size_t)budget;
+
+    const int tid = threadIdx.x;
+    const int c = tid % kChunks;
+    const int rs = tid / kChunks;
+
+    for (int t0 = 0; t0 < budget; t0 += kTile) {
+        u32x4 buf[kUnroll];
+        bool move[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int r = t0 + u * kRowsPerStep + rs;
+            move[u] = false;
+            if (r < budget) {
+                const int src = idx[r];
+                // entries outside [0, len) are ignored rather than followed
+                if (src != r && (unsigned)src < (unsigned)len) {
+                    buf[u] = *reinterpret_cast<const u32x4*>(rows + (size_t)src * ROWB + 16 * c);
+                    move[u] = true;
+                }
+            }
+        }
+        const int pr = t0 + tid;
+        int32_t pval = 0;
+        bool pmove = false;
+        if (!is_v && tid < kTile && pr < budget) {
+            const int src = idx[pr];
+            if (src != pr && (unsigned)src < (unsigned)len) {
+                pval = hpos[src];
+                pmove = true;
+            }
+        }
+        // every read of this tile has landed before any lane writes
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (move[u]) {
+                const int r = t0 + u * kRowsPerStep + rs;
+                *reinterpret_cast<u32x4*>(rows + (size_t)r * ROWB + 16 * c) = buf[u];
+            }
+        }
+        if (pmove) hpos[pr] = pval;
+    }
+}
+
+template <int ROWB>
+hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_heads,
+                  const int32_t* kept, int budget, hipStream_t stream)
+{
+    hipLaunchKernelGGL(compact_kernel<ROWB>, dim3(n_heads, 2), dim3(kBlock), 0, stream,
+                       static_cast<unsigned char*>(k), static_cast<unsigned char*>(v), pos, cap,
+                       len, kept, budget);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
+                          int n_heads, const int32_t* kept, int budget, hipStream_t stream)
+{
+    if (n_heads <= 0 || budget <= 0) return hipSuccess;
+    switch (row_bytes) {
+    case 128: return launch<128>(k, v, pos, cap, len, n_heads, kept, budget, stream);
+    case 256: return launch<256>(k, v, pos, cap, len, n_heads, kept, budget, stream);
+    case 512: return launch<512>(k, v, pos, cap, len, n_heads, kept, budget, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tri

@@ -1,0 +1,195 @@
+// Fused key-score kernel: per cached key, the offset-averaged trigonometric
+// distance-preference series plus the concentration-weighted norm term.
+//
+// Source: romaanj.github.io "TriAttention" review, section "Method" (trig
+// term per band |E q_f| |k_f| cos(w_f * distance + phase difference), norm
+// term weighted by (1 - R_f), averaging over future offsets);
+// dimensionstp.github.io review, section 2-2 (RoPE logit as a per-band
+// cosine series of the query-key distance) and section 3-2 items 2)-4).
+//
+// Algebra.  With the stored (post-RoPE) band K_f = k_f * e^{i w_f p}, the
+// un-rotation e^{-i w_f p} and the distance factor e^{i w_f (p_now + delta - p)}
+// cancel in p, so
+//     trig = sum_f Re( C_f * conj(K_f) ),  C_f = E[q_f] * A_f * e^{i w_f p_now},
+// i.e. the plain dot product of u = [Re C ; Im C] with the stored row, and
+// |k_f| = |K_f|.  C_f is folded in fp64 (w_0 * p_now reaches 1e5 rad, where
+// an fp32 angle would be off by ~1e-2 rad) and rounded to fp32 once per
+// workgroup; each key then costs d FMAs for the dot product, d/2 band
+// energies, d/2 square roots and d/2 FMAs for the norm term, in fp32.
+//
+// Layout.  A row of head_dim elements is two halves (real parts, imaginary
+// parts).  LPR lanes cover one row; lane j loads 16 bytes of each half at
+// byte offset 16*j, so one wave instruction reads 64/LPR whole half-rows,
+// fully coalesced 128-byte lines, and every lane holds matching real and
+// imaginary parts of E = 16/elem_size bands: no cross-lane exchange is needed
+// until the final row sum, which is a DPP butterfly within the LPR lanes.
+#include "tri_internal.h"
+
+namespace tri {
+namespace {
+
+constexpr int kBlock = 256;      // threads per workgroup
+constexpr int kTileRows = 1024;  // rows of one head per workgroup
+constexpr int kUnroll = 4;       // rows per lane kept in flight
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPR consecutive lanes; every lane of the group
+// receives the total.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
+    x += dpp<0xB1>(x);                          // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp<0x4E>(x);                          // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8) x += dpp<0x141>(x);   // row_half_mirror: quads of an 8-lane half
+    if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror: halves of a 16-lane row
+    if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
+template <bool BF16>
+struct Elem;
+
+template <>
+struct Elem<true> {
+    static constexpr int kSize = 2;
+    // 16 bytes = 8 bf16; element 2m sits in the low half of word m.
+    __device__ static __forceinline__ void unpack(const u32x4& v, float* out)
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            out[2 * m] = __uint_as_float(w[m] << 16);
+            out[2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+        }
+    }
+};
+
+template <>
+struct Elem<false> {
+    static constexpr int kSize = 4;
+    __device__ static __forceinline__ void unpack(const u32x4& v, float* out)
+    {
+        out[0] = __uint_as_float(v.x);
+        out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z);
+        out[3] = __uint_as_float(v.w);
+    }
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kBlock) void score_kernel(
+    const unsigned char* __restrict__ k, int64_t cap, int len, int tiles_per_head, double p_now,
+    const double* __restrict__ omega, const double2* __restrict__ qa, const float* __restrict__ w,
+    float* __restrict__ scores)
+{
+    constexpr int kHalf = D / 2;
+    constexpr int kElem = Elem<BF16>::kSize;
+    constexpr int kRowBytes = D * kElem;
+    constexpr int kHalfBytes = kRowBytes / 2;
+    constexpr int LPR = kHalfBytes / 16;   // lanes per row
+    constexpr int E = 16 / kElem;          // bands per lane
+    constexpr int G = kBlock / LPR;        // rows per workgroup step
+
+    __shared__ float s_u[D];
+    __shared__ float s_w[kHalf];
+
+    const int head = blockIdx.x / tiles_per_head;
+    const int tile = blockIdx.x - head * tiles_per_head;
+    const int tid = threadIdx.x;
+
+    // fold C_f = E[q_f] * A_f * e^{i w_f p_now} in fp64, once per workgroup
+    if (tid < kHalf) {
+        double s, c;
+        sincos(omega[tid] * p_now, &s, &c);
+        const double2 a = qa[(size_t)head * kHalf + tid];
+        s_u[tid] = (float)(a.x * c - a.y * s);
+        s_u[tid + kHalf] = (float)(a.x * s + a.y * c);
+        s_w[tid] = w[(size_t)head * kHalf + tid];
+    }
+    __syncthreads();
+
+    const int j = tid % LPR;   // lane within the row
+    const int g = tid / LPR;   // row group within the workgroup
+    float u_re[E], u_im[E], wt[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        u_re[e] = s_u[j * E + e];
+        u_im[e] = s_u[kHalf + j * E + e];
+        wt[e] = s_w[j * E + e];
+    }
+
+    const unsigned char* base = k + (size_t)head * (size_t)cap * kRowBytes + 16 * j;
+    float* out = scores + (size_t)head * (size_t)len;
+    const int row_end = min(len, (tile + 1) * kTileRows);
+
+    for (int r0 = tile * kTileRows + g; r0 < row_end; r0 += G * kUnroll) {
+        u32x4 re[kUnroll], im[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            // rows past the end re-read the last row of the tile (in bounds;
+            // their sums are never stored)
+            const int row = min(r0 + u * G, row_end - 1);
+            const unsigned char* p = base + (size_t)row * kRowBytes;
+            re[u] = *reinterpret_cast<const u32x4*>(p);
+            im[u] = *reinterpret_cast<const u32x4*>(p + kHalfBytes);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = r0 + u * G;
+            float a[E], b[E];
+            Elem<BF16>::unpack(re[u], a);
+            Elem<BF16>::unpack(im[u], b);
+            float dot = 0.f, nrm = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                dot = fmaf(u_re[e], a[e], dot);
+                dot = fmaf(u_im[e], b[e], dot);
+                const float energy = fmaf(a[e], a[e], b[e] * b[e]);
+                nrm = fmaf(wt[e], __builtin_amdgcn_sqrtf(energy), nrm);
+            }
+            // every lane takes part in the DPP sum, also past the row end
+            const float total = group_sum<LPR>(dot + nrm);
+            if (j == 0 && row < row_end) out[row] = total;
+        }
+    }
+}
+
+template <int D, bool BF16>
+hipError_t launch(const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
+                  const double* omega, const double2* qa, const float* w, float* scores,
+                  hipStream_t stream)
+{
+    const int tiles = (len + kTileRows - 1) / kTileRows;
+    const int64_t grid = (int64_t)tiles * n_heads;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((score_kernel<D, BF16>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                       static_cast<const unsigned char*>(k), cap, len, tiles, (double)p_now, omega,
+                       qa, w, scores);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score(tri_dtype dtype, int head_dim, const void* k, int64_t cap, int len,
+                        int n_heads, int64_t p_now, const double* omega, const double2* qa,
+                        const float* w, float* scores, hipStream_t stream)
+{
+    if (len <= 0 || n_heads <= 0) return hipSuccess;
+    if (dtype == TRI_BF16 && head_dim == 128)
+        return launch<128, true>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+    if (dtype == TRI_F32 && head_dim == 64)
+        return launch<64, false>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+    if (dtype == TRI_BF16 && head_dim == 64)
+        return launch<64, true>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+    if (dtype == TRI_F32 && head_dim == 128)
+        return launch<128, false>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tri

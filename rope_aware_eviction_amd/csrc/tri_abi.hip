@@ -1,0 +1,284 @@
+// Host side of the C ABI declared in include/tri.h: argument validation,
+// calibration context, and the launches of one prune step's kernels on the
+// caller's stream.  Validation runs entirely on the host and returns before
+// any HIP call, so argument errors are reported synchronously and without a
+// device.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "tri_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+tri_status hip_fail(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return TRI_E_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported(int head_dim, tri_dtype dtype)
+{
+    return (head_dim == 64 || head_dim == 128) && (dtype == TRI_F32 || dtype == TRI_BF16);
+}
+
+int elem_size(tri_dtype dtype) { return dtype == TRI_F32 ? 4 : 2; }
+
+// The device current on this thread must be the context's.
+tri_status check_device(const tri_ctx* ctx)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    return dev == ctx->device ? TRI_OK : TRI_E_INVAL;
+}
+
+// Shape checks common to every per-step call.
+tri_status check_seqs(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq, bool need_kv)
+{
+    if (!ctx || n_seq < 0 || (n_seq > 0 && !seqs)) return TRI_E_INVAL;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        const tri_seq& q = seqs[s];
+        if (q.cap < 0 || q.len < 0 || q.len > q.cap) return TRI_E_INVAL;
+        if (q.p_now < -(int64_t(1) << 52) || q.p_now > (int64_t(1) << 52)) return TRI_E_INVAL;
+        if (q.len == 0) continue;
+        if (!q.k || !aligned16(q.k)) return TRI_E_INVAL;
+        if (need_kv && (!q.v || !aligned16(q.v) || !q.pos || ((uintptr_t)q.pos & 3u)))
+            return TRI_E_INVAL;
+    }
+    return TRI_OK;
+}
+
+bool fires(const tri_seq& q, int32_t budget, int32_t window)
+{
+    return (int64_t)q.len > (int64_t)budget + (int64_t)window;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tri_status_str(tri_status s)
+{
+    switch (s) {
+    case TRI_OK: return "ok";
+    case TRI_E_INVAL: return "invalid argument";
+    case TRI_E_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case TRI_E_HIP: return "HIP runtime error";
+    case TRI_E_NOMEM: return "out of memory";
+    }
+    return "unknown status";
+}
+
+int tri_last_hip_error(void) { return g_last_hip_error; }
+
+void tri_ctx_destroy(tri_ctx* ctx)
+{
+    if (!ctx) return;
+    int prev = -1;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    if (hipSetDevice(ctx->device) == hipSuccess) {
+        (void)hipFree(ctx->omega);
+        (void)hipFree(ctx->qa);
+        (void)hipFree(ctx->w);
+    }
+    if (have_prev) (void)hipSetDevice(prev);
+    delete ctx;
+}
+
+tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out)
+{
+    if (!out) return TRI_E_INVAL;
+    *out = nullptr;
+    if (!d) return TRI_E_INVAL;
+    if (d->head_dim != 64 && d->head_dim != 128) return TRI_E_UNSUPPORTED;
+    if (d->n_layers < 1 || d->n_kv_heads < 1 || d->n_offsets < 1 || device < 0) return TRI_E_INVAL;
+    if ((int64_t)d->n_layers * d->n_kv_heads > (1 << 24)) return TRI_E_INVAL;
+    if (!d->offsets || !d->qc_re || !d->qc_im || !d->q_mean_norm || !d->q_mrl) return TRI_E_INVAL;
+    const int half = d->head_dim / 2;
+    const int n_heads = d->n_layers * d->n_kv_heads;
+    const size_t nb = (size_t)n_heads * half;
+    if (d->inv_freq) {
+        for (int f = 0; f < half; ++f)
+            if (!std::isfinite(d->inv_freq[f]) || !(d->inv_freq[f] > 0.0)) return TRI_E_INVAL;
+    } else if (!std::isfinite(d->rope_theta) || !(d->rope_theta > 0.0)) {
+        return TRI_E_INVAL;
+    }
+    for (int o = 0; o < d->n_offsets; ++o)
+        if (d->offsets[o] < 0 || d->offsets[o] > (int64_t(1) << 40)) return TRI_E_INVAL;
+    for (size_t i = 0; i < nb; ++i) {
+        if (!std::isfinite(d->qc_re[i]) || !std::isfinite(d->qc_im[i])) return TRI_E_INVAL;
+        if (!std::isfinite(d->q_mean_norm[i]) || d->q_mean_norm[i] < 0.0) return TRI_E_INVAL;
+        if (!(d->q_mrl[i] >= 0.0 && d->q_mrl[i] <= 1.0)) return TRI_E_INVAL;
+    }
+
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipSetDevice(device);
+    if (e != hipSuccess) return hip_fail(e);
+
+    tri_ctx* ctx = new (std::nothrow) tri_ctx{};
+    if (!ctx) {
+        (void)hipSetDevice(prev);
+        return TRI_E_NOMEM;
+    }
+    ctx->device = device;
+    ctx->n_layers = d->n_layers;
+    ctx->n_kv_heads = d->n_kv_heads;
+    ctx->head_dim = d->head_dim;
+    ctx->n_heads = n_heads;
+
+    // raw table staged on the device, derived tables computed there in fp64
+    double *r_inv = nullptr, *r_re = nullptr, *r_im = nullptr, *r_m = nullptr, *r_R = nullptr;
+    int64_t* r_off = nullptr;
+    tri_status st = TRI_OK;
+    auto alloc = [&](void** p, size_t bytes) {
+        if (st != TRI_OK) return;
+        hipError_t a = hipMalloc(p, bytes);
+        if (a != hipSuccess) {
+            g_last_hip_error = (int)a;
+            st = a == hipErrorOutOfMemory ? TRI_E_NOMEM : TRI_E_HIP;
+        }
+    };
+    auto put = [&](void* dst, const void* src, size_t bytes) {
+        if (st != TRI_OK) return;
+        hipError_t c = hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
+        if (c != hipSuccess) st = hip_fail(c);
+    };
+    alloc((void**)&ctx->omega, sizeof(double) * half);
+    alloc((void**)&ctx->qa, sizeof(double2) * nb);
+    alloc((void**)&ctx->w, sizeof(float) * nb);
+    if (d->inv_freq) alloc((void**)&r_inv, sizeof(double) * half);
+    alloc((void**)&r_off, sizeof(int64_t) * d->n_offsets);
+    alloc((void**)&r_re, sizeof(double) * nb);
+    alloc((void**)&r_im, sizeof(double) * nb);
+    alloc((void**)&r_m, sizeof(double) * nb);
+    alloc((void**)&r_R, sizeof(double) * nb);
+    if (d->inv_freq) put(r_inv, d->inv_freq, sizeof(double) * half);
+    put(r_off, d->offsets, sizeof(int64_t) * d->n_offsets);
+    put(r_re, d->qc_re, sizeof(double) * nb);
+    put(r_im, d->qc_im, sizeof(double) * nb);
+    put(r_m, d->q_mean_norm, sizeof(double) * nb);
+    put(r_R, d->q_mrl, sizeof(double) * nb);
+    if (st == TRI_OK) {
+        e = tri::launch_calibrate(n_heads, d->head_dim, d->rope_theta, r_inv, r_off, d->n_offsets,
+                                  r_re, r_im, r_m, r_R, ctx->omega, ctx->qa, ctx->w, nullptr);
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) st = hip_fail(e);
+    }
+    (void)hipFree(r_inv);
+    (void)hipFree(r_off);
+    (void)hipFree(r_re);
+    (void)hipFree(r_im);
+    (void)hipFree(r_m);
+    (void)hipFree(r_R);
+    if (st != TRI_OK) {
+        (void)hipFree(ctx->omega);
+        (void)hipFree(ctx->qa);
+        (void)hipFree(ctx->w);
+        delete ctx;
+        (void)hipSetDevice(prev);
+        return st;
+    }
+    (void)hipSetDevice(prev);
+    *out = ctx;
+    return TRI_OK;
+}
+
+int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
+{
+    if (!ctx || n_seq < 0 || (n_seq > 0 && !seqs)) return -1;
+    int64_t total = 0;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        if (seqs[s].len < 0) return -1;
+        total += (int64_t)ctx->n_heads * seqs[s].len;
+    }
+    return total;
+}
+
+tri_status tri_score(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, int32_t n_seq,
+                     float* scores, void* stream)
+{
+    tri_status st = check_seqs(ctx, seqs, n_seq, false);
+    if (st != TRI_OK) return st;
+    if (!supported(ctx->head_dim, dtype)) return TRI_E_UNSUPPORTED;
+    const int64_t total = tri_scores_count(ctx, seqs, n_seq);
+    if (total > 0 && (!scores || ((uintptr_t)scores & 3u))) return TRI_E_INVAL;
+    if (total == 0) return TRI_OK;
+    st = check_device(ctx);
+    if (st != TRI_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int64_t off = 0;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        const tri_seq& q = seqs[s];
+        if (q.len > 0) {
+            hipError_t e = tri::launch_score(dtype, ctx->head_dim, q.k, q.cap, q.len, ctx->n_heads,
+                                             q.p_now, ctx->omega, ctx->qa, ctx->w, scores + off,
+                                             hs);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        off += (int64_t)ctx->n_heads * q.len;
+    }
+    return TRI_OK;
+}
+
+tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
+                           const float* scores, int32_t budget, int32_t window, int32_t* kept,
+                           void* stream)
+{
+    tri_status st = check_seqs(ctx, seqs, n_seq, false);
+    if (st != TRI_OK) return st;
+    if (budget < 1 || window < 0) return TRI_E_INVAL;
+    bool any = false;
+    for (int32_t s = 0; s < n_seq; ++s) any = any || fires(seqs[s], budget, window);
+    if (!any) return TRI_OK;
+    if (!scores || !kept || ((uintptr_t)scores & 3u) || ((uintptr_t)kept & 3u)) return TRI_E_INVAL;
+    st = check_device(ctx);
+    if (st != TRI_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int64_t off = 0;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        const tri_seq& q = seqs[s];
+        if (fires(q, budget, window)) {
+            hipError_t e = tri::launch_select(scores + off, q.len, ctx->n_heads, budget,
+                                              kept + (int64_t)s * ctx->n_heads * budget, hs);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        off += (int64_t)ctx->n_heads * q.len;
+    }
+    return TRI_OK;
+}
+
+tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, int32_t n_seq,
+                          const int32_t* kept, int32_t budget, int32_t window, void* stream)
+{
+    tri_status st = check_seqs(ctx, seqs, n_seq, true);
+    if (st != TRI_OK) return st;
+    if (!supported(ctx->head_dim, dtype)) return TRI_E_UNSUPPORTED;
+    if (budget < 1 || window < 0) return TRI_E_INVAL;
+    bool any = false;
+    for (int32_t s = 0; s < n_seq; ++s) any = any || fires(seqs[s], budget, window);
+    if (!any) return TRI_OK;
+    if (!kept || ((uintptr_t)kept & 3u)) return TRI_E_INVAL;
+    st = check_device(ctx);
+    if (st != TRI_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int row_bytes = ctx->head_dim * elem_size(dtype);
+    for (int32_t s = 0; s < n_seq; ++s) {
+        tri_seq& q = seqs[s];
+        if (!fires(q, budget, window)) continue;
+        hipError_t e = tri::launch_compact(row_bytes, q.k, q.v, q.pos, q.cap, q.len, ctx->n_heads,
+                                           kept + (int64_t)s * ctx->n_heads * budget, budget, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        q.len = budget;
+    }
+    return TRI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal declarations shared by the HIP translation units of libtri.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tri.h"
+
+struct tri_ctx {
+    int device;
+    int n_layers;
+    int n_kv_heads;
+    int head_dim;
+    int n_heads;          // n_layers * n_kv_heads
+    double* omega;        // device [head_dim/2]        band frequencies
+    double2* qa;          // device [n_heads][head_dim/2] E[q_f] * A_f (complex, fp64)
+    float* w;             // device [n_heads][head_dim/2] (1 - R_f) * E|q_f|
+};
+
+namespace tri {
+
+// 16-byte native vector: loads and stores of it are single dwordx4 memory
+// instructions, and arrays of it stay in registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Launchers (one per kernel family).  Each enqueues on `stream` and returns
+// the launch's hipError_t.
+
+hipError_t launch_calibrate(int n_heads, int head_dim, double rope_theta, const double* inv_freq,
+                            const int64_t* offsets, int n_offsets, const double* qc_re,
+                            const double* qc_im, const double* q_mean_norm, const double* q_mrl,
+                            double* omega, double2* qa, float* w, hipStream_t stream);
+
+// Scores rows [0, len) of n_heads heads of one sequence.
+hipError_t launch_score(tri_dtype dtype, int head_dim, const void* k, int64_t cap, int len,
+                        int n_heads, int64_t p_now, const double* omega, const double2* qa,
+                        const float* w, float* scores, hipStream_t stream);
+
+// Top-`budget` of each of n_heads score rows of length n.
+hipError_t launch_select(const float* scores, int n, int n_heads, int budget, int32_t* kept,
+                         hipStream_t stream);
+
+// In-place stable gather of the first `budget` rows of every head.
+hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
+                          int n_heads, const int32_t* kept, int budget, hipStream_t stream);
+
+}  // namespace tri
