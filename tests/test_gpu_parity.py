@@ -405,21 +405,30 @@ def test_fused_mixed_firing_batch(orc):
 
 
 def test_exact_duplicate_rows_keep_the_lower_slot(orc):
-    """Bit-identical stored rows score bit-identically on the GPU; at the
-    threshold the lower slot must be kept."""
-    spec = synth.workload("llama8b").replace(name="dups", n_layers=1, n_kv_heads=2, lengths=(4000,), budget=1000)
+    """Bit-identical stored rows score bit-identically on the GPU.  With every
+    row stored twice (slots i and i + 2000) and an odd budget 2m - 1, the top
+    m - 1 pairs are kept whole and of the m-th pair only the lower slot."""
+    B = 999
+    spec = synth.workload("llama8b").replace(name="dups", n_layers=1, n_kv_heads=2, lengths=(4000,),
+                                             budget=B)
     cache = synth.make_cache(spec, "cuda", seed=11)
     K = cache.k[0]
-    K[:, :, 2000:4000] = K[:, :, 0:2000].clone()       # every row appears twice
+    K[:, :, 2000:4000] = K[:, :, 0:2000].clone()
     ctx = ctx_for(cache)
     seqs = seqs_for(cache)
     scores = torch.empty(2 * 4000, device="cuda")
-    kept = torch.empty(2 * 1000, dtype=torch.int32, device="cuda")
+    kept = torch.empty(2 * B, dtype=torch.int32, device="cuda")
     tri.tri_score(ctx, seqs, scores)
-    tri.tri_select_topb(ctx, seqs, scores, 1000, 128, kept)
+    tri.tri_select_topb(ctx, seqs, scores, B, 128, kept)
     torch.cuda.synchronize()
     sc = scores.view(2, 4000)
-    assert torch.equal(sc[:, :2000], sc[:, 2000:])
-    check_topb_property(sc, kept.view(2, 1000), 4000)
-    # 1000 of 2000 distinct rows, each twice: the copies in 2000.. never win
-    assert int(kept.max()) < 2000
+    assert torch.equal(bits(sc[:, :2000]), bits(sc[:, 2000:]))
+    check_topb_property(sc, kept.view(2, B), 4000)
+    for h in range(2):
+        # the definition on the GPU's own scores: stable sort by score, descending
+        order = torch.sort(-sc[h], stable=True).indices[:B]
+        assert torch.equal(kept.view(2, B)[h], torch.sort(order).values.int())
+        kk = kept.view(2, B)[h].cpu().numpy()
+        lo, hi = kk[kk < 2000], kk[kk >= 2000] - 2000
+        # a kept copy at i + 2000 implies the kept copy at i; B odd splits a pair
+        assert set(hi.tolist()) <= set(lo.tolist()) and len(lo) > len(hi)
