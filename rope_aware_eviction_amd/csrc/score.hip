@@ -31,6 +31,8 @@ namespace {
 constexpr int kBlock = 256;      // threads per workgroup
 constexpr int kTileRows = 1024;  // rows of one head per workgroup
 constexpr int kUnroll = 4;       // rows per lane kept in flight
+// word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
@@ -102,20 +104,37 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
     const int head = blockIdx.x / tiles_per_head;
     const int tile = blockIdx.x - head * tiles_per_head;
     const int tid = threadIdx.x;
+    const int j = tid % LPR;   // lane within the row
+    const int g = tid / LPR;   // row group within the workgroup
+    const unsigned char* base = k + (size_t)head * (size_t)cap * kRowBytes + 16 * j;
+    float* out = scores + (size_t)head * (size_t)len;
+    const int row_end = min(len, (tile + 1) * kTileRows);
+
+    // K is streamed once: non-temporal loads keep it from displacing the
+    // scores and constants in the caches.  Rows past the end of the tile
+    // re-read its last row (in bounds, cache hits; their sums are dropped).
+    u32x4 re[kUnroll], im[kUnroll];
+    auto load_row = [&](int u, int row) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(base + (size_t)min(row, row_end - 1) * kRowBytes);
+        re[u] = __builtin_nontemporal_load(p);
+        im[u] = __builtin_nontemporal_load(p + kHalfBytes / 16);
+    };
+    const int tile_start = tile * kTileRows;
+    const int iters = (row_end - tile_start + G * kUnroll - 1) / (G * kUnroll);   // uniform
+    int r0 = tile_start + g;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) load_row(u, r0 + u * G);   // in flight during the fold
 
     // fold C_f = E[q_f] * A_f * e^{i w_f p_now} in fp64, once per workgroup
     if (tid < kHalf) {
-        double s, c;
-        sincos(omega[tid] * p_now, &s, &c);
+        double sn, cs;
+        sincos(omega[tid] * p_now, &sn, &cs);
         const double2 a = qa[(size_t)head * kHalf + tid];
-        s_u[tid] = (float)(a.x * c - a.y * s);
-        s_u[tid + kHalf] = (float)(a.x * s + a.y * c);
+        s_u[tid] = (float)(a.x * cs - a.y * sn);
+        s_u[tid + kHalf] = (float)(a.x * sn + a.y * cs);
         s_w[tid] = w[(size_t)head * kHalf + tid];
     }
     __syncthreads();
-
-    const int j = tid % LPR;   // lane within the row
-    const int g = tid / LPR;   // row group within the workgroup
     float u_re[E], u_im[E], wt[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -124,27 +143,29 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
         wt[e] = s_w[j * E + e];
     }
 
-    const unsigned char* base = k + (size_t)head * (size_t)cap * kRowBytes + 16 * j;
-    float* out = scores + (size_t)head * (size_t)len;
-    const int row_end = min(len, (tile + 1) * kTileRows);
+    // Scores leave through a bounds-checked buffer store: lanes that must not
+    // write (all but the first lane of a row, rows past the tile) get an
+    // offset beyond the head's range, which the hardware drops.  With no
+    // branch in the loop, the compiler can track how many loads are in
+    // flight across iterations instead of draining them at the loop head.
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out, 0, len * 4, kBufferWord3);
+    constexpr int kDropped = 0x7FFFFFF0;
 
-    for (int r0 = tile * kTileRows + g; r0 < row_end; r0 += G * kUnroll) {
-        u32x4 re[kUnroll], im[kUnroll];
+    // Rolling pipeline: as soon as row u of this batch is consumed, the same
+    // registers start loading row u of the next batch, so every wave keeps
+    // kUnroll - 1 to kUnroll rows in flight while it computes.
+    for (int it = 0; it < iters; ++it) {
+        const int r_next = r0 + G * kUnroll;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            // rows past the end re-read the last row of the tile (in bounds;
-            // their sums are never stored)
-            const int row = min(r0 + u * G, row_end - 1);
-            const unsigned char* p = base + (size_t)row * kRowBytes;
-            re[u] = *reinterpret_cast<const u32x4*>(p);
-            im[u] = *reinterpret_cast<const u32x4*>(p + kHalfBytes);
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int row = r0 + u * G;
             float a[E], b[E];
             Elem<BF16>::unpack(re[u], a);
             Elem<BF16>::unpack(im[u], b);
+            load_row(u, r_next + u * G);
+            // keep the scheduler from regrouping the stages (it would drain
+            // every load first and issue the next batch after the compute)
+            __builtin_amdgcn_sched_barrier(0);
             float dot = 0.f, nrm = 0.f;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
@@ -153,10 +174,13 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
                 const float energy = fmaf(a[e], a[e], b[e] * b[e]);
                 nrm = fmaf(wt[e], __builtin_amdgcn_sqrtf(energy), nrm);
             }
-            // every lane takes part in the DPP sum, also past the row end
             const float total = group_sum<LPR>(dot + nrm);
-            if (j == 0 && row < row_end) out[row] = total;
+            const int row = r0 + u * G;
+            const int off = (j == 0 && row < row_end) ? row * 4 : kDropped;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out_rsrc, off, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        r0 = r_next;
     }
 }
 

@@ -25,17 +25,31 @@ namespace {
 constexpr int kBlock = 1024;
 constexpr int kWaves = kBlock / 64;
 constexpr int kMaxDigitBits = 11;
+constexpr int kBatch = 8;        // keys per thread loaded before any is used
+// word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format
+constexpr int kBufferWord3 = 0x00020000;
+// stands for every key above the candidate range once phase A has run
+// (no score maps to it: +inf maps to 0xFF800000)
+constexpr uint32_t kTopKey = 0xFFFFFFFFu;
 constexpr int kHistBins = 1 << kMaxDigitBits;
 // keys of a head staged in LDS up to this many (4 bytes each, plus the
 // 8 KB histogram, within the 160 KB LDS of a gfx950 workgroup)
 constexpr int kLdsKeysMax = 36864;
 
+// Order-preserving map of fp32 scores to uint32 keys.  Key 0 is never
+// produced (it marks slots past the end of a head, below every real key).
 __device__ __forceinline__ uint32_t ordered_key(float x)
 {
-    if (x != x) return 0u;                   // NaN below every number
+    if (x != x) return 1u;                   // NaN below every number
     uint32_t u = __float_as_uint(x);
     if (u == 0x80000000u) u = 0u;            // -0 equals +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of ordered_key for keys of numbers (key >= 2).
+__device__ __forceinline__ float key_to_float(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 template <bool kInLds>
@@ -49,6 +63,13 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v)
 {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
     return v;
 }
 
@@ -78,11 +99,20 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict_
 
     // stage keys (when they fit) and find the key range of the head
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int i = tid; i < n; i += kBlock) {
-        const uint32_t key = ordered_key(sc[i]);
-        if constexpr (kInLds) lds_keys[i] = key;
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
+    for (int i0 = tid; i0 < n; i0 += kBlock * kBatch) {
+        float x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) x[u] = sc[min(i0 + u * kBlock, n - 1)];   // kBatch loads in flight
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = i0 + u * kBlock;
+            if (i < n) {
+                const uint32_t key = ordered_key(x[u]);
+                if constexpr (kInLds) lds_keys[i] = key;
+                kmin = min(kmin, key);
+                kmax = max(kmax, key);
+            }
+        }
     }
     kmin = wave_min(kmin);
     kmax = wave_max(kmax);
@@ -119,9 +149,14 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict_
             const uint32_t dmask = nbins - 1u;
             for (uint32_t b = tid; b < nbins; b += kBlock) hist[b] = 0u;
             __syncthreads();
-            for (int i = tid; i < n; i += kBlock) {
-                const uint32_t key = key_at<kInLds>(lds_keys, sc, i);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+            for (int i0 = tid; i0 < n; i0 += kBlock * kBatch) {
+                uint32_t key[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) key[u] = key_at<kInLds>(lds_keys, sc, min(i0 + u * kBlock, n - 1));
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    if (i0 + u * kBlock < n && (key[u] & pmask) == prefix)
+                        atomicAdd(&hist[(key[u] >> shift) & dmask], 1u);
             }
             __syncthreads();
             if (wave == 0) {
@@ -212,13 +247,287 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict_
     }
 }
 
+// Digit holding the rem-th largest counted key: wave 0 scans the histogram
+// from the top in two levels (64 runs of `per` bins, then the bins of the
+// run that crosses rem), each an inclusive scan over the lanes.  Writes the
+// digit, the count in higher bins and the count in the digit's bin.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nbins, uint32_t rem,
+                                           int lane, uint32_t* s_digit, uint32_t* s_above,
+                                           uint32_t* s_inbin)
+{
+    const uint32_t per = nbins >= 64u ? nbins / 64u : 1u;      // <= 32
+    const uint32_t top = nbins - 1u - (uint32_t)lane * per;      // first bin of this lane's run
+    uint32_t sum = 0u;
+    if ((uint32_t)lane * per < nbins)
+        for (uint32_t t = 0; t < per; ++t) sum += hist[top - t];
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)incl, o);
+        if (lane >= o) incl += v;
+    }
+    const int L = __ffsll((long long)__ballot(incl >= rem)) - 1;
+    const uint32_t above_run = (uint32_t)__shfl((int)(incl - sum), L);
+    const uint32_t run_top = nbins - 1u - (uint32_t)L * per;
+    const uint32_t h = (uint32_t)lane < per ? hist[run_top - lane] : 0u;
+    uint32_t incl2 = h;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)incl2, o);
+        if (lane >= o) incl2 += v;
+    }
+    incl2 += above_run;
+    const int L2 = __ffsll((long long)__ballot((uint32_t)lane < per && incl2 >= rem)) - 1;
+    if (lane == L2) {
+        *s_digit = run_top - (uint32_t)L2;
+        *s_above = incl2 - h;
+        *s_inbin = h;
+    }
+}
+
+// Sorts one value per lane of a wave in descending order (bitonic network).
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane)
+{
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t p = (uint32_t)__shfl_xor((int)v, j);
+            const bool first = (lane & k) == 0;        // block sorted descending
+            const bool lower = (lane & j) == 0;        // lower lane of the pair
+            v = (first == lower) ? max(v, p) : min(v, p);
+        }
+    }
+    return v;
+}
+
+// Register-resident variant for heads of at most NT * KPT keys (NT threads):
+// lane l of wave w holds the keys of slots w*64*KPT + c*64 + l, c < KPT,
+// which is the order the output sweep consumes them in.  LDS holds only the
+// histogram and a short candidate list.
+//
+// Radix select on offsets: all live keys lie in [base, base + 2^wb); each
+// pass histograms (key - base) >> (wb - 11) into 2048 bins, so the bins
+// always span the populated key range (the keys of concentrated scores sit
+// in a narrow range, often straddling a power of two, and a bit-aligned
+// digit would pile them into a few bins).  Keys above the chosen bin are
+// kept, keys below it evicted.  Once at most 64 candidates are left, one
+// wave sorts them in registers and reads off the threshold.  The result is
+// either "keep every key >= Tlo" (exactly B keys) or, when equal keys
+// straddle the threshold, "keep keys > T and the first need_eq keys == T in
+// slot order".
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict__ scores,
+                                                        int n, int budget,
+                                                        int32_t* __restrict__ kept)
+{
+    constexpr int kW = NT / 64;
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t s_cand[64];
+    __shared__ uint32_t s_wa[kW], s_wb[kW];
+    __shared__ uint32_t s_digit, s_above, s_inbin, s_ncand;
+    __shared__ uint32_t s_T, s_need, s_tie;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const float* sc = scores + (size_t)blockIdx.x * (size_t)n;
+    int32_t* out = kept + (size_t)blockIdx.x * (size_t)budget;
+    const int seg0 = wave * (64 * KPT) + lane;     // slot of key[0]
+
+    // Slots past the head's end hold key 0, below every real key (ordered_key
+    // never returns 0): with budget < n they are never kept.
+    uint32_t key[KPT];
+    {
+        // bounds-checked buffer loads: one offset register for all KPT loads
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)sc, 0, n * 4, kBufferWord3);
+        uint32_t x[KPT];
+#pragma unroll
+        for (int c = 0; c < KPT; ++c)
+            x[c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (seg0 + 64 * c) * 4, 0, 0);
+#pragma unroll
+        for (int c = 0; c < KPT; ++c)
+            key[c] = seg0 + 64 * c < n ? ordered_key(__uint_as_float(x[c])) : 0u;
+    }
+
+    uint32_t kmin, kmax;
+    {
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+            lo = min(lo, key[c] ? key[c] : 0xFFFFFFFFu);
+            hi = max(hi, key[c]);
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) {
+            s_wa[wave] = lo;
+            s_wb[wave] = hi;
+        }
+        __syncthreads();
+        kmin = s_wa[0];
+        kmax = s_wb[0];
+        for (int x = 1; x < kW; ++x) {
+            kmin = min(kmin, s_wa[x]);
+            kmax = max(kmax, s_wb[x]);
+        }
+    }
+
+    // Decision: tie = false -> keep key >= T (exactly budget keys);
+    //           tie = true  -> keep key > T, then the first need_eq keys == T.
+    uint32_t T, need_eq;
+    bool tie;
+    if (kmin == kmax) {
+        T = kmin;
+        need_eq = (uint32_t)budget;
+        tie = true;
+    } else {
+        uint32_t base = kmin;
+        int wb = 32 - __clz((int)(kmax - kmin));       // live keys: [base, base + 2^wb)
+        uint32_t rem = (uint32_t)budget;
+        for (;;) {
+            const int nb = min(kMaxDigitBits, wb);
+            const int sh = wb - nb;
+            const uint32_t nbins = 1u << nb;
+            const uint32_t span = wb >= 32 ? 0xFFFFFFFFu : (1u << wb) - 1u;
+            __syncthreads();                            // previous readers of hist / s_*
+            for (uint32_t b = tid; b < nbins; b += NT) hist[b] = 0u;
+            if (tid == 0) s_ncand = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < KPT; ++c) {
+                const uint32_t off = key[c] - base;
+                if (off <= span && key[c]) atomicAdd(&hist[off >> sh], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) find_digit(hist, nbins, rem, lane, &s_digit, &s_above, &s_inbin);
+            __syncthreads();
+            const uint32_t d = s_digit & (nbins - 1u);
+            const uint32_t in_bin = s_inbin;
+            rem -= s_above;
+            base += d << sh;
+            wb = sh;
+            if (rem == in_bin) {            // the whole bin is kept
+                T = base;
+                need_eq = 0u;
+                tie = false;
+                break;
+            }
+            if (wb == 0) {                  // the bin is one key value: equal keys straddle
+                T = base;
+                need_eq = rem;
+                tie = true;
+                break;
+            }
+            if (in_bin <= 64u) {
+                // stage the few candidates and let one wave sort them
+                const uint32_t cspan = (1u << wb) - 1u;
+#pragma unroll
+                for (int c = 0; c < KPT; ++c) {
+                    const uint32_t off = key[c] - base;
+                    if (off <= cspan && key[c]) {
+                        const uint32_t at = atomicAdd(&s_ncand, 1u);
+                        if (at < 64u) s_cand[at] = key[c];
+                    }
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    const uint32_t v = wave_sort_desc((uint32_t)lane < in_bin ? s_cand[lane] : 0u, lane);
+                    const uint32_t t = (uint32_t)__shfl((int)v, (int)rem - 1);
+                    const uint32_t g = (uint32_t)__popcll(__ballot(v > t));
+                    const uint32_t e = (uint32_t)__popcll(__ballot(v == t));
+                    if (lane == 0) {
+                        s_T = t;
+                        s_need = rem - g;
+                        s_tie = (rem - g) != e;
+                    }
+                }
+                __syncthreads();
+                T = s_T;
+                need_eq = s_need;
+                tie = s_tie != 0u;
+                break;
+            }
+        }
+    }
+
+    // ---- output sweeps
+    // an opaque copy of T keeps the compiler from carrying the counting
+    // sweep's comparison masks over into the writing sweep
+    uint32_t T2 = T;
+    asm volatile("" : "+v"(T2));
+    const unsigned long long below = (1ull << lane) - 1ull;
+    if (!tie) {
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) cnt += key[c] >= T ? 1u : 0u;
+        cnt = wave_sum(cnt);
+        __syncthreads();
+        if (lane == 0) s_wa[wave] = cnt;
+        __syncthreads();
+        uint32_t at0 = 0u;
+        for (int x = 0; x < wave; ++x) at0 += s_wa[x];
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+            const bool keep = key[c] >= T2;
+            const unsigned long long m = __ballot(keep);
+            const uint32_t at = at0 + (uint32_t)__popcll(m & below);
+            if (keep && at < (uint32_t)budget) out[at] = seg0 + 64 * c;
+            at0 += (uint32_t)__popcll(m);
+        }
+    } else {
+        uint32_t cgt = 0u, ceq = 0u;
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+            cgt += key[c] > T ? 1u : 0u;
+            ceq += key[c] == T ? 1u : 0u;
+        }
+        cgt = wave_sum(cgt);
+        ceq = wave_sum(ceq);
+        __syncthreads();
+        if (lane == 0) {
+            s_wa[wave] = cgt;
+            s_wb[wave] = ceq;
+        }
+        __syncthreads();
+        uint32_t gt_before = 0u, eq_before = 0u;
+        for (int x = 0; x < wave; ++x) {
+            gt_before += s_wa[x];
+            eq_before += s_wb[x];
+        }
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+            const bool gt = key[c] > T2;
+            const bool eq = key[c] == T2;
+            const unsigned long long mgt = __ballot(gt);
+            const unsigned long long meq = __ballot(eq);
+            const uint32_t my_gt = gt_before + (uint32_t)__popcll(mgt & below);
+            const uint32_t my_eq = eq_before + (uint32_t)__popcll(meq & below);
+            const uint32_t at = my_gt + min(my_eq, need_eq);
+            if ((gt || (eq && my_eq < need_eq)) && at < (uint32_t)budget) out[at] = seg0 + 64 * c;
+            gt_before += (uint32_t)__popcll(mgt);
+            eq_before += (uint32_t)__popcll(meq);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_select(const float* scores, int n, int n_heads, int budget, int32_t* kept,
                          hipStream_t stream)
 {
     if (n_heads <= 0 || n <= budget) return hipSuccess;
-    if (n <= kLdsKeysMax) {
+    if (n <= kBlock * 8) {
+        hipLaunchKernelGGL((select_reg_kernel<8, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
+                           scores, n, budget, kept);
+    } else if (n <= kBlock * 16) {
+        hipLaunchKernelGGL((select_reg_kernel<16, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
+                           scores, n, budget, kept);
+    } else if (n <= kBlock * 32) {
+        hipLaunchKernelGGL((select_reg_kernel<32, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
+                           scores, n, budget, kept);
+    } else if (n <= kLdsKeysMax) {
         const size_t lds = (size_t)(kHistBins + n) * sizeof(uint32_t);
         static bool attr_set = false;
         if (!attr_set) {

@@ -380,6 +380,8 @@ def make_scores(kind: str, n_heads: int, n: int, seed: int = 0) -> np.ndarray:
     kinds: ``normal`` (i.i.d. N(0,1)), ``ties`` (values from a 7-element set),
     ``allequal``, ``special`` (NaN, +/-inf, +/-0 and denormals mixed in),
     ``dups`` (normal with 30% exact duplicates of other slots),
+    ``straddle`` (concentrated around 2.0), ``outlier`` (normal plus one
+    +1e30 and one -1e30), ``narrow`` (all within a few ulps of 1.0),
     ``ulp`` (clusters of values one fp32 ulp apart).
     """
     rng = _np_rng(seed, "scores", kind, n_heads, n)
@@ -401,6 +403,18 @@ def make_scores(kind: str, n_heads: int, n: int, seed: int = 0) -> np.ndarray:
             tgt = rng.random(n) < 0.3
             src = rng.integers(0, n, size=int(tgt.sum()))
             s[h, tgt] = s[h, src]
+    elif kind == "straddle":
+        # concentrated around 2.0: keys differ in the exponent bits
+        s = (2.0 + 0.05 * rng.standard_normal((n_heads, n))).astype(np.float32)
+    elif kind == "outlier":
+        s = rng.standard_normal((n_heads, n)).astype(np.float32)
+        s[:, int(rng.integers(0, n))] = 1e30
+        s[:, int(rng.integers(0, n))] = -1e30
+    elif kind == "narrow":
+        # every score within a few ulps of 1.0
+        base = np.full((n_heads, n), 1.0, dtype=np.float32)
+        steps = rng.integers(0, 6, size=(n_heads, n)).astype(np.int32)
+        s = (base.view(np.int32) + steps).view(np.float32)
     elif kind == "ulp":
         base = rng.standard_normal((n_heads, max(n // 16, 1))).astype(np.float32)
         idx = rng.integers(0, base.shape[1], size=(n_heads, n))

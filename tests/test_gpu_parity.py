@@ -222,7 +222,9 @@ SELECT_CASES = [
     ("normal", 1000, 100), ("normal", 4097, 2048), ("ties", 3000, 700), ("allequal", 2500, 300),
     ("special", 5000, 1234), ("dups", 8192, 2048), ("ulp", 32768, 4096), ("normal", 36864, 4096),
     ("ties", 36865, 5000), ("special", 70001, 8192), ("ulp", 131072, 8192), ("normal", 300, 299),
-    ("normal", 129, 1),
+    ("normal", 129, 1), ("straddle", 32768, 4096), ("straddle", 20000, 2048),
+    ("outlier", 32768, 4096), ("outlier", 7000, 3500), ("narrow", 32768, 4096), ("narrow", 9000, 100),
+    ("straddle", 131072, 8192), ("outlier", 36000, 1000),
 ]
 
 
