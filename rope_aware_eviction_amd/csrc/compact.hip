@@ -6,18 +6,24 @@
 // (cache compaction is part of the kernel work the method needs).
 //
 // Hazard.  kept[] is strictly ascending, so kept[r] >= r: row r is only ever
-// filled from itself or from a later row.  Writing row r can therefore only
-// destroy a source needed by a destination r' <= r.  Destinations are
-// processed in ascending tiles; a tile's sources are all read into
-// registers, every wave waits for its reads to land, the workgroup meets at
-// a barrier, and only then is the tile written.  Sources of later tiles are
-// >= their destinations, hence above every row written so far, so a tile's
-// loads never see a clobbered row, and no tile writes a row that an earlier
-// tile still has to read.  One workgroup owns one (head, K or V) stream;
-// positions travel with K.  Rows already in place (kept[r] == r) are
-// skipped.  Rows are moved with non-temporal loads and stores: every byte
-// is touched once, and streaming past the caches measures ~5% faster for
-// copies on this part.
+// filled from itself or from a later row, and writing row r can only destroy
+// a source needed by a destination r' <= r.  Destinations are processed in
+// ascending tiles of T rows: tile t reads rows >= tT and writes rows
+// [tT, (t+1)T).  Its writes may destroy sources of tiles <= t only, so a
+// tile is written once the reads of every tile up to it have landed; reads
+// of later tiles never touch rows written so far.  One workgroup owns one
+// (head, K or V) stream and walks its tiles in order; positions travel with
+// K.
+//
+// Pipeline.  The loads of tile t+1 are issued before the stores of tile t,
+// then the workgroup waits until those loads (not the stores, which share
+// the in-order memory counter) have landed and meets at a barrier.  Every
+// load and store is an unconditional bounds-checked buffer access (rows that
+// need no move get an offset past the buffer, which the hardware drops), so
+// the number of memory instructions per tile is fixed and the wait can
+// count them exactly.  The head's kept list is staged in LDS so index reads
+// stay off the memory counter.  Rows are moved with non-temporal accesses:
+// every byte is touched once.
 #include "tri_internal.h"
 
 namespace tri {
@@ -25,6 +31,19 @@ namespace {
 
 constexpr int kBlock = 512;
 constexpr int kUnroll = 8;
+constexpr int kIdxChunk = 8192;                 // kept entries staged in LDS at a time
+constexpr uint32_t kDrop = 0xFFFFFFC0u;          // buffer offset that is always out of range
+constexpr int kBufferWord3 = 0x00020000;         // raw buffer resource word 3, gfx9 family
+constexpr int kNT = 2;                           // cache-policy bits: non-temporal
+
+// s_waitcnt with only the vector-memory count bounded (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 template <int ROWB>
 __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restrict__ k,
@@ -34,66 +53,102 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
                                                          const int32_t* __restrict__ kept,
                                                          int budget)
 {
-    constexpr int kChunks = ROWB / 16;          // 16-byte chunks per row
+    constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
     constexpr int kRowsPerStep = kBlock / kChunks;
     constexpr int kTile = kRowsPerStep * kUnroll;
     constexpr int kPosPerThread = (kTile + kBlock - 1) / kBlock;
+    constexpr int kStores = kUnroll + kPosPerThread;    // memory stores per thread per tile
+    static_assert(kIdxChunk % kTile == 0, "tiles never straddle an index chunk");
+
+    __shared__ int32_t s_idx[kIdxChunk];
 
     const int head = blockIdx.x;
     const bool is_v = blockIdx.y != 0;
     unsigned char* rows = (is_v ? v : k) + (size_t)head * (size_t)cap * ROWB;
     int32_t* hpos = pos + (size_t)head * (size_t)cap;
     const int32_t* idx = kept + (size_t)head * (size_t)budget;
+    const __amdgpu_buffer_rsrc_t rrows =
+        __builtin_amdgcn_make_buffer_rsrc(rows, 0, len * ROWB, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rpos =
+        __builtin_amdgcn_make_buffer_rsrc(hpos, 0, len * 4, kBufferWord3);
 
     const int tid = threadIdx.x;
     const int c = tid % kChunks;
     const int rs = tid / kChunks;
 
-    for (int t0 = 0; t0 < budget; t0 += kTile) {
+    // one tile's data in flight: rows, their destinations, positions
+    struct Tile {
         u32x4 buf[kUnroll];
-        bool move[kUnroll];
+        uint32_t dst[kUnroll];
+        uint32_t pval[kPosPerThread];
+        uint32_t pdst[kPosPerThread];
+    };
+    Tile ta, tb;
+
+    auto load = [&](Tile& t, int t0, int c0) {
+        // all of the tile's indices first, so the LDS reads overlap
+        int srcs[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int r = t0 + u * kRowsPerStep + rs;
-            move[u] = false;
-            if (r < budget) {
-                const int src = idx[r];
-                // entries outside [0, len) are ignored rather than followed
-                if (src != r && (unsigned)src < (unsigned)len) {
-                    buf[u] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4*>(rows + (size_t)src * ROWB + 16 * c));
-                    move[u] = true;
-                }
-            }
+            srcs[u] = s_idx[min(r, c0 + kIdxChunk - 1) - c0];
         }
-        int32_t pval[kPosPerThread];
-        bool pmove[kPosPerThread];
-#pragma unroll
-        for (int q = 0; q < kPosPerThread; ++q) {
-            const int pr = t0 + q * kBlock + tid;
-            pmove[q] = false;
-            if (!is_v && q * kBlock + tid < kTile && pr < budget) {
-                const int src = idx[pr];
-                if (src != pr && (unsigned)src < (unsigned)len) {
-                    pval[q] = hpos[src];
-                    pmove[q] = true;
-                }
-            }
-        }
-        // every read of this tile has landed before any lane writes
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (move[u]) {
-                const int r = t0 + u * kRowsPerStep + rs;
-                __builtin_nontemporal_store(buf[u],
-                                            reinterpret_cast<u32x4*>(rows + (size_t)r * ROWB + 16 * c));
-            }
+            const int r = t0 + u * kRowsPerStep + rs;
+            const int src = r < budget ? srcs[u] : r;
+            const bool mv = r < budget && src != r && (unsigned)src < (unsigned)len;
+            const uint32_t from = mv ? (uint32_t)src * ROWB + 16u * c : kDrop;
+            t.dst[u] = mv ? (uint32_t)r * ROWB + 16u * c : kDrop;
+            t.buf[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrows, from, 0, kNT));
         }
 #pragma unroll
+        for (int q = 0; q < kPosPerThread; ++q) {
+            const int i = q * kBlock + tid;
+            const int r = t0 + i;
+            const int src = (i < kTile && r < budget) ? s_idx[r - c0] : r;
+            const bool mv = !is_v && i < kTile && r < budget && src != r && (unsigned)src < (unsigned)len;
+            t.pdst[q] = mv ? (uint32_t)r * 4u : kDrop;
+            t.pval[q] = __builtin_amdgcn_raw_buffer_load_b32(rpos, mv ? (uint32_t)src * 4u : kDrop, 0, 0);
+        }
+    };
+    auto store = [&](const Tile& t) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(t.buf[u], rrows, t.dst[u], 0, kNT);
+#pragma unroll
         for (int q = 0; q < kPosPerThread; ++q)
-            if (pmove[q]) hpos[t0 + q * kBlock + tid] = pval[q];
+            __builtin_amdgcn_raw_buffer_store_b32(t.pval[q], rpos, t.pdst[q], 0, 0);
+    };
+
+    for (int c0 = 0; c0 < budget; c0 += kIdxChunk) {
+        const int c1 = min(budget, c0 + kIdxChunk);
+        __syncthreads();                               // previous chunk's index reads done
+        for (int i = c0 + tid; i < c1; i += kBlock) s_idx[i - c0] = idx[i];
+        __syncthreads();
+        const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
+        load(ta, c0, c0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        // tiles alternate between the two register sets
+        // (the scheduling barriers keep every load of the next tile ahead of
+        // the stores, which the exact wait count relies on)
+        for (int t = 0; t < n_tiles; t += 2) {
+            const int t0 = c0 + t * kTile;
+            if (t + 1 < n_tiles) load(tb, t0 + kTile, c0);
+            __builtin_amdgcn_sched_barrier(0);
+            store(ta);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<kStores>();                     // tile t+1's reads have landed
+            __syncthreads();
+            if (t + 1 >= n_tiles) break;
+            if (t + 2 < n_tiles) load(ta, t0 + 2 * kTile, c0);
+            __builtin_amdgcn_sched_barrier(0);
+            store(tb);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<kStores>();
+            __syncthreads();
+        }
     }
 }
 
@@ -113,6 +168,8 @@ hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t
                           int n_heads, const int32_t* kept, int budget, hipStream_t stream)
 {
     if (n_heads <= 0 || budget <= 0) return hipSuccess;
+    // buffer offsets are 32-bit: a head's rows must span less than 2 GiB
+    if ((int64_t)len * row_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     switch (row_bytes) {
     case 128: return launch<128>(k, v, pos, cap, len, n_heads, kept, budget, stream);
     case 256: return launch<256>(k, v, pos, cap, len, n_heads, kept, budget, stream);

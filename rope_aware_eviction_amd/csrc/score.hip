@@ -29,10 +29,10 @@ namespace tri {
 namespace {
 
 constexpr int kBlock = 256;      // threads per workgroup
-constexpr int kTileRows = 1024;  // rows of one head per workgroup
+constexpr int kTileRows = 512;   // rows of one head per workgroup
 constexpr int kUnroll = 4;       // rows per lane kept in flight
-// word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format
-constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource word 3, gfx9 family
+constexpr int kSC1 = 16;                   // cache-policy bits: sc1
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
@@ -100,6 +100,7 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
 
     __shared__ float s_u[D];
     __shared__ float s_w[kHalf];
+    __shared__ float s_out[kTileRows];
 
     const int head = blockIdx.x / tiles_per_head;
     const int tile = blockIdx.x - head * tiles_per_head;
@@ -143,15 +144,10 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
         wt[e] = s_w[j * E + e];
     }
 
-    // Scores leave through a bounds-checked buffer store: lanes that must not
-    // write (all but the first lane of a row, rows past the tile) get an
-    // offset beyond the head's range, which the hardware drops.  With no
-    // branch in the loop, the compiler can track how many loads are in
-    // flight across iterations instead of draining them at the loop head.
-    const __amdgpu_buffer_rsrc_t out_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(out, 0, len * 4, kBufferWord3);
-    constexpr int kDropped = 0x7FFFFFF0;
-
+    // Scores of the tile are staged in LDS and leave in one coalesced sweep
+    // at the end: a store inside the loop would share the in-order memory
+    // counter with the row loads, so every wait for a row would also wait
+    // for earlier partial-line score writes to be acknowledged.
     // Rolling pipeline: as soon as row u of this batch is consumed, the same
     // registers start loading row u of the next batch, so every wave keeps
     // kUnroll - 1 to kUnroll rows in flight while it computes.
@@ -175,13 +171,17 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
                 nrm = fmaf(wt[e], __builtin_amdgcn_sqrtf(energy), nrm);
             }
             const float total = group_sum<LPR>(dot + nrm);
-            const int row = r0 + u * G;
-            const int off = (j == 0 && row < row_end) ? row * 4 : kDropped;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(total), out_rsrc, off, 0, 0);
+            if (j == 0) s_out[r0 + u * G - tile_start] = total;   // row < tile_start + kTileRows
             __builtin_amdgcn_sched_barrier(0);
         }
         r0 = r_next;
     }
+    __syncthreads();
+    // sc1 stores: measured to cost the read stream far less than default
+    // write-back stores, while the scores stay cached for the selection
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, len * 4, kBufferWord3);
+    for (int i = tid; i < row_end - tile_start; i += kBlock)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_out[i]), ro, (tile_start + i) * 4, 0, kSC1);
 }
 
 template <int D, bool BF16>
