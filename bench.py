@@ -10,9 +10,8 @@ both are outside the timed events.  Times come from HIP events recorded on the
 stream the kernels run on.
 
 Prints one JSON line.  Extra modes:
-  --pmc-steps N      run N steps with no restore/flush between launches of
-                     interest, plus a plain 1 GiB device copy (for rocprofv3
-                     counter runs; see --summarize-pmc)
+  --pmc-steps N      a plain 1 GiB device copy, then N steps with no restores
+                     (for rocprofv3 counter runs; see --summarize-pmc)
   --summarize-pmc D  turn rocprofv3 counter CSVs under D into the traffic
                      summary that later runs report as roofline.traffic
 """
@@ -124,14 +123,15 @@ def summarize_pmc(directory: str):
 
     res = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        per_kernel = {}
+        score, copy = [], []
         for r in rows(counter):
             name = r.get("Kernel_Name", "")
-            key = ("score" if SCORE_KERNEL in name else
-                   "copy" if ("copy" in name.lower() or "elementwise" in name.lower()) else None)
-            if key:
-                per_kernel.setdefault(key, []).append(float(r["Counter_Value"]))
-        res[counter] = {k: float(np.median(v)) for k, v in per_kernel.items()}
+            if SCORE_KERNEL in name:
+                score.append(float(r["Counter_Value"]))
+            elif "copyBuffer" in name:
+                copy.append(float(r["Counter_Value"]))
+        # the 1 GiB copy is the run's only large copy: its counter is the largest
+        res[counter] = {"score": float(np.median(score)), "copy": max(copy)}
     copy_bytes = float(1 << 30)
     f_scale = copy_bytes / (res["FETCH_SIZE"]["copy"] * 1024.0)
     w_scale = copy_bytes / (res["WRITE_SIZE"]["copy"] * 1024.0)
@@ -189,9 +189,29 @@ def main():
     total = sum(H * n for n in cache.lens)
     scores = torch.empty(total, dtype=torch.float32, device=dev)
     kept = torch.empty(spec.n_seq * H * B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def seqs():
+        return [tri.Seq(cache.k[s], cache.v[s], cache.pos[s], cache.lens[s], cache.p_now[s])
+                for s in range(spec.n_seq)]
+
+    if args.pmc_steps:
+        # counter runs: one plain 1 GiB device copy (the scale for the byte
+        # counters) and a few steps; no restores, so that copy is the only
+        # large copy in the run.  Later steps score the compacted cache,
+        # which moves the same bytes through the score kernel.
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        for _ in range(args.pmc_steps):
+            tri.prune_step(ctx, seqs(), B, W, scores, kept)
+        torch.cuda.synchronize()
+        print("pmc steps done", file=sys.stderr, flush=True)
+        return
+
     pristine = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
     def restore():
         for (k0, v0, p0), k, v, p in zip(pristine, cache.k, cache.v, cache.pos):
@@ -199,21 +219,6 @@ def main():
             v.copy_(v0)
             p.copy_(p0)
         flush.fill_(1)
-
-    def seqs():
-        return [tri.Seq(cache.k[s], cache.v[s], cache.pos[s], cache.lens[s], cache.p_now[s])
-                for s in range(spec.n_seq)]
-
-    if args.pmc_steps:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(args.pmc_steps):
-            restore()
-            dst.copy_(src)
-            tri.prune_step(ctx, seqs(), B, W, scores, kept)
-        torch.cuda.synchronize()
-        print("pmc steps done", file=sys.stderr, flush=True)
-        return
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for _ in range(args.warmup):
