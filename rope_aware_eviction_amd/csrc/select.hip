@@ -10,7 +10,7 @@
 // One workgroup of 1024 threads per head.  Scores map to order-preserving
 // uint32 keys.  A radix select finds the key T of the B-th largest score and
 // how many keys equal to T are still needed: it starts at the highest bit in
-// which the head's keys differ (so the first 11-bit histogram spreads over
+// which the head's keys differ (so the first histogram spreads over
 // the populated range instead of piling into a few exponent bins) and stops
 // early when a whole histogram bin is kept.  Histograms live in LDS; when
 // the head's keys fit, they are staged in LDS once and every pass reads
@@ -32,6 +32,8 @@ constexpr int kBufferWord3 = 0x00020000;
 // (no score maps to it: +inf maps to 0xFF800000)
 constexpr uint32_t kTopKey = 0xFFFFFFFFu;
 constexpr int kHistBins = 1 << kMaxDigitBits;
+// digit width of the register-resident selection's histogram passes
+constexpr int kRegDigitBits = 12;
 // keys of a head staged in LDS up to this many (4 bytes each, plus the
 // 8 KB histogram, within the 160 KB LDS of a gfx950 workgroup)
 constexpr int kLdsKeysMax = 36864;
@@ -247,41 +249,48 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict_
     }
 }
 
-// Digit holding the rem-th largest counted key: wave 0 scans the histogram
-// from the top in two levels (64 runs of `per` bins, then the bins of the
-// run that crosses rem), each an inclusive scan over the lanes.  Writes the
-// digit, the count in higher bins and the count in the digit's bin.
+// Digit holding the rem-th largest counted key, found by the whole
+// workgroup: thread t owns a run of `per` bins counted from the top (thread 0
+// the highest), the run sums are scanned within each wave and across the
+// waves' totals, and the one thread whose run crosses rem walks its bins.
+// Writes the digit, the count in higher bins and the count in the digit's
+// bin; the caller's barrier publishes them.  Requires rem <= the number of
+// counted keys.
+template <int NT>
 __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nbins, uint32_t rem,
-                                           int lane, uint32_t* s_digit, uint32_t* s_above,
+                                           int tid, int lane, int wave, uint32_t* s_run,
+                                           uint32_t* s_digit, uint32_t* s_above,
                                            uint32_t* s_inbin)
 {
-    const uint32_t per = nbins >= 64u ? nbins / 64u : 1u;      // <= 32
-    const uint32_t top = nbins - 1u - (uint32_t)lane * per;      // first bin of this lane's run
+    const uint32_t per = nbins > (uint32_t)NT ? nbins / (uint32_t)NT : 1u;
+    const uint32_t first = (uint32_t)tid * per;
+    const bool active = first < nbins;
     uint32_t sum = 0u;
-    if ((uint32_t)lane * per < nbins)
-        for (uint32_t t = 0; t < per; ++t) sum += hist[top - t];
+    if (active)
+        for (uint32_t t = 0; t < per; ++t) sum += hist[nbins - 1u - first - t];
     uint32_t incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t v = (uint32_t)__shfl_up((int)incl, o);
         if (lane >= o) incl += v;
     }
-    const int L = __ffsll((long long)__ballot(incl >= rem)) - 1;
-    const uint32_t above_run = (uint32_t)__shfl((int)(incl - sum), L);
-    const uint32_t run_top = nbins - 1u - (uint32_t)L * per;
-    const uint32_t h = (uint32_t)lane < per ? hist[run_top - lane] : 0u;
-    uint32_t incl2 = h;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-        const uint32_t v = (uint32_t)__shfl_up((int)incl2, o);
-        if (lane >= o) incl2 += v;
-    }
-    incl2 += above_run;
-    const int L2 = __ffsll((long long)__ballot((uint32_t)lane < per && incl2 >= rem)) - 1;
-    if (lane == L2) {
-        *s_digit = run_top - (uint32_t)L2;
-        *s_above = incl2 - h;
-        *s_inbin = h;
+    if (lane == 63) s_run[wave] = incl;
+    __syncthreads();
+    for (int x = 0; x < wave; ++x) incl += s_run[x];
+    const uint32_t excl = incl - sum;
+    if (active && excl < rem && rem <= incl) {
+        uint32_t acc = excl;
+        for (uint32_t t = 0; t < per; ++t) {
+            const uint32_t b = nbins - 1u - first - t;
+            const uint32_t h = hist[b];
+            if (acc + h >= rem) {
+                *s_digit = b;
+                *s_above = acc;
+                *s_inbin = h;
+                break;
+            }
+            acc += h;
+        }
     }
 }
 
@@ -307,7 +316,7 @@ __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane)
 // histogram and a short candidate list.
 //
 // Radix select on offsets: all live keys lie in [base, base + 2^wb); each
-// pass histograms (key - base) >> (wb - 11) into 2048 bins, so the bins
+// pass histograms (key - base) >> (wb - 12) into 4096 bins, so the bins
 // always span the populated key range (the keys of concentrated scores sit
 // in a narrow range, often straddling a power of two, and a bit-aligned
 // digit would pile them into a few bins).  Keys above the chosen bin are
@@ -322,9 +331,9 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
                                                         int32_t* __restrict__ kept)
 {
     constexpr int kW = NT / 64;
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t hist[1 << kRegDigitBits];
     __shared__ uint32_t s_cand[64];
-    __shared__ uint32_t s_wa[kW], s_wb[kW];
+    __shared__ uint32_t s_wa[kW], s_wb[kW], s_run[kW];
     __shared__ uint32_t s_digit, s_above, s_inbin, s_ncand;
     __shared__ uint32_t s_T, s_need, s_tie;
 
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
         int wb = 32 - __clz((int)(kmax - kmin));       // live keys: [base, base + 2^wb)
         uint32_t rem = (uint32_t)budget;
         for (;;) {
-            const int nb = min(kMaxDigitBits, wb);
+            const int nb = min(kRegDigitBits, wb);
             const int sh = wb - nb;
             const uint32_t nbins = 1u << nb;
             const uint32_t span = wb >= 32 ? 0xFFFFFFFFu : (1u << wb) - 1u;
@@ -395,13 +404,18 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             for (uint32_t b = tid; b < nbins; b += NT) hist[b] = 0u;
             if (tid == 0) s_ncand = 0u;
             __syncthreads();
+            // padding keys (0) are skipped; the comparison value is opaque so
+            // the compiler recomputes the KPT masks per pass instead of
+            // keeping them live in scalar registers across passes
+            uint32_t pad = 0u;
+            asm volatile("" : "+v"(pad));
 #pragma unroll
             for (int c = 0; c < KPT; ++c) {
                 const uint32_t off = key[c] - base;
-                if (off <= span && key[c]) atomicAdd(&hist[off >> sh], 1u);
+                if (off <= span && key[c] != pad) atomicAdd(&hist[off >> sh], 1u);
             }
             __syncthreads();
-            if (wave == 0) find_digit(hist, nbins, rem, lane, &s_digit, &s_above, &s_inbin);
+            find_digit<NT>(hist, nbins, rem, tid, lane, wave, s_run, &s_digit, &s_above, &s_inbin);
             __syncthreads();
             const uint32_t d = s_digit & (nbins - 1u);
             const uint32_t in_bin = s_inbin;
@@ -426,7 +440,7 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
 #pragma unroll
                 for (int c = 0; c < KPT; ++c) {
                     const uint32_t off = key[c] - base;
-                    if (off <= cspan && key[c]) {
+                    if (off <= cspan && key[c] != pad) {
                         const uint32_t at = atomicAdd(&s_ncand, 1u);
                         if (at < 64u) s_cand[at] = key[c];
                     }
