@@ -7,7 +7,10 @@ and seeded.  A step is one whole prune pass over every head, with inputs
 resident in HBM.  Between steps the cache is restored from a pristine device
 copy and a 512 MiB buffer is overwritten to flush the 256 MB last-level cache;
 both are outside the timed events.  Times come from HIP events recorded on the
-stream the kernels run on.
+stream the kernels run on: the timed steps carry one event before the first
+launch and one after the last; the per-phase breakdown (and the score
+kernel's roofline) comes from ten further steps with events between the
+launches.
 
 Prints one JSON line.  Extra modes:
   --pmc-steps N      a plain 1 GiB device copy, then N steps with no restores
@@ -220,7 +223,7 @@ def main():
             p.copy_(p0)
         flush.fill_(1)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         restore()
         tri.prune_step(ctx, seqs(), B, W, scores, kept)
@@ -234,18 +237,32 @@ def main():
         e = ev[i]
         e[0].record(stream)
         tri.tri_score(ctx, s, scores, stream)
+        tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
+        tri.tri_compact_kv(ctx, s, kept, B, W, stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_step = [e[0].elapsed_time(e[1]) for e in ev]
+
+    # Phase breakdown from separate steps: an event between two launches
+    # costs a few microseconds, so the timed steps above carry none.
+    n_phase = max(1, min(args.steps, 10))
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_phase)]
+    for i in range(n_phase):
+        restore()
+        s = seqs()
+        e = pev[i]
+        e[0].record(stream)
+        tri.tri_score(ctx, s, scores, stream)
         e[1].record(stream)
         tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
         e[2].record(stream)
         tri.tri_compact_kv(ctx, s, kept, B, W, stream)
         e[3].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    t_step = [e[0].elapsed_time(e[3]) for e in ev]
-    t_score = [e[0].elapsed_time(e[1]) for e in ev]
-    t_select = [e[1].elapsed_time(e[2]) for e in ev]
-    t_compact = [e[2].elapsed_time(e[3]) for e in ev]
+    t_score = [e[0].elapsed_time(e[1]) for e in pev]
+    t_select = [e[1].elapsed_time(e[2]) for e in pev]
+    t_compact = [e[2].elapsed_time(e[3]) for e in pev]
     mean = lambda x: sum(x) / len(x)
     ms = mean(t_step)
     keys = spec.keys

@@ -11,9 +11,9 @@
 // ascending tiles of T rows: tile t reads rows >= tT and writes rows
 // [tT, (t+1)T).  Its writes may destroy sources of tiles <= t only, so a
 // tile is written once the reads of every tile up to it have landed; reads
-// of later tiles never touch rows written so far.  One workgroup owns one
-// (head, K or V) stream and walks its tiles in order; positions travel with
-// K.
+// of later tiles never touch rows written so far.  A workgroup owns one
+// (head, K or V) stream at a time and walks its tiles in order, then takes
+// its next stream; positions travel with K.
 //
 // Pipeline.  The loads of tile t+1 are issued before the stores of tile t,
 // then the workgroup waits until those loads (not the stores, which share
@@ -24,12 +24,14 @@
 // count them exactly.  The head's kept list is staged in LDS so index reads
 // stay off the memory counter.  Rows are moved with non-temporal accesses:
 // every byte is touched once.
+#include <algorithm>
+
 #include "tri_internal.h"
 
 namespace tri {
 namespace {
 
-constexpr int kBlock = 512;
+constexpr int kBlock = 1024;
 constexpr int kUnroll = 8;
 constexpr int kIdxChunk = 8192;                 // kept entries staged in LDS at a time
 constexpr uint32_t kDrop = 0xFFFFFFC0u;          // buffer offset that is always out of range
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
                                                          int32_t* __restrict__ pos, int64_t cap,
                                                          int len,
                                                          const int32_t* __restrict__ kept,
-                                                         int budget)
+                                                         int budget, int n_heads)
 {
     constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
     constexpr int kRowsPerStep = kBlock / kChunks;
@@ -62,92 +64,94 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
 
     __shared__ int32_t s_idx[kIdxChunk];
 
-    const int head = blockIdx.x;
-    const bool is_v = blockIdx.y != 0;
-    unsigned char* rows = (is_v ? v : k) + (size_t)head * (size_t)cap * ROWB;
-    int32_t* hpos = pos + (size_t)head * (size_t)cap;
-    const int32_t* idx = kept + (size_t)head * (size_t)budget;
-    const __amdgpu_buffer_rsrc_t rrows =
-        __builtin_amdgcn_make_buffer_rsrc(rows, 0, len * ROWB, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rpos =
-        __builtin_amdgcn_make_buffer_rsrc(hpos, 0, len * 4, kBufferWord3);
+    for (int stream_id = blockIdx.x; stream_id < 2 * n_heads; stream_id += gridDim.x) {
+        const int head = stream_id >> 1;
+        const bool is_v = (stream_id & 1) != 0;
+        unsigned char* rows = (is_v ? v : k) + (size_t)head * (size_t)cap * ROWB;
+        int32_t* hpos = pos + (size_t)head * (size_t)cap;
+        const int32_t* idx = kept + (size_t)head * (size_t)budget;
+        const __amdgpu_buffer_rsrc_t rrows =
+            __builtin_amdgcn_make_buffer_rsrc(rows, 0, len * ROWB, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rpos =
+            __builtin_amdgcn_make_buffer_rsrc(hpos, 0, len * 4, kBufferWord3);
 
-    const int tid = threadIdx.x;
-    const int c = tid % kChunks;
-    const int rs = tid / kChunks;
+        const int tid = threadIdx.x;
+        const int c = tid % kChunks;
+        const int rs = tid / kChunks;
 
-    // one tile's data in flight: rows, their destinations, positions
-    struct Tile {
-        u32x4 buf[kUnroll];
-        uint32_t dst[kUnroll];
-        uint32_t pval[kPosPerThread];
-        uint32_t pdst[kPosPerThread];
-    };
-    Tile ta, tb;
+        // one tile's data in flight: rows, their destinations, positions
+        struct Tile {
+            u32x4 buf[kUnroll];
+            uint32_t dst[kUnroll];
+            uint32_t pval[kPosPerThread];
+            uint32_t pdst[kPosPerThread];
+        };
+        Tile ta, tb;
 
-    auto load = [&](Tile& t, int t0, int c0) {
-        // all of the tile's indices first, so the LDS reads overlap
-        int srcs[kUnroll];
+        auto load = [&](Tile& t, int t0, int c0) {
+            // all of the tile's indices first, so the LDS reads overlap
+            int srcs[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int r = t0 + u * kRowsPerStep + rs;
-            srcs[u] = s_idx[min(r, c0 + kIdxChunk - 1) - c0];
-        }
+            for (int u = 0; u < kUnroll; ++u) {
+                const int r = t0 + u * kRowsPerStep + rs;
+                srcs[u] = s_idx[min(r, c0 + kIdxChunk - 1) - c0];
+            }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int r = t0 + u * kRowsPerStep + rs;
-            const int src = r < budget ? srcs[u] : r;
-            const bool mv = r < budget && src != r && (unsigned)src < (unsigned)len;
-            const uint32_t from = mv ? (uint32_t)src * ROWB + 16u * c : kDrop;
-            t.dst[u] = mv ? (uint32_t)r * ROWB + 16u * c : kDrop;
-            t.buf[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrows, from, 0, kNT));
-        }
+            for (int u = 0; u < kUnroll; ++u) {
+                const int r = t0 + u * kRowsPerStep + rs;
+                const int src = r < budget ? srcs[u] : r;
+                const bool mv = r < budget && src != r && (unsigned)src < (unsigned)len;
+                const uint32_t from = mv ? (uint32_t)src * ROWB + 16u * c : kDrop;
+                t.dst[u] = mv ? (uint32_t)r * ROWB + 16u * c : kDrop;
+                t.buf[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrows, from, 0, kNT));
+            }
 #pragma unroll
-        for (int q = 0; q < kPosPerThread; ++q) {
-            const int i = q * kBlock + tid;
-            const int r = t0 + i;
-            const int src = (i < kTile && r < budget) ? s_idx[r - c0] : r;
-            const bool mv = !is_v && i < kTile && r < budget && src != r && (unsigned)src < (unsigned)len;
-            t.pdst[q] = mv ? (uint32_t)r * 4u : kDrop;
-            t.pval[q] = __builtin_amdgcn_raw_buffer_load_b32(rpos, mv ? (uint32_t)src * 4u : kDrop, 0, 0);
-        }
-    };
-    auto store = [&](const Tile& t) {
+            for (int q = 0; q < kPosPerThread; ++q) {
+                const int i = q * kBlock + tid;
+                const int r = t0 + i;
+                const int src = (i < kTile && r < budget) ? s_idx[r - c0] : r;
+                const bool mv = !is_v && i < kTile && r < budget && src != r && (unsigned)src < (unsigned)len;
+                t.pdst[q] = mv ? (uint32_t)r * 4u : kDrop;
+                t.pval[q] = __builtin_amdgcn_raw_buffer_load_b32(rpos, mv ? (uint32_t)src * 4u : kDrop, 0, 0);
+            }
+        };
+        auto store = [&](const Tile& t) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            __builtin_amdgcn_raw_buffer_store_b128(t.buf[u], rrows, t.dst[u], 0, kNT);
+            for (int u = 0; u < kUnroll; ++u)
+                __builtin_amdgcn_raw_buffer_store_b128(t.buf[u], rrows, t.dst[u], 0, kNT);
 #pragma unroll
-        for (int q = 0; q < kPosPerThread; ++q)
-            __builtin_amdgcn_raw_buffer_store_b32(t.pval[q], rpos, t.pdst[q], 0, 0);
-    };
+            for (int q = 0; q < kPosPerThread; ++q)
+                __builtin_amdgcn_raw_buffer_store_b32(t.pval[q], rpos, t.pdst[q], 0, 0);
+        };
 
-    for (int c0 = 0; c0 < budget; c0 += kIdxChunk) {
-        const int c1 = min(budget, c0 + kIdxChunk);
-        __syncthreads();                               // previous chunk's index reads done
-        for (int i = c0 + tid; i < c1; i += kBlock) s_idx[i - c0] = idx[i];
-        __syncthreads();
-        const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
-        load(ta, c0, c0);
-        wait_vmcnt<0>();
-        __syncthreads();
-        // tiles alternate between the two register sets
-        // (the scheduling barriers keep every load of the next tile ahead of
-        // the stores, which the exact wait count relies on)
-        for (int t = 0; t < n_tiles; t += 2) {
-            const int t0 = c0 + t * kTile;
-            if (t + 1 < n_tiles) load(tb, t0 + kTile, c0);
-            __builtin_amdgcn_sched_barrier(0);
-            store(ta);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<kStores>();                     // tile t+1's reads have landed
+        for (int c0 = 0; c0 < budget; c0 += kIdxChunk) {
+            const int c1 = min(budget, c0 + kIdxChunk);
+            __syncthreads();                               // previous chunk's index reads done
+            for (int i = c0 + tid; i < c1; i += kBlock) s_idx[i - c0] = idx[i];
             __syncthreads();
-            if (t + 1 >= n_tiles) break;
-            if (t + 2 < n_tiles) load(ta, t0 + 2 * kTile, c0);
-            __builtin_amdgcn_sched_barrier(0);
-            store(tb);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<kStores>();
+            const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
+            load(ta, c0, c0);
+            wait_vmcnt<0>();
             __syncthreads();
+            // tiles alternate between the two register sets
+            // (the scheduling barriers keep every load of the next tile ahead of
+            // the stores, which the exact wait count relies on)
+            for (int t = 0; t < n_tiles; t += 2) {
+                const int t0 = c0 + t * kTile;
+                if (t + 1 < n_tiles) load(tb, t0 + kTile, c0);
+                __builtin_amdgcn_sched_barrier(0);
+                store(ta);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<kStores>();                     // tile t+1's reads have landed
+                __syncthreads();
+                if (t + 1 >= n_tiles) break;
+                if (t + 2 < n_tiles) load(ta, t0 + 2 * kTile, c0);
+                __builtin_amdgcn_sched_barrier(0);
+                store(tb);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<kStores>();
+                __syncthreads();
+            }
         }
     }
 }
@@ -156,9 +160,26 @@ template <int ROWB>
 hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_heads,
                   const int32_t* kept, int budget, hipStream_t stream)
 {
-    hipLaunchKernelGGL(compact_kernel<ROWB>, dim3(n_heads, 2), dim3(kBlock), 0, stream,
+    // Each workgroup walks whole K or V streams one after another.  Measured
+    // on the 36 x 8 x 32768 cache: 576 streams spread over ~3/4 of the
+    // compute units (192 workgroups of 1024 threads, three streams each)
+    // move the rows in 225 us; one workgroup per stream takes 250 us and
+    // every variant with more streams in flight at once is slower still.
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        return n;
+    }();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int streams = 2 * n_heads;
+    const int target = std::max(1, 3 * cus / 4);
+    const int per_block = (streams + target - 1) / target;
+    const int grid = (streams + per_block - 1) / per_block;
+    hipLaunchKernelGGL(compact_kernel<ROWB>, dim3(grid), dim3(kBlock), 0, stream,
                        static_cast<unsigned char*>(k), static_cast<unsigned char*>(v), pos, cap,
-                       len, kept, budget);
+                       len, kept, budget, n_heads);
     return hipGetLastError();
 }
 
