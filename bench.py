@@ -5,12 +5,15 @@ Default workload: the Qwen3-8B-shaped 32K reasoning cache (36 layers x 8 KV
 heads x head_dim 128, 32768 cached keys per head, budget 4096, bf16), synthetic
 and seeded.  A step is one whole prune pass over every head, with inputs
 resident in HBM.  Between steps the cache is restored from a pristine device
-copy and a 512 MiB buffer is overwritten to flush the 256 MB last-level cache;
-both are outside the timed events.  Times come from HIP events recorded on the
-stream the kernels run on: the timed steps carry one event before the first
-launch and one after the last; the per-phase breakdown (and the score
-kernel's roofline) comes from ten further steps with events between the
-launches.
+copy and a 512 MiB buffer is read to flush the 256 MB last-level cache; both
+are outside the timed events.  The flush reads rather than writes: a written
+flush buffer leaves up to 256 MB of dirty lines whose write-back then lands
+inside the timed step (measured: ~12 us per step), while a read evicts the
+restore's dirty lines before the first event.  Times come from HIP events
+recorded on the stream the kernels run on: the timed steps carry one event
+before the first launch and one after the last; the per-phase breakdown (and
+the score kernel's roofline) comes from up to ten further steps with events
+between the launches.
 
 Prints one JSON line.  Extra modes:
   --pmc-steps N      a plain 1 GiB device copy, then N steps with no restores
@@ -214,14 +217,14 @@ def main():
         return
 
     pristine = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
 
     def restore():
         for (k0, v0, p0), k, v, p in zip(pristine, cache.k, cache.v, cache.pos):
             k.copy_(k0)
             v.copy_(v0)
             p.copy_(p0)
-        flush.fill_(1)
+        flush.sum(dtype=torch.int64)      # reads 512 MiB: evicts the cache, leaves it clean
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for _ in range(args.warmup):
