@@ -160,11 +160,14 @@ template <int ROWB>
 hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_heads,
                   const int32_t* kept, int budget, hipStream_t stream)
 {
-    // Each workgroup walks whole K or V streams one after another.  Measured
-    // on the 36 x 8 x 32768 cache: 576 streams spread over ~3/4 of the
-    // compute units (192 workgroups of 1024 threads, three streams each)
-    // move the rows in 225 us; one workgroup per stream takes 250 us and
-    // every variant with more streams in flight at once is slower still.
+    // Each workgroup walks whole K or V streams one after another, at most
+    // one workgroup per compute unit, every workgroup the same number of
+    // streams.  Measured on the 36 x 8 x 32768 cache (576 streams of 4096
+    // rows): 192 workgroups of three streams move the rows in 225 us, one
+    // 512-thread workgroup per stream in 250 us, and more streams in flight
+    // at once is slower still.  On the 32 x 8 x 8192 cache (512 streams of
+    // 2048 rows) 256 workgroups of two streams take 98 us (one per stream:
+    // 97.5 us).
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -174,8 +177,7 @@ hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_he
     }();
     if (cus <= 0) return hipErrorInvalidDevice;
     const int streams = 2 * n_heads;
-    const int target = std::max(1, 3 * cus / 4);
-    const int per_block = (streams + target - 1) / target;
+    const int per_block = (streams + cus - 1) / cus;
     const int grid = (streams + per_block - 1) / per_block;
     hipLaunchKernelGGL(compact_kernel<ROWB>, dim3(grid), dim3(kBlock), 0, stream,
                        static_cast<unsigned char*>(k), static_cast<unsigned char*>(v), pos, cap,
