@@ -55,19 +55,22 @@ def workload_bytes(spec):
 
     pass:  per head N*row (read K) + 4*B*row (read and write kept K and V rows)
            + 8*B (read and write kept positions)
-    score: per head N*row (read K) + 4*N (write fp32 scores)
+    score: per head N*row (read K) + 4*N (write fp32 scores); with G > 1 query
+           heads per KV head the score phase also writes and reads back the G
+           raw scores per key: + 8*G*N
     """
-    H, row, B = spec.heads, spec.row_bytes, spec.budget
+    H, row, B, G = spec.heads, spec.row_bytes, spec.budget, spec.group
     p = sum(H * (n * row + 4 * B * row + 8 * B) for n in spec.lengths if n > B + spec.window)
-    s = sum(H * (n * row + 4 * n) for n in spec.lengths)
+    s = sum(H * (n * row + 4 * n + (8 * G * n if G > 1 else 0)) for n in spec.lengths)
     return p, s
 
 
 def describe(spec) -> str:
     ln = spec.lengths
     lens = "%d cached keys" % ln[0] if len(ln) == 1 else "%d sequences, %d..%d keys" % (len(ln), min(ln), max(ln))
-    return "%s: %d layers x %d KV heads x head_dim %d, %s, budget %d, %s" % (
-        spec.name, spec.n_layers, spec.n_kv_heads, spec.head_dim, lens, spec.budget, spec.dtype)
+    gqa = ", %d query heads per KV head" % spec.group if spec.group > 1 else ""
+    return "%s: %d layers x %d KV heads x head_dim %d%s, %s, budget %d, %s" % (
+        spec.name, spec.n_layers, spec.n_kv_heads, spec.head_dim, gqa, lens, spec.budget, spec.dtype)
 
 
 def cpu_baseline(cache, n_heads_sample: int):
@@ -82,13 +85,15 @@ def cpu_baseline(cache, n_heads_sample: int):
     om = orc.omega(sp.head_dim, sp.rope_theta)
     jobs = []
     n = cache.lens[0]
+    G = sp.group
     for hi in range(n_heads_sample):
         l, h = divmod(hi, sp.n_kv_heads)
+        q = slice(h * G, (h + 1) * G) if G > 1 else h
         jobs.append(dict(
             K=cache.k[0][l, h, :n].float().cpu().numpy(), V=cache.v[0][l, h, :n].cpu().view(
                 __import__("torch").int16).numpy(), pos=cache.pos[0][l, h, :n].cpu().numpy(),
-            p_now=cache.p_now[0], om=om, offsets=cal.offsets, qc_re=cal.qc_re[l, h],
-            qc_im=cal.qc_im[l, h], q_mean_norm=cal.q_mean_norm[l, h], q_mrl=cal.q_mrl[l, h],
+            p_now=cache.p_now[0], om=om, offsets=cal.offsets, qc_re=cal.qc_re[l, q],
+            qc_im=cal.qc_im[l, q], q_mean_norm=cal.q_mean_norm[l, q], q_mrl=cal.q_mrl[l, q],
             budget=sp.budget, window=sp.window))
     t0 = time.perf_counter()
     orc.prune_heads_parallel(jobs, threads)
@@ -190,7 +195,7 @@ def main():
     cal = cache.calib
     ctx = tri.tri_calibrate_load(spec.n_layers, spec.n_kv_heads, spec.head_dim, cal.qc_re, cal.qc_im,
                                  cal.q_mean_norm, cal.q_mrl, cal.offsets, rope_theta=cal.rope_theta,
-                                 device=0)
+                                 device=0, n_q_heads=spec.n_q_heads)
     H, B, W = spec.heads, spec.budget, spec.window
     total = sum(H * n for n in cache.lens)
     scores = torch.empty(total, dtype=torch.float32, device=dev)
@@ -200,6 +205,10 @@ def main():
     def seqs():
         return [tri.Seq(cache.k[s], cache.v[s], cache.pos[s], cache.lens[s], cache.p_now[s])
                 for s in range(spec.n_seq)]
+
+    # GQA contexts score through a workspace (G raw scores per key)
+    ws_bytes = tri.score_workspace_bytes(ctx, seqs())
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     if args.pmc_steps:
         # counter runs: one plain 1 GiB device copy (the scale for the byte
@@ -211,7 +220,7 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         for _ in range(args.pmc_steps):
-            tri.prune_step(ctx, seqs(), B, W, scores, kept)
+            tri.prune_step(ctx, seqs(), B, W, scores, kept, workspace=ws)
         torch.cuda.synchronize()
         print("pmc steps done", file=sys.stderr, flush=True)
         return
@@ -229,7 +238,7 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         restore()
-        tri.prune_step(ctx, seqs(), B, W, scores, kept)
+        tri.prune_step(ctx, seqs(), B, W, scores, kept, workspace=ws)
     torch.cuda.synchronize()
     print("bench: warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -239,7 +248,7 @@ def main():
         s = seqs()
         e = ev[i]
         e[0].record(stream)
-        tri.tri_score(ctx, s, scores, stream)
+        tri.tri_score(ctx, s, scores, stream, ws)
         tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
         tri.tri_compact_kv(ctx, s, kept, B, W, stream)
         e[1].record(stream)
@@ -256,7 +265,7 @@ def main():
         s = seqs()
         e = pev[i]
         e[0].record(stream)
-        tri.tri_score(ctx, s, scores, stream)
+        tri.tri_score(ctx, s, scores, stream, ws)
         e[1].record(stream)
         tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
         e[2].record(stream)
@@ -292,7 +301,9 @@ def main():
         "config": {"workload": describe(spec), "layers": spec.n_layers, "kv_heads": spec.n_kv_heads,
                    "head_dim": spec.head_dim, "cached_keys": list(spec.lengths)[:1] if spec.n_seq == 1 else "ragged",
                    "budget": B, "window": W, "storage": spec.dtype, "offsets": len(spec.offsets)},
-        "roofline": {"bound": "hbm", "kernel": SCORE_KERNEL, "achieved": score_gbs, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": SCORE_KERNEL if spec.group == 1 else
+                     "GQA score phase (gqa_score_kernel, gqa_stats_kernel, gqa_norm_kernel)",
+                     "achieved": score_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": score_gbs / HBM_PEAK_GBS,
                      "traffic": load_traffic(spec), "alg_bytes_per_launch": bytes_score,
                      "launch_ms": mean(t_score)},

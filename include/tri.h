@@ -69,10 +69,13 @@ typedef struct {
     const double* inv_freq;       /* host [head_dim/2] explicit band frequencies (> 0, finite), or NULL */
     const int64_t* offsets;       /* host [n_offsets] future offsets D, each in [0, 2^40] */
     int32_t n_offsets;            /* >= 1 */
-    const double* qc_re;          /* host [n_layers][n_kv_heads][head_dim/2]: Re E[q_f] (pre-RoPE) */
+    const double* qc_re;          /* host [n_layers][n_q_heads][head_dim/2]: Re E[q_f] (pre-RoPE) */
     const double* qc_im;          /* host, same shape: Im E[q_f] */
     const double* q_mean_norm;    /* host, same shape: E|q_f| >= 0 */
     const double* q_mrl;          /* host, same shape: mean resultant length R_f in [0, 1] */
+    int32_t n_q_heads;            /* query heads per layer: 0 or n_kv_heads for one query table per
+                                     KV head; otherwise G * n_kv_heads with G in [2, 8] (GQA: query
+                                     heads j*G .. j*G+G-1 share KV head j) */
 } tri_calib_desc;
 
 typedef struct tri_ctx tri_ctx;   /* opaque; immutable after tri_calibrate_load */
@@ -123,6 +126,8 @@ int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
  * C_f = E[q_f] * A_f * exp(i*w_f*p_now) once per head in fp64 and takes
  * score = sum_f (Re C_f * K[f] + Im C_f * K[f + d/2]) + sum_f w_f * |K_f|
  * from the stored row, accumulating in fp32.
+ * GQA contexts (n_q_heads > n_kv_heads) need tri_score_ws; tri_score
+ * returns TRI_E_INVAL for them.
  *   dtype   element type of every seq's K (TRI_F32 or TRI_BF16)
  *   scores  device fp32, tri_scores_count() slots: the scores of sequence s
  *           start after those of sequences 0..s-1, each sequence laid out
@@ -136,6 +141,35 @@ int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
  */
 tri_status tri_score(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, int32_t n_seq,
                      float* scores, void* stream);
+
+/* Device workspace bytes tri_score_ws needs for these sequences: 0 for a
+ * context with one query table per KV head; for GQA contexts 4 * G bytes per
+ * cached key plus per-tile statistics.  Returns -1 on bad arguments. */
+int64_t tri_score_workspace_bytes(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq);
+
+/*
+ * tri_score with a caller-owned device workspace (16-byte aligned, at least
+ * tri_score_workspace_bytes(); may be NULL when that is 0).  Contexts with
+ * one query table per KV head score exactly as tri_score.  For GQA contexts
+ * (G query heads per KV head) every key first gets G scores, one per query
+ * head of its KV head, each the score above with that query head's table;
+ * each query head's scores are z-normalized over the head's cached keys,
+ *   z_g = (s_g - mean_g) / sd_g   (mean and population deviation of the finite s_g),
+ * and the key's score is the largest z_g.  K is read once.  Readings: a
+ * deviation at most 1e-9 of the largest |s_g| counts as zero and gives
+ * z_g = 0; a non-finite s_g gives NaN, which loses to every number; mean_g
+ * and sd_g are accumulated in fp64 in a fixed order (the result does not
+ * depend on scheduling).  Output layout as tri_score; the workspace holds
+ * intermediates only and is overwritten.  Calls sharing a workspace must not
+ * overlap in time.
+ * Errors: TRI_E_INVAL (also: GQA context with a missing or short workspace),
+ * TRI_E_UNSUPPORTED, TRI_E_HIP.
+ * Source: dimensionstp.github.io review, section 3-2 item 6 (per query head
+ * z-score normalization, then max aggregation over the query heads sharing
+ * a KV head); romaanj.github.io review, section "Method".
+ */
+tri_status tri_score_ws(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, int32_t n_seq,
+                        float* scores, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Selects, for every head of every firing sequence, the `budget` keys with

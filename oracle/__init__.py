@@ -83,6 +83,10 @@ class Oracle:
         lib.tri_oracle_select_head.restype = ctypes.c_int
         lib.tri_oracle_select_head.argtypes = [
             ctypes.c_int, _dp, _i64p, ctypes.c_int, ctypes.c_int, _i32p]
+        lib.tri_oracle_gqa_head.restype = ctypes.c_int
+        lib.tri_oracle_gqa_head.argtypes = [
+            ctypes.c_int, ctypes.c_int, _dp, _i64p, ctypes.c_int64, _dp, _i64p,
+            ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.tri_oracle_gather_rows.restype = None
         lib.tri_oracle_gather_rows.argtypes = [
             ctypes.c_int, _i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
@@ -144,6 +148,34 @@ class Oracle:
             _ptr(out, _dp))
         return out
 
+    def gqa_head(self, K, pos, p_now, om, offsets, qc_re, qc_im, q_mean_norm, q_mrl):
+        """GQA normalize-then-aggregate score of one KV head.
+
+        The calibration arrays are [G][d/2], one row per query head of the
+        group.  Returns (raw [G][n], z [G][n], score [n]), fp64: each query
+        head's score row, its z-normalized row, and the max over the group.
+        """
+        K = _f64(K)
+        n, d = K.shape
+        pos = _i64(pos)
+        om = _f64(om)
+        offsets = _i64(offsets)
+        qc_re, qc_im, q_mean_norm, q_mrl = (_f64(np.atleast_2d(x)) for x in (qc_re, qc_im, q_mean_norm, q_mrl))
+        G = qc_re.shape[0]
+        for x in (qc_re, qc_im, q_mean_norm, q_mrl):
+            assert x.shape == (G, d // 2)
+        raw = np.empty((G, n))
+        z = np.empty((G, n))
+        score = np.empty(n)
+        r = self.lib.tri_oracle_gqa_head(
+            d, n, _ptr(K, _dp), _ptr(pos, _i64p), int(p_now), _ptr(om, _dp),
+            _ptr(offsets, _i64p), len(offsets), G, _ptr(qc_re, _dp), _ptr(qc_im, _dp),
+            _ptr(q_mean_norm, _dp), _ptr(q_mrl, _dp), _ptr(raw, _dp), _ptr(z, _dp),
+            _ptr(score, _dp))
+        if r != 0:
+            raise ValueError("bad arguments to the oracle's GQA score")
+        return raw, z, score
+
     def select_head(self, score, pos, budget: int, window: int):
         """Kept slots (ascending) of one head, or None when the head does not fire."""
         score = _f64(score)
@@ -170,13 +202,17 @@ class Oracle:
 
     def prune_head(self, K, V, pos, p_now, om, offsets, qc_re, qc_im, q_mean_norm, q_mrl,
                    budget, window):
-        """One head's full prune step: score, top-B, gather.
+        """One head's full prune step: score, top-B, gather.  With [G][d/2]
+        calibration arrays the score is the GQA normalize-then-aggregate one.
 
         Returns dict(score, kept, K, V, pos); kept/K/V/pos are None when the
         head does not fire.
         """
-        _, _, score = self.score_head(K, pos, p_now, om, offsets, qc_re, qc_im,
-                                      q_mean_norm, q_mrl)
+        if np.ndim(qc_re) == 2:         # [G][d/2]: a GQA group sharing this KV head
+            _, _, score = self.gqa_head(K, pos, p_now, om, offsets, qc_re, qc_im, q_mean_norm, q_mrl)
+        else:
+            _, _, score = self.score_head(K, pos, p_now, om, offsets, qc_re, qc_im,
+                                          q_mean_norm, q_mrl)
         kept = self.select_head(score, pos, budget, window)
         if kept is None:
             return dict(score=score, kept=None, K=None, V=None, pos=None)

@@ -19,7 +19,9 @@
  *        (RoPE logit as a sum over bands of r_q*r_k*cos((i-j)*theta_f+phi_f)),
  *        section 3-2 items 2)-5) (cached key has a known position and
  *        pre-RoPE form; score = S_tri + S_norm; window-based pruning keeps
- *        the top-budget keys).
+ *        the top-budget keys), section 3-2 item 6 (GQA: per query head
+ *        z-score normalization, then max aggregation over the query heads
+ *        that share a KV head).
  *
  * Readings taken where the pages leave a step open (each is listed in the
  * design notes of the repository):
@@ -30,6 +32,12 @@
  *   - the norm-term weight of band f is (1 - R_f) * E|q_f|;
  *   - the average over offsets is the plain arithmetic mean;
  *   - the trig and norm terms are added unscaled;
+ *   - GQA: query heads [h*G, (h+1)*G) share KV head h; each query head's
+ *     score row is z-normalized with the mean and population standard
+ *     deviation of its finite scores over the head's cached keys; a
+ *     deviation of at most 1e-9 of the row's largest |score| (rounding
+ *     level) counts as zero and gives z = 0; a non-finite score stays NaN
+ *     and loses to any number in the max over the group;
  *   - a head fires iff n > budget + window; top-B orders keys by
  *     (score descending, position ascending), NaN below every number,
  *     -0 equal to +0; kept slots are returned in ascending slot order.
@@ -161,6 +169,70 @@ void tri_oracle_bound_head(int d, int n, const double* K, const double* omega,
         bound[i] = m;
     }
     free(coef);
+}
+
+/* ---- GQA: normalize, then aggregate ------------------------------------ */
+
+/*
+ * Score of the n keys of one KV head shared by `group` query heads
+ * [R2 3-2 item 6; R1 Method]: query head g scores every key with its own
+ * calibration (exactly tri_oracle_score_head), its row s_g is z-normalized
+ * over the head's cached keys, z_g = (s_g - mean_g) / std_g, and a key's
+ * score is the largest z_g over the group, so a key that any query head
+ * ranks highly survives.
+ *   qc_re, qc_im, q_mean_norm, q_mrl  [group][d/2]  query head g's table
+ *   raw    [group][n]  out: s_g (may be NULL)
+ *   zrow   [group][n]  out: z_g (may be NULL)
+ *   score  [n]         out: max over g of z_g
+ * mean_g and std_g (population: divided by the count) run over the finite
+ * entries of s_g; a row whose std_g is at most GQA_FLAT times its largest
+ * |score| counts as constant (mathematically equal scores leave a deviation
+ * of a few ulps in fp64 sums) and gets z_g = 0; a non-finite s_g gives
+ * z_g = NaN, and NaN loses to every number in the max.  Returns 0, or -1 on
+ * bad arguments.
+ */
+#define GQA_FLAT 1e-9
+
+int tri_oracle_gqa_head(int d, int n, const double* K, const int64_t* pos,
+                        int64_t p_now, const double* omega,
+                        const int64_t* offsets, int n_off, int group,
+                        const double* qc_re, const double* qc_im,
+                        const double* q_mean_norm, const double* q_mrl,
+                        double* raw, double* zrow, double* score)
+{
+    if (d < 2 || n < 0 || group < 1 || n_off < 1) return -1;
+    const int half = d / 2;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; ++i) score[i] = NAN;
+    for (int g = 0; g < group; ++g) {
+        tri_oracle_score_head(d, n, K, pos, p_now, omega, offsets, n_off,
+                              qc_re + (size_t)g * half, qc_im + (size_t)g * half,
+                              q_mean_norm + (size_t)g * half, q_mrl + (size_t)g * half,
+                              NULL, NULL, s);
+        if (raw) memcpy(raw + (size_t)g * n, s, sizeof(double) * (size_t)n);
+
+        /* mean and population standard deviation of the finite scores */
+        double sum = 0.0, big = 0.0;
+        long count = 0;
+        for (int i = 0; i < n; ++i)
+            if (isfinite(s[i])) { sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }
+        const double mean = count ? sum / (double)count : 0.0;
+        double sq = 0.0;
+        for (int i = 0; i < n; ++i)
+            if (isfinite(s[i])) { const double e = s[i] - mean; sq += e * e; }
+        const double sd = count ? sqrt(sq / (double)count) : 0.0;
+        /* a row that varies by no more than rounding counts as constant */
+        const int flat = sd <= GQA_FLAT * big;
+
+        for (int i = 0; i < n; ++i) {
+            double z = NAN;
+            if (isfinite(s[i])) z = flat ? 0.0 : (s[i] - mean) / sd;
+            if (zrow) zrow[(size_t)g * n + i] = z;
+            if (!isnan(z) && (isnan(score[i]) || z > score[i])) score[i] = z;
+        }
+    }
+    free(s);
+    return 0;
 }
 
 /* ---- top-B selection ---------------------------------------------------- */

@@ -8,6 +8,7 @@ names and semantics are those of ``include/tri.h``:
     ctx = tri_calibrate_load(n_layers, n_kv_heads, head_dim, qc_re, qc_im,
                              q_mean_norm, q_mrl, offsets, rope_theta=...)
     tri_score(ctx, seqs, scores)                         # fp32 per cached key
+    tri_score(ctx, seqs, scores, workspace=ws)           # GQA contexts (n_q_heads > n_kv_heads)
     tri_select_topb(ctx, seqs, scores, budget, window, kept)
     tri_compact_kv(ctx, seqs, kept, budget, window)      # in place; updates seq.len
 
@@ -30,7 +31,8 @@ TRI_OK, TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP, TRI_E_NOMEM = 0, 1, 2, 3, 4
 TRI_F32, TRI_BF16 = 0, 1
 
 EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last_hip_error",
-            "tri_scores_count", "tri_score", "tri_select_topb", "tri_compact_kv")
+            "tri_scores_count", "tri_score", "tri_score_workspace_bytes", "tri_score_ws",
+            "tri_select_topb", "tri_compact_kv")
 
 
 class TriError(RuntimeError):
@@ -50,6 +52,7 @@ class _CalibDesc(ctypes.Structure):
         ("offsets", ctypes.POINTER(ctypes.c_int64)), ("n_offsets", ctypes.c_int32),
         ("qc_re", ctypes.POINTER(ctypes.c_double)), ("qc_im", ctypes.POINTER(ctypes.c_double)),
         ("q_mean_norm", ctypes.POINTER(ctypes.c_double)), ("q_mrl", ctypes.POINTER(ctypes.c_double)),
+        ("n_q_heads", ctypes.c_int32),
     ]
 
 
@@ -82,6 +85,11 @@ def library() -> ctypes.CDLL:
         lib.tri_scores_count.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32]
         lib.tri_score.restype = ctypes.c_int
         lib.tri_score.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq), ctypes.c_int32, vp, vp]
+        lib.tri_score_workspace_bytes.restype = ctypes.c_int64
+        lib.tri_score_workspace_bytes.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32]
+        lib.tri_score_ws.restype = ctypes.c_int
+        lib.tri_score_ws.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq), ctypes.c_int32, vp, vp,
+                                     ctypes.c_int64, vp]
         lib.tri_select_topb.restype = ctypes.c_int
         lib.tri_select_topb.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
                                         ctypes.c_int32, ctypes.c_int32, vp, vp]
@@ -107,12 +115,14 @@ def _check(status: int, what: str):
 class Context:
     """A loaded calibration table (owns the device tables of one tri_ctx)."""
 
-    def __init__(self, handle: int, n_layers: int, n_kv_heads: int, head_dim: int, device: int):
+    def __init__(self, handle: int, n_layers: int, n_kv_heads: int, head_dim: int, device: int,
+                 group: int = 1):
         self.handle = handle
         self.n_layers = n_layers
         self.n_kv_heads = n_kv_heads
         self.head_dim = head_dim
         self.device = device
+        self.group = group          # query heads per KV head
 
     @property
     def n_heads(self) -> int:
@@ -152,13 +162,15 @@ def _f64_ptr(a: np.ndarray):
 
 def tri_calibrate_load(n_layers: int, n_kv_heads: int, head_dim: int, qc_re, qc_im, q_mean_norm,
                        q_mrl, offsets, rope_theta: float = 10000.0, inv_freq=None,
-                       device: Optional[int] = None) -> Context:
-    """Loads a calibration table (host arrays [n_layers][n_kv_heads][head_dim/2])."""
+                       device: Optional[int] = None, n_q_heads: Optional[int] = None) -> Context:
+    """Loads a calibration table (host arrays [n_layers][n_q_heads][head_dim/2];
+    n_q_heads defaults to n_kv_heads, a multiple of it is a GQA grouping)."""
     lib = library()
     if device is None:
         device = torch.cuda.current_device()
+    n_q = n_kv_heads if n_q_heads is None else int(n_q_heads)
     arrs = [np.ascontiguousarray(x, dtype=np.float64) for x in (qc_re, qc_im, q_mean_norm, q_mrl)]
-    shape = (n_layers, n_kv_heads, head_dim // 2)
+    shape = (n_layers, n_q, head_dim // 2)
     for a in arrs:
         if a.shape != shape:
             raise ValueError("calibration arrays must have shape %s, got %s" % (shape, a.shape))
@@ -168,11 +180,11 @@ def tri_calibrate_load(n_layers: int, n_kv_heads: int, head_dim: int, qc_re, qc_
         n_layers, n_kv_heads, head_dim, float(rope_theta),
         _f64_ptr(inv) if inv is not None else None,
         off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(off),
-        _f64_ptr(arrs[0]), _f64_ptr(arrs[1]), _f64_ptr(arrs[2]), _f64_ptr(arrs[3]))
+        _f64_ptr(arrs[0]), _f64_ptr(arrs[1]), _f64_ptr(arrs[2]), _f64_ptr(arrs[3]), n_q)
     h = ctypes.c_void_p()
     _check(lib.tri_calibrate_load(ctypes.byref(desc), int(device), ctypes.byref(h)),
            "tri_calibrate_load")
-    return Context(h.value, n_layers, n_kv_heads, head_dim, int(device))
+    return Context(h.value, n_layers, n_kv_heads, head_dim, int(device), n_q // n_kv_heads)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -218,16 +230,36 @@ def scores_count(ctx: Context, seqs: Sequence[Seq]) -> int:
     return sum(ctx.n_heads * s.len for s in seqs)
 
 
-def tri_score(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, stream=None):
+def score_workspace_bytes(ctx: Context, seqs: Sequence[Seq]) -> int:
+    """Device workspace bytes tri_score needs (0 unless the context is GQA)."""
+    arr, _ = _seq_array(ctx, seqs, need_kv=False)
+    n = library().tri_score_workspace_bytes(ctx.handle, arr, len(seqs))
+    if n < 0:
+        raise ValueError("bad sequences for tri_score_workspace_bytes")
+    return int(n)
+
+
+def tri_score(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, stream=None,
+              workspace: Optional[torch.Tensor] = None):
     """Scores every cached key of every head; ``scores`` fp32 on the GPU with
-    at least scores_count(ctx, seqs) elements, sequence-major [L][H][len]."""
+    at least scores_count(ctx, seqs) elements, sequence-major [L][H][len].
+    GQA contexts also need ``workspace``: a contiguous GPU tensor of at least
+    score_workspace_bytes(ctx, seqs) bytes (tri_score_ws)."""
     arr, dtype = _seq_array(ctx, seqs, need_kv=False)
     if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous() \
             or scores.numel() < scores_count(ctx, seqs):
         raise ValueError("scores must be a contiguous fp32 GPU tensor of %d elements"
                          % scores_count(ctx, seqs))
-    _check(library().tri_score(ctx.handle, dtype, arr, len(seqs), scores.data_ptr(),
-                               _stream_ptr(stream)), "tri_score")
+    if workspace is None:
+        _check(library().tri_score(ctx.handle, dtype, arr, len(seqs), scores.data_ptr(),
+                                   _stream_ptr(stream)), "tri_score")
+        return
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(library().tri_score_ws(ctx.handle, dtype, arr, len(seqs), scores.data_ptr(),
+                                  workspace.data_ptr(), nbytes, _stream_ptr(stream)),
+           "tri_score_ws")
 
 
 def tri_select_topb(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, budget: int,
@@ -267,8 +299,8 @@ def fires(seq: Seq, budget: int, window: int) -> bool:
 
 
 def prune_step(ctx: Context, seqs: List[Seq], budget: int, window: int, scores: torch.Tensor,
-               kept: torch.Tensor, stream=None):
+               kept: torch.Tensor, stream=None, workspace: Optional[torch.Tensor] = None):
     """One prune step (score, select, compact) on one stream, no host sync."""
-    tri_score(ctx, seqs, scores, stream)
+    tri_score(ctx, seqs, scores, stream, workspace)
     tri_select_topb(ctx, seqs, scores, budget, window, kept, stream)
     tri_compact_kv(ctx, seqs, kept, budget, window, stream)

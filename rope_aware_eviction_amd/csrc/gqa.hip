@@ -1,0 +1,468 @@
+// GQA normalize-then-aggregate scoring: G query heads share each KV head.
+//
+// Source: dimensionstp.github.io "TriAttention ... Review", section 3-2
+// item 6 (each query head's key scores are z-score normalized, then the max
+// over the query heads of a KV head is the key's score), and romaanj.github.io
+// "TriAttention" review, section "Method" (GQA: per-head z-score, then max).
+// Readings: the mean and the population standard deviation run over the
+// finite scores of the head's cached keys; a deviation of at most 1e-9 of
+// the largest |score| counts as zero and gives z = 0; a non-finite score
+// gives NaN, which loses to every number in the max.
+//
+// Three launches per sequence:
+//   1. gqa_score_kernel: one pass over K.  Every row gets G raw scores (the
+//      score of the single-query-head kernel with query head g's folded
+//      constants); the band magnitudes |K_f| are shared by the G norm terms.
+//      Raw scores go to the workspace [head][row][g]; per 512-row tile and
+//      query head the kernel also writes fp64 partial statistics (sum, sum
+//      of squares, count of finite scores, largest |score|).
+//   2. gqa_stats_kernel: per (head, g), the partials summed in tile order
+//      (deterministic) into the mean and the deviation (0 when flat).
+//   3. gqa_norm_kernel: z = (s - mean) / sd per query head in fp64, the max
+//      over the group, rounded once to fp32 into the caller's score array.
+#include <type_traits>
+
+#include "tri_internal.h"
+
+namespace tri {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kTileRows = 512;
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource word 3, gfx9 family
+constexpr int kSC1 = 16;                   // cache-policy bits: sc1
+constexpr double kFlat = 1e-9;             // deviation at or below kFlat * max|s| counts as zero
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPR consecutive lanes; every lane of the group
+// receives the total.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "lanes per row");
+    x += dpp<0xB1>(x);                          // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp<0x4E>(x);                          // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8) x += dpp<0x141>(x);   // row_half_mirror: quads of an 8-lane half
+    if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror: halves of a 16-lane row
+    if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+    if constexpr (LPR >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Partner value at lane distance S inside aligned groups (the pairing of
+// each step of the reductions below): xor for 32, 16, 2 and 1; a mirror of
+// the 16-lane row for 8 and of the 8-lane half for 4.  Each pairs a lane
+// whose bit S is clear with one whose bit S is set.
+template <int S>
+__device__ __forceinline__ float partner(float x)
+{
+    if constexpr (S == 32 || S == 16) return __shfl_xor(x, S);
+    else if constexpr (S == 8) return dpp<0x140>(x);   // row_mirror
+    else if constexpr (S == 4) return dpp<0x141>(x);   // row_half_mirror
+    else if constexpr (S == 2) return dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    else return dpp<0xB1>(x);                          // quad_perm [1,0,3,2]
+}
+
+// Sums M values per lane over aligned groups of LPR lanes, M a power of two
+// <= LPR, with the values split between partners: at each of the first
+// log2(M) steps a lane keeps one half of its values, sends the other half
+// and adds what its partner sends, so the work halves every step.  Lane j of
+// a group ends with the group total of value g = j / (LPR / M) (the lanes
+// of one g hold the same total).
+template <int LPR, int S, int M>
+__device__ __forceinline__ float split_reduce(float* v, int j)
+{
+    if constexpr (S == 0) {
+        return v[0];
+    } else if constexpr (M > 1) {
+        const bool lower = (j & S) == 0;
+#pragma unroll
+        for (int k = 0; k < M / 2; ++k) {
+            const float keep = lower ? v[k] : v[M / 2 + k];
+            const float send = lower ? v[M / 2 + k] : v[k];
+            v[k] = keep + partner<S>(send);
+        }
+        return split_reduce<LPR, S / 2, M / 2>(v, j);
+    } else {
+        v[0] += partner<S>(v[0]);
+        return split_reduce<LPR, S / 2, 1>(v, j);
+    }
+}
+
+constexpr int pow2_at_least(int x)
+{
+    int p = 1;
+    while (p < x) p *= 2;
+    return p;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ double wave_max_d(double v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+    return v;
+}
+
+// EB bytes of one half-row per lane, unpacked to fp32 bands.
+template <bool BF16, int EB>
+struct Chunk {
+    static constexpr int kElem = BF16 ? 2 : 4;
+    static constexpr int E = EB / kElem;        // bands per lane
+    static constexpr int W = EB / 4;            // 32-bit words per lane
+    uint32_t w[W];
+    __device__ __forceinline__ void load(const unsigned char* p)
+    {
+        if constexpr (W == 2) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+            w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+        }
+    }
+    __device__ __forceinline__ void unpack(float* out) const
+    {
+#pragma unroll
+        for (int m = 0; m < W; ++m) {
+            if constexpr (BF16) {
+                out[2 * m] = __uint_as_float(w[m] << 16);
+                out[2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+            } else {
+                out[m] = __uint_as_float(w[m]);
+            }
+        }
+    }
+};
+
+template <int D, bool BF16, int G>
+struct GqaShape {
+    static constexpr int kElem = BF16 ? 2 : 4;
+    static constexpr int kHalf = D / 2;
+    static constexpr int kRowBytes = D * kElem;
+    static constexpr int kHalfBytes = kRowBytes / 2;
+    // 8 bytes per lane and half row while G * 3 * bands fits in 48 registers
+    static constexpr int EB = (3 * G * (8 / kElem) <= 48 && kHalfBytes / 8 <= 64) ? 8 : 4;
+    static constexpr int LPR = kHalfBytes / EB;   // lanes per row
+    static constexpr int E = EB / kElem;          // bands per lane
+    static constexpr int RPI = 64 / LPR;          // rows per wave instruction
+    static constexpr int GR = kBlock / LPR;       // rows per workgroup step
+    static constexpr int kUnroll = 64 / EB;       // rows per lane in flight (64 bytes)
+    static_assert(LPR >= 4 && LPR <= 64 && E >= 1, "lane layout");
+    static_assert(3 * G * E <= 48, "folded constants fit in registers");
+    static_assert(kTileRows % (GR * kUnroll) == 0, "a tile is whole iterations");
+};
+
+template <int D, bool BF16, int G>
+__global__ __launch_bounds__(kBlock) void gqa_score_kernel(
+    const unsigned char* __restrict__ k, int64_t cap, int len, int tiles_per_head, double p_now,
+    const double* __restrict__ omega, const double2* __restrict__ qa, const float* __restrict__ w,
+    float* __restrict__ raw, double* __restrict__ partial)
+{
+    using S = GqaShape<D, BF16, G>;
+    constexpr int kHalf = S::kHalf, LPR = S::LPR, E = S::E, GR = S::GR, kUnroll = S::kUnroll;
+    constexpr int GP = pow2_at_least(G);      // query heads padded to a power of two
+    static_assert(GP <= LPR, "one lane per query head in a row group");
+    constexpr int kRowBytes = S::kRowBytes, kHalfBytes = S::kHalfBytes, EB = S::EB;
+
+    __shared__ float s_u[G][D];
+    __shared__ float s_w[G][kHalf];
+    __shared__ float s_raw[kTileRows * G];
+    __shared__ double s_red[kBlock / 64][4];
+
+    const int head = blockIdx.x / tiles_per_head;
+    const int tile = blockIdx.x - head * tiles_per_head;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = tid % LPR;   // lane within the row
+    const int g0 = tid / LPR;  // row within a workgroup step
+    const unsigned char* base = k + (size_t)head * (size_t)cap * kRowBytes + EB * j;
+    const int tile_start = tile * kTileRows;
+    const int row_end = min(len, tile_start + kTileRows);
+
+    Chunk<BF16, EB> re[kUnroll], im[kUnroll];
+    auto load_row = [&](int u, int row) {
+        const unsigned char* p = base + (size_t)min(row, row_end - 1) * kRowBytes;
+        re[u].load(p);
+        im[u].load(p + kHalfBytes);
+    };
+    const int iters = (row_end - tile_start + GR * kUnroll - 1) / (GR * kUnroll);
+    int r0 = tile_start + g0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) load_row(u, r0 + u * GR);   // in flight during the fold
+
+    // fold C_f = E[q_f] A_f e^{i w_f p_now} of each query head in fp64
+    for (int t = tid; t < G * kHalf; t += kBlock) {
+        const int g = t / kHalf, f = t - g * kHalf;
+        double sn, cs;
+        sincos(omega[f] * p_now, &sn, &cs);
+        const double2 a = qa[((size_t)head * G + g) * kHalf + f];
+        s_u[g][f] = (float)(a.x * cs - a.y * sn);
+        s_u[g][f + kHalf] = (float)(a.x * sn + a.y * cs);
+        s_w[g][f] = w[((size_t)head * G + g) * kHalf + f];
+    }
+    __syncthreads();
+    float u_re[G][E], u_im[G][E], wt[G][E];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            u_re[g][e] = s_u[g][j * E + e];
+            u_im[g][e] = s_u[g][kHalf + j * E + e];
+            wt[g][e] = s_w[g][j * E + e];
+        }
+
+    // rolling pipeline as in the single-query-head kernel
+    for (int it = 0; it < iters; ++it) {
+        const int r_next = r0 + GR * kUnroll;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float a[E], b[E];
+            re[u].unpack(a);
+            im[u].unpack(b);
+            load_row(u, r_next + u * GR);
+            __builtin_amdgcn_sched_barrier(0);
+            float mag[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) mag[e] = __builtin_amdgcn_sqrtf(fmaf(a[e], a[e], b[e] * b[e]));
+            float part[GP];
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                float t = 0.f;
+                if (g < G) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        t = fmaf(u_re[g][e], a[e], t);
+                        t = fmaf(u_im[g][e], b[e], t);
+                    }
+                    float nrm = 0.f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) nrm = fmaf(wt[g][e], mag[e], nrm);
+                    t += nrm;
+                }
+                part[g] = t;
+            }
+            const float total = split_reduce<LPR, LPR / 2, GP>(part, j);
+            const int gq = j / (LPR / GP);           // query head whose total this lane holds
+            if (j % (LPR / GP) == 0 && gq < G)
+                s_raw[(r0 + u * GR - tile_start) * G + gq] = total;   // < kTileRows * G
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        r0 = r_next;
+    }
+    __syncthreads();
+
+    // raw scores of the tile: rows [tile_start, row_end) x G, contiguous
+    const int n_out = (row_end - tile_start) * G;
+    float* out = raw + ((size_t)head * (size_t)len + tile_start) * G;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, n_out * 4, kBufferWord3);
+    for (int i = tid; i < n_out; i += kBlock)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_raw[i]), ro, i * 4, 0, kSC1);
+
+    // fp64 partial statistics of the tile per query head, in a fixed order
+    double* pt = partial + (((size_t)head * tiles_per_head + tile) * G) * 4;
+    const int n_rows = row_end - tile_start;
+    for (int g = 0; g < G; ++g) {
+        double s1 = 0.0, s2 = 0.0, cnt = 0.0, big = 0.0;
+        for (int r = tid; r < n_rows; r += kBlock) {
+            const double x = (double)s_raw[r * G + g];
+            if (isfinite(x)) {
+                s1 += x;
+                s2 += x * x;
+                cnt += 1.0;
+                big = fmax(big, fabs(x));
+            }
+        }
+        s1 = wave_sum_d(s1);
+        s2 = wave_sum_d(s2);
+        cnt = wave_sum_d(cnt);
+        big = wave_max_d(big);
+        if (lane == 0) {
+            s_red[wave][0] = s1;
+            s_red[wave][1] = s2;
+            s_red[wave][2] = cnt;
+            s_red[wave][3] = big;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double a1 = 0.0, a2 = 0.0, ac = 0.0, ab = 0.0;
+            for (int x = 0; x < kBlock / 64; ++x) {
+                a1 += s_red[x][0];
+                a2 += s_red[x][1];
+                ac += s_red[x][2];
+                ab = fmax(ab, s_red[x][3]);
+            }
+            pt[g * 4 + 0] = a1;
+            pt[g * 4 + 1] = a2;
+            pt[g * 4 + 2] = ac;
+            pt[g * 4 + 3] = ab;
+        }
+        __syncthreads();
+    }
+}
+
+// mean and deviation per (head, query head): one wave per head; lane t sums
+// tiles t, t + 64, ... in order, then a fixed butterfly combines the lanes,
+// so the result does not depend on scheduling
+__global__ __launch_bounds__(64) void gqa_stats_kernel(const double* __restrict__ partial,
+                                                       int tiles_per_head, int group,
+                                                       double2* __restrict__ stats)
+{
+    const int head = blockIdx.x;
+    const int lane = threadIdx.x;
+    for (int g = 0; g < group; ++g) {
+        double s1 = 0.0, s2 = 0.0, cnt = 0.0, big = 0.0;
+        for (int tile = lane; tile < tiles_per_head; tile += 64) {
+            const double* p = partial + (((size_t)head * tiles_per_head + tile) * group + g) * 4;
+            s1 += p[0];
+            s2 += p[1];
+            cnt += p[2];
+            big = fmax(big, p[3]);
+        }
+        s1 = wave_sum_d(s1);
+        s2 = wave_sum_d(s2);
+        cnt = wave_sum_d(cnt);
+        big = wave_max_d(big);
+        if (lane == 0) {
+            double mean = 0.0, sd = 0.0;
+            if (cnt > 0.0) {
+                mean = s1 / cnt;
+                sd = sqrt(fmax(s2 / cnt - mean * mean, 0.0));
+                if (sd <= kFlat * big) sd = 0.0;
+            }
+            stats[(size_t)head * group + g] = make_double2(mean, sd);
+        }
+    }
+}
+
+// z per query head in fp64, max over the group, rounded once to fp32
+template <int G>
+__global__ __launch_bounds__(kBlock) void gqa_norm_kernel(const float* __restrict__ raw,
+                                                          const double2* __restrict__ stats,
+                                                          int len, int tiles_per_head,
+                                                          float* __restrict__ scores)
+{
+    __shared__ double s_mean[G], s_inv[G];   // s_inv = 0: flat row, z = 0
+    const int head = blockIdx.x / tiles_per_head;
+    const int tile = blockIdx.x - head * tiles_per_head;
+    if (threadIdx.x < G) {
+        const double2 st = stats[(size_t)head * G + threadIdx.x];
+        s_mean[threadIdx.x] = st.x;
+        s_inv[threadIdx.x] = st.y > 0.0 ? 1.0 / st.y : 0.0;
+    }
+    __syncthreads();
+    const int row_end = min(len, (tile + 1) * kTileRows);
+    for (int r = tile * kTileRows + threadIdx.x; r < row_end; r += kBlock) {
+        const float* p = raw + ((size_t)head * len + r) * G;
+        float x[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) x[g] = __builtin_nontemporal_load(p + g);
+        double best = NAN;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const double s = (double)x[g];
+            if (isfinite(s)) {
+                const double z = (s - s_mean[g]) * s_inv[g];
+                if (isnan(best) || z > best) best = z;
+            }
+        }
+        scores[(size_t)head * len + r] = (float)best;
+    }
+}
+
+template <int D, bool BF16, int G>
+hipError_t launch_g(const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
+                    const double* omega, const double2* qa, const float* w, float* raw,
+                    double* partial, double2* stats, float* scores, hipStream_t stream)
+{
+    const int tiles = (len + kTileRows - 1) / kTileRows;
+    const int64_t grid = (int64_t)tiles * n_heads;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gqa_score_kernel<D, BF16, G>), dim3((unsigned)grid), dim3(kBlock), 0,
+                       stream, static_cast<const unsigned char*>(k), cap, len, tiles,
+                       (double)p_now, omega, qa, w, raw, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gqa_stats_kernel, dim3(n_heads), dim3(64), 0, stream, partial, tiles, G,
+                       stats);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gqa_norm_kernel<G>), dim3((unsigned)grid), dim3(kBlock), 0, stream, raw,
+                       stats, len, tiles, scores);
+    return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_d(int group, const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
+                    const double* omega, const double2* qa, const float* w, float* raw,
+                    double* partial, double2* stats, float* scores, hipStream_t stream)
+{
+#define TRI_GQA_CASE(G)                                                                           \
+    case G:                                                                                       \
+        return launch_g<D, BF16, G>(k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,      \
+                                    stats, scores, stream);
+    switch (group) {
+        TRI_GQA_CASE(2)
+        TRI_GQA_CASE(3)
+        TRI_GQA_CASE(4)
+        TRI_GQA_CASE(5)
+        TRI_GQA_CASE(6)
+        TRI_GQA_CASE(7)
+        TRI_GQA_CASE(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef TRI_GQA_CASE
+}
+
+}  // namespace
+
+int64_t gqa_workspace_bytes(int64_t n_heads, int64_t len, int group)
+{
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    const int64_t tiles = (len + kTileRows - 1) / kTileRows;
+    return up(n_heads * len * group * 4) + up(n_heads * tiles * group * 4 * 8) +
+           up(n_heads * group * 16);
+}
+
+hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void* k, int64_t cap,
+                            int len, int n_heads, int64_t p_now, const double* omega,
+                            const double2* qa, const float* w, void* workspace, float* scores,
+                            hipStream_t stream)
+{
+    if (len <= 0 || n_heads <= 0) return hipSuccess;
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    const int64_t tiles = (len + kTileRows - 1) / kTileRows;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* raw = reinterpret_cast<float*>(ws);
+    double* partial = reinterpret_cast<double*>(ws + up((int64_t)n_heads * len * group * 4));
+    double2* stats = reinterpret_cast<double2*>(ws + up((int64_t)n_heads * len * group * 4) +
+                                                up((int64_t)n_heads * tiles * group * 4 * 8));
+    if (dtype == TRI_BF16 && head_dim == 128)
+        return launch_d<128, true>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
+                                   stats, scores, stream);
+    if (dtype == TRI_F32 && head_dim == 64)
+        return launch_d<64, false>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
+                                   stats, scores, stream);
+    if (dtype == TRI_BF16 && head_dim == 64)
+        return launch_d<64, true>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
+                                  stats, scores, stream);
+    if (dtype == TRI_F32 && head_dim == 128)
+        return launch_d<128, false>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
+                                    stats, scores, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tri

@@ -100,9 +100,14 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
     if (d->n_layers < 1 || d->n_kv_heads < 1 || d->n_offsets < 1 || device < 0) return TRI_E_INVAL;
     if ((int64_t)d->n_layers * d->n_kv_heads > (1 << 24)) return TRI_E_INVAL;
     if (!d->offsets || !d->qc_re || !d->qc_im || !d->q_mean_norm || !d->q_mrl) return TRI_E_INVAL;
+    // query heads per KV head: 1, or a GQA group of 2..8
+    const int n_q = d->n_q_heads == 0 ? d->n_kv_heads : d->n_q_heads;
+    if (n_q < d->n_kv_heads || n_q % d->n_kv_heads != 0) return TRI_E_INVAL;
+    const int group = n_q / d->n_kv_heads;
+    if (group > 8) return TRI_E_UNSUPPORTED;
     const int half = d->head_dim / 2;
     const int n_heads = d->n_layers * d->n_kv_heads;
-    const size_t nb = (size_t)n_heads * half;
+    const size_t nb = (size_t)n_heads * group * half;   // query tables, [head][g][band]
     if (d->inv_freq) {
         for (int f = 0; f < half; ++f)
             if (!std::isfinite(d->inv_freq[f]) || !(d->inv_freq[f] > 0.0)) return TRI_E_INVAL;
@@ -133,6 +138,7 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
     ctx->n_kv_heads = d->n_kv_heads;
     ctx->head_dim = d->head_dim;
     ctx->n_heads = n_heads;
+    ctx->group = group;
 
     // raw table staged on the device, derived tables computed there in fp64
     double *r_inv = nullptr, *r_re = nullptr, *r_im = nullptr, *r_m = nullptr, *r_R = nullptr;
@@ -167,7 +173,7 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
     put(r_m, d->q_mean_norm, sizeof(double) * nb);
     put(r_R, d->q_mrl, sizeof(double) * nb);
     if (st == TRI_OK) {
-        e = tri::launch_calibrate(n_heads, d->head_dim, d->rope_theta, r_inv, r_off, d->n_offsets,
+        e = tri::launch_calibrate(n_heads * group, d->head_dim, d->rope_theta, r_inv, r_off, d->n_offsets,
                                   r_re, r_im, r_m, r_R, ctx->omega, ctx->qa, ctx->w, nullptr);
         if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
         if (e != hipSuccess) st = hip_fail(e);
@@ -202,30 +208,60 @@ int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
     return total;
 }
 
-tri_status tri_score(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, int32_t n_seq,
-                     float* scores, void* stream)
+int64_t tri_score_workspace_bytes(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
+{
+    if (!ctx || n_seq < 0 || (n_seq > 0 && !seqs)) return -1;
+    if (ctx->group == 1) return 0;
+    int64_t total = 0;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        if (seqs[s].len < 0) return -1;
+        if (seqs[s].len > 0) total += tri::gqa_workspace_bytes(ctx->n_heads, seqs[s].len, ctx->group);
+    }
+    return total;
+}
+
+tri_status tri_score_ws(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, int32_t n_seq,
+                        float* scores, void* workspace, int64_t workspace_bytes, void* stream)
 {
     tri_status st = check_seqs(ctx, seqs, n_seq, false);
     if (st != TRI_OK) return st;
     if (!supported(ctx->head_dim, dtype)) return TRI_E_UNSUPPORTED;
     const int64_t total = tri_scores_count(ctx, seqs, n_seq);
     if (total > 0 && (!scores || ((uintptr_t)scores & 3u))) return TRI_E_INVAL;
+    const int64_t need = tri_score_workspace_bytes(ctx, seqs, n_seq);
+    if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+        return TRI_E_INVAL;
     if (total == 0) return TRI_OK;
     st = check_device(ctx);
     if (st != TRI_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int64_t off = 0;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
     for (int32_t s = 0; s < n_seq; ++s) {
         const tri_seq& q = seqs[s];
         if (q.len > 0) {
-            hipError_t e = tri::launch_score(dtype, ctx->head_dim, q.k, q.cap, q.len, ctx->n_heads,
-                                             q.p_now, ctx->omega, ctx->qa, ctx->w, scores + off,
-                                             hs);
+            hipError_t e;
+            if (ctx->group == 1) {
+                e = tri::launch_score(dtype, ctx->head_dim, q.k, q.cap, q.len, ctx->n_heads, q.p_now,
+                                      ctx->omega, ctx->qa, ctx->w, scores + off, hs);
+            } else {
+                e = tri::launch_gqa_score(dtype, ctx->head_dim, ctx->group, q.k, q.cap, q.len,
+                                          ctx->n_heads, q.p_now, ctx->omega, ctx->qa, ctx->w, ws,
+                                          scores + off, hs);
+                ws += tri::gqa_workspace_bytes(ctx->n_heads, q.len, ctx->group);
+            }
             if (e != hipSuccess) return hip_fail(e);
         }
         off += (int64_t)ctx->n_heads * q.len;
     }
     return TRI_OK;
+}
+
+tri_status tri_score(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, int32_t n_seq,
+                     float* scores, void* stream)
+{
+    if (ctx && ctx->group != 1) return TRI_E_INVAL;   // GQA needs tri_score_ws
+    return tri_score_ws(ctx, dtype, seqs, n_seq, scores, nullptr, 0, stream);
 }
 
 tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,

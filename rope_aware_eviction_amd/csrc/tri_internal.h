@@ -12,9 +12,10 @@ struct tri_ctx {
     int n_kv_heads;
     int head_dim;
     int n_heads;          // n_layers * n_kv_heads
+    int group;            // query heads per KV head (1: one query table per KV head)
     double* omega;        // device [head_dim/2]        band frequencies
-    double2* qa;          // device [n_heads][head_dim/2] E[q_f] * A_f (complex, fp64)
-    float* w;             // device [n_heads][head_dim/2] (1 - R_f) * E|q_f|
+    double2* qa;          // device [n_heads][group][head_dim/2] E[q_f] * A_f (complex, fp64)
+    float* w;             // device [n_heads][group][head_dim/2] (1 - R_f) * E|q_f|
 };
 
 namespace tri {
@@ -35,6 +36,14 @@ hipError_t launch_calibrate(int n_heads, int head_dim, double rope_theta, const 
 hipError_t launch_score(tri_dtype dtype, int head_dim, const void* k, int64_t cap, int len,
                         int n_heads, int64_t p_now, const double* omega, const double2* qa,
                         const float* w, float* scores, hipStream_t stream);
+
+// GQA (group >= 2): G raw scores per key, per-query-head statistics, then
+// the normalized max into `scores`.  `workspace` holds gqa_workspace_bytes.
+int64_t gqa_workspace_bytes(int64_t n_heads, int64_t len, int group);
+hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void* k, int64_t cap,
+                            int len, int n_heads, int64_t p_now, const double* omega,
+                            const double2* qa, const float* w, void* workspace, float* scores,
+                            hipStream_t stream);
 
 // Top-`budget` of each of n_heads score rows of length n.
 hipError_t launch_select(const float* scores, int n, int n_heads, int budget, int32_t* kept,

@@ -21,6 +21,13 @@ Workloads (the five cache shapes the pass is specified on):
              20% of slots hold a copy of another slot's stored row with one
              element nudged by one bf16 ulp (adversarial near-ties).
 
+GQA workloads (G query heads share each KV head; query head g > 0 of a group
+has its own centre, concentration and a score scale e^U(-0.7, 0.7)):
+``gqa_toy`` (toy shape, G = 2, fp32), ``gqa_small`` (2 x 4, d 128, 4096 keys,
+G = 4, bf16), ``gqa_g7`` (1 x 4, d 128, G = 7, phase recipe), ``gqa_g8_d64``
+(2 x 2, d 64, 8192 keys, G = 8) and ``qwen3_32k_gqa`` (the qwen3_32k shape with
+G = 4: 32 query heads over 8 KV heads).
+
 Recipe details and the readings behind them are written out in each
 ``_draw_*`` function.  Calibration statistics and key centres (the "model")
 are drawn on the host in fp64 from numpy and do not depend on the device;
@@ -59,6 +66,11 @@ class Spec:
     recipe: str             # "toy", "concentrated", "phase", "neartie"
     outlier_frac: float = 0.0
     dup_frac: float = 0.0
+    group: int = 1          # query heads per KV head (GQA); 1 = one query table per KV head
+
+    @property
+    def n_q_heads(self) -> int:
+        return self.n_kv_heads * self.group
 
     @property
     def n_seq(self) -> int:
@@ -106,10 +118,27 @@ def workload(name: str, seed: int = 0) -> Spec:
     if name == "wide":
         return Spec("wide", 64, 8, 128, 1e6, (131072,), 8192, 128, "bf16",
                     pow2_offsets(16), "neartie", dup_frac=0.20)
+    # GQA: several query heads per KV head, each with its own calibration
+    if name == "gqa_toy":
+        return Spec("gqa_toy", 1, 2, 64, 1e4, (512,), 128, 128, "f32", pow2_offsets(12), "toy",
+                    group=2)
+    if name == "gqa_small":
+        return Spec("gqa_small", 2, 4, 128, 5e5, (4096,), 1024, 128, "bf16", pow2_offsets(16),
+                    "concentrated", outlier_frac=0.05, group=4)
+    if name == "gqa_g7":
+        return Spec("gqa_g7", 1, 4, 128, 1e6, (4096,), 1024, 128, "bf16", pow2_offsets(16),
+                    "phase", group=7)
+    if name == "gqa_g8_d64":
+        return Spec("gqa_g8_d64", 2, 2, 64, 1.5e5, (8192,), 2048, 128, "bf16", pow2_offsets(16),
+                    "concentrated", group=8)
+    if name == "qwen3_32k_gqa":
+        return Spec("qwen3_32k_gqa", 36, 8, 128, 1e6, (32768,), 4096, 128, "bf16",
+                    pow2_offsets(16), "phase", group=4)
     raise KeyError(name)
 
 
 WORKLOADS = ("toy", "llama8b", "qwen3_32k", "batched", "wide")
+GQA_WORKLOADS = ("gqa_toy", "gqa_small", "gqa_g7", "gqa_g8_d64", "qwen3_32k_gqa")
 
 
 # --------------------------------------------------------------------------
@@ -137,7 +166,8 @@ def _torch_gen(device, seed: int, *parts) -> torch.Generator:
 
 @dataclasses.dataclass
 class Calib:
-    """Query-side calibration table, fp64, each [n_layers][n_kv_heads][d/2]."""
+    """Query-side calibration table, fp64, each [n_layers][n_q_heads][d/2]
+    (query heads j*G .. j*G+G-1 share KV head j)."""
     qc_re: np.ndarray
     qc_im: np.ndarray
     q_mean_norm: np.ndarray
@@ -158,38 +188,51 @@ def _model(spec: Spec, seed: int):
     taken for every workload that does not say otherwise).  Band f of a
     vector x is x[f] + i*x[f+d/2].
     """
-    L, H, d = spec.n_layers, spec.n_kv_heads, spec.head_dim
+    L, H, d, G = spec.n_layers, spec.n_kv_heads, spec.head_dim, spec.group
     h = d // 2
     kc = np.empty((L, H, d))
-    qc_re = np.empty((L, H, h))
-    qc_im = np.empty((L, H, h))
-    qm = np.empty((L, H, h))
-    qr = np.empty((L, H, h))
+    qc_re = np.empty((L, H * G, h))
+    qc_im = np.empty((L, H * G, h))
+    qm = np.empty((L, H * G, h))
+    qr = np.empty((L, H * G, h))
     conc = np.empty((L, H))
+
+    def query_table(rng, zq, R_h=None):
+        if spec.recipe == "phase":
+            # Query band phases with mean resultant length R_h: the
+            # calibrated centre is |c_f| * R_h * e^{i arg c_f}, the mean
+            # norm |c_f|, the band MRL R_h.
+            qc = np.abs(zq) * R_h * np.exp(1j * np.angle(zq))
+            return qc.real, qc.imag, np.abs(zq), np.full(h, R_h)
+        # E[q_f] = centre band; E|q_f| = |E q_f| * (1 + U(0, 0.5));
+        # R_f = |E q_f| / E|q_f| (consistent MRL).
+        m = np.abs(zq) * (1.0 + rng.uniform(0.0, 0.5, size=h))
+        return zq.real, zq.imag, m, np.abs(zq) / m
+
     for l in range(L):
         for j in range(H):
             rng = _np_rng(seed, spec.name, "model", l, j)
             kc[l, j] = _unit_norm_scaled(rng, d, 4.0)
             cq = _unit_norm_scaled(rng, d, 4.0)
             zq = cq[:h] + 1j * cq[h:]
+            R_h = None
             if spec.recipe == "phase":
-                # Query band phases with mean resultant length R_h: the
-                # calibrated centre is |c_f| * R_h * e^{i arg c_f}, the mean
-                # norm |c_f|, the band MRL R_h.
                 R_h = rng.uniform(0.6, 0.99)
                 conc[l, j] = R_h
-                qc = np.abs(zq) * R_h * np.exp(1j * np.angle(zq))
-                qc_re[l, j], qc_im[l, j] = qc.real, qc.imag
-                qm[l, j] = np.abs(zq)
-                qr[l, j] = R_h
             else:
-                # E[q_f] = centre band; E|q_f| = |E q_f| * (1 + U(0, 0.5));
-                # R_f = |E q_f| / E|q_f| (consistent MRL).
-                qc_re[l, j], qc_im[l, j] = zq.real, zq.imag
-                m = np.abs(zq) * (1.0 + rng.uniform(0.0, 0.5, size=h))
-                qm[l, j] = m
-                qr[l, j] = np.abs(zq) / m
                 conc[l, j] = np.nan
+            row = j * G
+            qc_re[l, row], qc_im[l, row], qm[l, row], qr[l, row] = query_table(rng, zq, R_h)
+            # GQA: the other query heads of the group have their own centres,
+            # concentrations and score scales (scale e^U(-0.7, 0.7)), which is
+            # what makes per-query-head normalization matter.
+            for g in range(1, G):
+                rq = _np_rng(seed, spec.name, "model-q", l, j, g)
+                cq = _unit_norm_scaled(rq, d, 4.0) * math.exp(rq.uniform(-0.7, 0.7))
+                zq = cq[:h] + 1j * cq[h:]
+                R_g = rq.uniform(0.6, 0.99) if spec.recipe == "phase" else None
+                qc_re[l, row + g], qc_im[l, row + g], qm[l, row + g], qr[l, row + g] = \
+                    query_table(rq, zq, R_g)
     calib = Calib(qc_re, qc_im, qm, qr, float(spec.rope_theta),
                   np.asarray(spec.offsets, dtype=np.int64))
     return kc, conc, calib

@@ -70,7 +70,8 @@ def _desc(**over):
     d = tri._CalibDesc(over.get("n_layers", 1), over.get("n_kv_heads", 2), over.get("head_dim", 64),
                        over.get("rope_theta", 1e4), None,
                        off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(off),
-                       p(arr["qc_re"]), p(arr["qc_im"]), p(arr["q_mean_norm"]), p(arr["q_mrl"]))
+                       p(arr["qc_re"]), p(arr["qc_im"]), p(arr["q_mean_norm"]), p(arr["q_mrl"]),
+                       over.get("n_q_heads", 0))
     return d, keep
 
 
@@ -85,6 +86,10 @@ def _desc(**over):
     ({"q_mrl": np.full((1, 2, 32), 1.5)}, tri.TRI_E_INVAL),
     ({"q_mean_norm": np.full((1, 2, 32), -1.0)}, tri.TRI_E_INVAL),
     ({"qc_re": np.full((1, 2, 32), np.inf)}, tri.TRI_E_INVAL),
+    ({"n_q_heads": 3}, tri.TRI_E_INVAL),          # not a multiple of the 2 KV heads
+    ({"n_q_heads": 1}, tri.TRI_E_INVAL),          # fewer query heads than KV heads
+    ({"n_q_heads": -2}, tri.TRI_E_INVAL),
+    ({"n_q_heads": 18}, tri.TRI_E_UNSUPPORTED),   # group of 9
 ])
 def test_calibrate_rejects_bad_tables_before_any_hip_call(lib, over, status):
     d, keep = _desc(**over)
@@ -101,4 +106,6 @@ def test_calls_reject_null_context_and_bad_shapes(lib):
     assert lib.tri_select_topb(None, arr, 1, None, 4, 0, None, None) == tri.TRI_E_INVAL
     assert lib.tri_compact_kv(None, tri.TRI_BF16, arr, 1, None, 4, 0, None) == tri.TRI_E_INVAL
     assert lib.tri_scores_count(None, arr, 1) == -1
+    assert lib.tri_score_ws(None, tri.TRI_BF16, arr, 1, None, None, 0, None) == tri.TRI_E_INVAL
+    assert lib.tri_score_workspace_bytes(None, arr, 1) == -1
     lib.tri_ctx_destroy(None)     # allowed

@@ -1,0 +1,200 @@
+"""GPU parity of the GQA normalize-then-aggregate score (tri_score_ws)
+against the fp64 oracle, called through the C ABI.
+
+Source: dimensionstp.github.io TriAttention review, section 3-2 item 6, and
+romaanj.github.io TriAttention review, section "Method".
+
+Bar (derived from the arithmetic): the GPU's raw per-query-head scores carry
+the single-head score error, at most e * M_{g,i} with e = 2e-3 and M the
+oracle's per-key bound; the mean then moves by at most e * mean(M_g) and the
+deviation by at most e * rms(M_g), so
+    |z_gpu - z_ref| <= e * (M_{g,i} + mean(M_g) + |z_ref| * rms(M_g)) / sd_g,
+and the max over the group inherits the largest of these.  Kept sets are
+checked as in the single-head parity tests with that per-key tolerance:
+keys clearly above the B-th aggregated score are kept, keys clearly below
+are evicted, disagreements lie within 1/20 of the tolerance band of the
+threshold.  GPU-internal properties (ascending kept lists of B keys that are
+the top-B of the GPU's own scores, bit-exact compaction, run-to-run
+determinism) are checked on every head.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import rope_aware_eviction_amd as tri
+from test_gpu_parity import bits, check_topb_property, head_inputs, say, seqs_for
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+TIGHT = TOL / 20
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    return oracle.load()
+
+
+def ctx_gqa(cache):
+    sp, cal = cache.spec, cache.calib
+    return tri.tri_calibrate_load(sp.n_layers, sp.n_kv_heads, sp.head_dim, cal.qc_re, cal.qc_im,
+                                  cal.q_mean_norm, cal.q_mrl, cal.offsets,
+                                  rope_theta=cal.rope_theta, device=0, n_q_heads=sp.n_q_heads)
+
+
+def workspace_for(ctx, seqs):
+    n = tri.score_workspace_bytes(ctx, seqs)
+    assert n > 0
+    return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def oracle_gqa(orc, cache, s, l, h, K, P):
+    """Aggregated score, per-key tolerance and the per-query-head pieces."""
+    sp, cal = cache.spec, cache.calib
+    G = sp.group
+    om = orc.omega(sp.head_dim, sp.rope_theta)
+    rows = slice(h * G, (h + 1) * G)
+    args = (cal.qc_re[l, rows], cal.qc_im[l, rows], cal.q_mean_norm[l, rows], cal.q_mrl[l, rows])
+    raw, z, score = orc.gqa_head(K, P, cache.p_now[s], om, cal.offsets, *args)
+    tol = np.zeros(len(score))
+    for g in range(G):
+        M = orc.bound_head(K, om, cal.offsets, cal.qc_re[l, h * G + g], cal.qc_im[l, h * G + g],
+                           cal.q_mean_norm[l, h * G + g], cal.q_mrl[l, h * G + g])
+        fin = np.isfinite(raw[g])
+        sd = raw[g][fin].std()
+        if sd > 0:
+            zg = np.where(np.isfinite(z[g]), np.abs(z[g]), 0.0)
+            tg = TOL * (M + M[fin].mean() + zg * np.sqrt((M[fin] ** 2).mean())) / sd
+            tol = np.maximum(tol, tg)
+    return score, tol
+
+
+def check_agg(s_gpu, s_ref, tol, what):
+    assert np.array_equal(np.isnan(s_gpu), np.isnan(s_ref)), what + ": NaN pattern differs"
+    m = ~np.isnan(s_ref)
+    err = np.abs(s_gpu[m].astype(np.float64) - s_ref[m])
+    ratio = err / np.maximum(tol[m], 1e-300)
+    say("  %s: max |dz| = %.3g, max |dz|/tol = %.3g over %d keys" % (what, err.max(), ratio.max(), m.sum()))
+    assert np.all(err <= tol[m]), what
+
+
+def check_kept(orc, s_ref, tol, P, kept_gpu, B, window, what):
+    n = len(s_ref)
+    kept_ref = orc.select_head(s_ref, P, B, window)
+    key = np.where(np.isnan(s_ref), -np.inf, s_ref)
+    order = np.lexsort((P, -key))
+    ti = order[B - 1]
+    t, tt = key[ti], tol[ti]
+    sel = np.zeros(n, bool)
+    sel[kept_gpu] = True
+    assert sel.sum() == B
+    band = tol + tt
+    assert sel[key > t + band].all(), what + ": a clearly kept key was evicted"
+    assert not sel[key < t - band].any(), what + ": a clearly evicted key was kept"
+    ref = np.zeros(n, bool)
+    ref[kept_ref] = True
+    dis = np.nonzero(ref != sel)[0]
+    if len(dis):
+        assert np.all(np.abs(key[dis] - t) <= (TIGHT / TOL) * band[dis]), what
+    say("  %s: kept-set disagreements with the oracle: %d of %d" % (what, len(dis), B))
+
+
+@pytest.mark.parametrize("name,heads", [("gqa_toy", None), ("gqa_small", None), ("gqa_g7", 2),
+                                        ("gqa_g8_d64", 2)])
+def test_gqa_scores_match_oracle(orc, name, heads):
+    spec = synth.workload(name)
+    say("gqa scores", name, "G =", spec.group)
+    cache = synth.make_cache(spec, "cuda", seed=3)
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    n = cache.lens[0]
+    scores = torch.full((spec.heads * n,), float("nan"), device="cuda")
+    tri.tri_score(ctx, seqs, scores, workspace=ws)
+    torch.cuda.synchronize()
+    sg = scores.cpu().numpy().reshape(spec.n_layers, spec.n_kv_heads, n)
+    pairs = [(l, h) for l in range(spec.n_layers) for h in range(spec.n_kv_heads)]
+    if heads is not None:
+        pairs = [pairs[0], pairs[-1]][:heads]
+    for l, h in pairs:
+        K, _, P = head_inputs(cache, 0, l, h)
+        s_ref, tol = oracle_gqa(orc, cache, 0, l, h, K, P)
+        check_agg(sg[l, h], s_ref, tol, "%s l%d h%d" % (name, l, h))
+
+
+def test_gqa_needs_its_workspace():
+    spec = synth.workload("gqa_toy")
+    cache = synth.make_cache(spec, "cuda", seed=4)
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    scores = torch.empty(spec.heads * cache.lens[0], device="cuda")
+    with pytest.raises(tri.TriError) as e:
+        tri.tri_score(ctx, seqs, scores)
+    assert e.value.status == tri.TRI_E_INVAL
+    small = torch.empty(tri.score_workspace_bytes(ctx, seqs) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tri.TriError) as e:
+        tri.tri_score(ctx, seqs, scores, workspace=small)
+    assert e.value.status == tri.TRI_E_INVAL
+
+
+def test_gqa_deterministic_and_flat_and_nonfinite_rows(orc):
+    """Two runs agree bit for bit; a head whose keys are all one row gets
+    score 0 everywhere (every query head is flat); non-finite keys score NaN
+    and drop out of the statistics of the others."""
+    spec = synth.workload("gqa_toy").replace(lengths=(700,))
+    cache = synth.make_cache(spec, "cuda", seed=5)
+    k = cache.k[0]
+    k[0, 0, :700] = k[0, 0, 3].clone()
+    cache.pos[0][0, 0, :700] = 650          # same row and position: equal scores
+    k[0, 1, 17, 5] = float("inf")
+    k[0, 1, 301, 0] = float("nan")
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    a = torch.empty(2 * 700, device="cuda")
+    b = torch.empty(2 * 700, device="cuda")
+    tri.tri_score(ctx, seqs, a, workspace=ws)
+    tri.tri_score(ctx, seqs, b, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(a), bits(b))
+    sg = a.cpu().numpy().reshape(2, 700)
+    assert np.all(sg[0] == 0.0)
+    K, _, P = head_inputs(cache, 0, 0, 1)
+    s_ref, tol = oracle_gqa(orc, cache, 0, 0, 1, K, P)
+    assert np.isnan(sg[1, 17]) and np.isnan(sg[1, 301])
+    check_agg(sg[1], s_ref, tol, "gqa non-finite keys")
+
+
+@pytest.mark.parametrize("name,sample", [("gqa_small", None), ("qwen3_32k_gqa", [(0, 0), (35, 7)])])
+def test_gqa_fused_pass(orc, name, sample):
+    spec = synth.workload(name)
+    B, W = spec.budget, spec.window
+    say("gqa fused pass", name)
+    cache = synth.make_cache(spec, "cuda", seed=6)
+    n = cache.lens[0]
+    pairs = sample or [(l, h) for l in range(spec.n_layers) for h in range(spec.n_kv_heads)]
+    inputs = {(l, h): head_inputs(cache, 0, l, h) for l, h in pairs}
+    k_in, v_in, p_in = cache.k[0].clone(), cache.v[0].clone(), cache.pos[0].clone()
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    scores = torch.empty(spec.heads * n, device="cuda")
+    kept = torch.empty(spec.heads * B, dtype=torch.int32, device="cuda")
+    tri.prune_step(ctx, seqs, B, W, scores, kept, workspace=ws)
+    torch.cuda.synchronize()
+    assert seqs[0].len == B
+    check_topb_property(scores.view(spec.heads, n), kept.view(spec.heads, B), n)
+    # compaction: rows r < B are the input rows at the GPU's kept list
+    kl = kept.view(spec.n_layers, spec.n_kv_heads, B).long()
+    for t_in, t_out in ((k_in, cache.k[0]), (v_in, cache.v[0])):
+        g = torch.gather(t_in, 2, kl[..., None].expand(-1, -1, -1, spec.head_dim))
+        assert torch.equal(bits(g), bits(t_out[:, :, :B]))
+    assert torch.equal(torch.gather(p_in, 2, kl), cache.pos[0][:, :, :B])
+    kg = kept.view(spec.n_layers, spec.n_kv_heads, B).cpu().numpy()
+    for (l, h), (K, _, P) in inputs.items():
+        s_ref, tol = oracle_gqa(orc, cache, 0, l, h, K, P)
+        check_kept(orc, s_ref, tol, P, kg[l, h], B, W, "%s l%d h%d" % (name, l, h))

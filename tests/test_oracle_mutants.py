@@ -11,6 +11,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_gqa as gqa_pins
 import test_oracle_pins as pins
 
 MUTANTS = {
@@ -37,6 +38,17 @@ MUTANTS = {
                              "if ((int64_t)n < (int64_t)budget + (int64_t)window) return 0;"),
     "kept list left in rank order": ("qsort(kept, (size_t)budget, sizeof(int32_t), by_int32);", ""),
     "gather copies the wrong row": ("s + (size_t)kept[r] * (size_t)row_bytes", "s + (size_t)r * (size_t)row_bytes"),
+    "GQA sample instead of population deviation": ("sqrt(sq / (double)count)",
+                                                   "sqrt(sq / (double)(count > 1 ? count - 1 : 1))"),
+    "GQA min instead of max over the group": ("z > score[i]", "z < score[i]"),
+    "GQA rows not centred": ("(s[i] - mean) / sd", "s[i] / sd"),
+    "GQA every query head uses the first table": (
+        "qc_re + (size_t)g * half, qc_im + (size_t)g * half,\n                              q_mean_norm + (size_t)g * half, q_mrl + (size_t)g * half",
+        "qc_re, qc_im,\n                              q_mean_norm, q_mrl"),
+    "GQA constant row gives NaN": ("z = flat ? 0.0 : (s[i] - mean) / sd", "z = (s[i] - mean) / sd"),
+    "GQA statistics include non-finite scores": (
+        "if (isfinite(s[i])) { sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }",
+        "{ sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }"),
 }
 
 
@@ -66,6 +78,16 @@ def _pin_calls():
         calls.append((pins.test_golden_select_examples, {"i": i}))
     for seed in range(12):
         calls.append((pins.test_select_equals_bruteforce_subset_search, {"seed": seed}))
+    for i in range(len(gqa_pins._golden()["examples"])):
+        calls.append((gqa_pins.test_gqa_golden_examples, {"i": i}))
+    calls += [
+        (gqa_pins.test_gqa_z_rows_have_zero_mean_and_unit_population_variance, {}),
+        (gqa_pins.test_gqa_score_is_free_of_each_query_heads_scale, {}),
+        (gqa_pins.test_gqa_single_query_head_keeps_the_plain_top_b, {}),
+        (gqa_pins.test_gqa_equal_scores_give_zero, {}),
+        (gqa_pins.test_gqa_nonfinite_key_is_left_out_of_the_statistics, {}),
+        (gqa_pins.test_gqa_max_over_the_group_of_separately_normalized_heads, {}),
+    ]
     return calls
 
 
