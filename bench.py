@@ -159,6 +159,40 @@ def summarize_pmc(directory: str):
     print(json.dumps(out))
 
 
+def bench_calib_stats(args, torch, synth, tri, dev):
+    """One JSON line for tri_calibrate_stats on Qwen3-8B-shaped query samples:
+    36 layers x 32 query heads = 1152 heads, head_dim 128, bf16."""
+    H, d, n = 36 * 32, 128, args.calib_stats
+    print("bench: generating %d query samples of %d heads" % (n, H), file=sys.stderr, flush=True)
+    q, _, _ = synth.query_samples(H, d, n, seed=args.seed, dtype="bf16", device=dev)
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        tri.tri_calibrate_stats(q)
+    times = []
+    for _ in range(args.steps):
+        flush.sum(dtype=torch.int64)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        tri.tri_calibrate_stats(q, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sum(times) / len(times)
+    nbytes = q.numel() * q.element_size()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "calibration statistics from pre-RoPE query samples (samples per second)",
+        "value": n / (ms * 1e-3), "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-8B query heads: 36 layers x 32 heads x head_dim 128",
+                   "samples": n, "heads": H, "head_dim": d},
+        "roofline": {"bound": "hbm", "kernel": "calib_stats_kernel", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "alg_bytes_per_launch": nbytes, "launch_ms": ms}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +204,9 @@ def main():
                     help="heads of the cache the oracle baseline prunes (0 = skip)")
     ap.add_argument("--pmc-steps", type=int, default=0)
     ap.add_argument("--summarize-pmc", default=None)
+    ap.add_argument("--calib-stats", type=int, default=0, metavar="N_SAMPLES",
+                    help="measure tri_calibrate_stats instead: N_SAMPLES pre-RoPE query samples of "
+                         "the Qwen3-8B query heads (36 layers x 32 heads x head_dim 128, bf16)")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -189,6 +226,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.calib_stats:
+        bench_calib_stats(args, torch, synth, tri, dev)
+        return
     spec = synth.workload(args.workload, seed=args.seed)
     print("bench: generating %s" % describe(spec), file=sys.stderr, flush=True)
     cache = synth.make_cache(spec, dev, seed=args.seed)

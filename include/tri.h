@@ -103,6 +103,33 @@ typedef struct {
  */
 tri_status tri_calibrate_load(const tri_calib_desc* desc, int device, tri_ctx** out);
 
+/*
+ * Calibration statistics of query heads from pre-RoPE query samples, on the
+ * device: for every head h and band f, over the n_samples samples,
+ *   E[q_f]  = mean of  q[f] + i*q[f + d/2]
+ *   E|q_f|  = mean of |q[f] + i*q[f + d/2]|
+ *   R_f     = |E[q_f]| / E|q_f|   (0 when E|q_f| = 0),
+ * accumulated in fp64 in a fixed order (two runs give identical bits).  The
+ * outputs are the tables tri_calib_desc takes; copy them to the host to load
+ * a context.  One workgroup per head reads that head's samples once.
+ *   q       device [n_samples][n_heads][head_dim] (dtype), 16-byte aligned;
+ *           n_heads counts the query heads of every layer (n_layers * n_q_heads)
+ *   qc_re, qc_im, q_mean_norm, q_mrl  device fp64 [n_heads][head_dim/2] outputs,
+ *           8-byte aligned, caller-owned
+ * Enqueued on `stream` (NULL: the null stream), no synchronisation; uses the
+ * device current on the calling thread.
+ * Errors: TRI_E_INVAL (NULL or misaligned pointer, n_samples < 1, n_heads < 1),
+ * TRI_E_UNSUPPORTED (head_dim or dtype), TRI_E_HIP.
+ * Source: romaanj.github.io review, section "Method" (per band: pre-RoPE query
+ * centre, mean norm, mean resultant length, from an offline calibration
+ * pass); dimensionstp.github.io review, section 3 (the calibration phase;
+ * concentration measured as MRL).  Reading: R_f = |E[q_f]| / E|q_f|, the
+ * resultant length of the mean band vector relative to the mean length.
+ */
+tri_status tri_calibrate_stats(tri_dtype dtype, const void* q, int64_t n_samples, int32_t n_heads,
+                               int32_t head_dim, double* qc_re, double* qc_im,
+                               double* q_mean_norm, double* q_mrl, void* stream);
+
 /* Frees a context (NULL is allowed).  Work enqueued with it must be complete. */
 void tri_ctx_destroy(tri_ctx* ctx);
 

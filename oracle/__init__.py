@@ -87,6 +87,8 @@ class Oracle:
         lib.tri_oracle_gqa_head.argtypes = [
             ctypes.c_int, ctypes.c_int, _dp, _i64p, ctypes.c_int64, _dp, _i64p,
             ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.tri_oracle_calib_stats.restype = ctypes.c_int
+        lib.tri_oracle_calib_stats.argtypes = [ctypes.c_int, ctypes.c_long, _dp, _dp, _dp, _dp, _dp]
         lib.tri_oracle_gather_rows.restype = None
         lib.tri_oracle_gather_rows.argtypes = [
             ctypes.c_int, _i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
@@ -175,6 +177,17 @@ class Oracle:
         if r != 0:
             raise ValueError("bad arguments to the oracle's GQA score")
         return raw, z, score
+
+    def calib_stats(self, Q):
+        """(qc_re, qc_im, q_mean_norm, q_mrl), each fp64 [d/2], of one query
+        head from pre-RoPE query samples Q [n][d]."""
+        Q = _f64(Q)
+        n, d = Q.shape
+        out = [np.empty(d // 2) for _ in range(4)]
+        r = self.lib.tri_oracle_calib_stats(d, n, _ptr(Q, _dp), *(_ptr(o, _dp) for o in out))
+        if r != 0:
+            raise ValueError("bad arguments to the oracle's calibration statistics")
+        return tuple(out)
 
     def select_head(self, score, pos, budget: int, window: int):
         """Kept slots (ascending) of one head, or None when the head does not fire."""

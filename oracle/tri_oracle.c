@@ -171,6 +171,45 @@ void tri_oracle_bound_head(int d, int n, const double* K, const double* omega,
     free(coef);
 }
 
+/* ---- calibration statistics from query samples --------------------------- */
+
+/*
+ * Per-band calibration statistics of one query head from n pre-RoPE query
+ * samples Q [n][d] [R1 Method: the offline pass estimates, per frequency
+ * band, the pre-RoPE query centre E[q_f], the mean norm and the mean
+ * resultant length R_f; R2 section 3 (the calibration phase computes head-
+ * and band-wise centre, expected norm and concentration, measured as MRL)]:
+ *   qc_f  = mean over samples of q_f = Q[t][f] + i*Q[t][f+d/2]
+ *   m_f   = mean over samples of |q_f|
+ *   R_f   = |qc_f| / m_f   (0 when m_f = 0)
+ * Reading: R_f is the resultant length of the mean band vector relative to
+ * the mean length (the mean resultant length of the band's phases, weighted
+ * by magnitude); with samples of equal magnitude it is the plain mean
+ * resultant length of the phases.  Returns 0, or -1 on bad arguments.
+ */
+int tri_oracle_calib_stats(int d, long n, const double* Q, double* qc_re, double* qc_im,
+                           double* mean_norm, double* mrl)
+{
+    if (d < 2 || n < 1) return -1;
+    const int half = d / 2;
+    for (int f = 0; f < half; ++f) {
+        double complex sum = 0.0;
+        double norm_sum = 0.0;
+        for (long t = 0; t < n; ++t) {
+            const double complex q = Q[(size_t)t * d + f] + I * Q[(size_t)t * d + f + half];
+            sum += q;
+            norm_sum += cabs(q);
+        }
+        const double complex centre = sum / (double)n;
+        const double m = norm_sum / (double)n;
+        qc_re[f] = creal(centre);
+        qc_im[f] = cimag(centre);
+        mean_norm[f] = m;
+        mrl[f] = m > 0.0 ? cabs(centre) / m : 0.0;
+    }
+    return 0;
+}
+
 /* ---- GQA: normalize, then aggregate ------------------------------------ */
 
 /*

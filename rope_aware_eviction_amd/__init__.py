@@ -32,7 +32,7 @@ TRI_F32, TRI_BF16 = 0, 1
 
 EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last_hip_error",
             "tri_scores_count", "tri_score", "tri_score_workspace_bytes", "tri_score_ws",
-            "tri_select_topb", "tri_compact_kv")
+            "tri_select_topb", "tri_compact_kv", "tri_calibrate_stats")
 
 
 class TriError(RuntimeError):
@@ -90,6 +90,9 @@ def library() -> ctypes.CDLL:
         lib.tri_score_ws.restype = ctypes.c_int
         lib.tri_score_ws.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq), ctypes.c_int32, vp, vp,
                                      ctypes.c_int64, vp]
+        lib.tri_calibrate_stats.restype = ctypes.c_int
+        lib.tri_calibrate_stats.argtypes = [ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_int32, vp, vp, vp, vp, vp]
         lib.tri_select_topb.restype = ctypes.c_int
         lib.tri_select_topb.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
                                         ctypes.c_int32, ctypes.c_int32, vp, vp]
@@ -185,6 +188,21 @@ def tri_calibrate_load(n_layers: int, n_kv_heads: int, head_dim: int, qc_re, qc_
     _check(lib.tri_calibrate_load(ctypes.byref(desc), int(device), ctypes.byref(h)),
            "tri_calibrate_load")
     return Context(h.value, n_layers, n_kv_heads, head_dim, int(device), n_q // n_kv_heads)
+
+
+def tri_calibrate_stats(q: torch.Tensor, stream=None):
+    """Per-band calibration statistics (qc_re, qc_im, q_mean_norm, q_mrl), each
+    an fp64 GPU tensor [n_heads][head_dim/2], from pre-RoPE query samples
+    ``q`` [n_samples][n_heads][head_dim] (float32 or bfloat16, contiguous, on
+    the GPU).  Enqueued on ``stream``; no synchronisation."""
+    if not (q.is_cuda and q.is_contiguous() and q.dim() == 3):
+        raise ValueError("q must be a contiguous 3-d GPU tensor [n_samples][n_heads][head_dim]")
+    n, h, d = q.shape
+    outs = [torch.empty((h, d // 2), dtype=torch.float64, device=q.device) for _ in range(4)]
+    _check(library().tri_calibrate_stats(_dtype_code(q), q.data_ptr(), int(n), int(h), int(d),
+                                         *(o.data_ptr() for o in outs), _stream_ptr(stream)),
+           "tri_calibrate_stats")
+    return tuple(outs)
 
 
 def _dtype_code(t: torch.Tensor) -> int:

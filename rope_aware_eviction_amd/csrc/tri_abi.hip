@@ -197,6 +197,19 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
     return TRI_OK;
 }
 
+tri_status tri_calibrate_stats(tri_dtype dtype, const void* q, int64_t n_samples, int32_t n_heads,
+                               int32_t head_dim, double* qc_re, double* qc_im,
+                               double* q_mean_norm, double* q_mrl, void* stream)
+{
+    if (!q || !aligned16(q) || n_samples < 1 || n_heads < 1) return TRI_E_INVAL;
+    for (const double* p : {qc_re, qc_im, q_mean_norm, q_mrl})
+        if (!p || ((uintptr_t)p & 7u)) return TRI_E_INVAL;
+    if (!supported(head_dim, dtype)) return TRI_E_UNSUPPORTED;
+    hipError_t e = tri::launch_calib_stats(dtype, head_dim, q, n_samples, n_heads, qc_re, qc_im,
+                                           q_mean_norm, q_mrl, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e);
+}
+
 int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
 {
     if (!ctx || n_seq < 0 || (n_seq > 0 && !seqs)) return -1;

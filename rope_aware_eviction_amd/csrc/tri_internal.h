@@ -32,6 +32,12 @@ hipError_t launch_calibrate(int n_heads, int head_dim, double rope_theta, const 
                             const double* qc_im, const double* q_mean_norm, const double* q_mrl,
                             double* omega, double2* qa, float* w, hipStream_t stream);
 
+// Per-band calibration statistics of n_heads query heads from samples
+// [n_samples][n_heads][head_dim].
+hipError_t launch_calib_stats(tri_dtype dtype, int head_dim, const void* q, int64_t n_samples,
+                              int n_heads, double* qc_re, double* qc_im, double* mean_norm,
+                              double* mrl, hipStream_t stream);
+
 // Scores rows [0, len) of n_heads heads of one sequence.
 hipError_t launch_score(tri_dtype dtype, int head_dim, const void* k, int64_t cap, int len,
                         int n_heads, int64_t p_now, const double* omega, const double2* qa,

@@ -343,6 +343,34 @@ def _near_ties(gen, K: torch.Tensor, frac: float) -> torch.Tensor:
     return K
 
 
+def query_samples(n_heads: int, head_dim: int, n_samples: int, seed: int = 0, dtype: str = "bf16",
+                  device="cpu", r_range=(0.3, 0.99), constant_norm: bool = False):
+    """Pre-RoPE query samples for the calibration statistics.
+
+    Returns (q [n_samples][n_heads][head_dim] in ``dtype`` on ``device``,
+    R_true [n_heads][d/2] fp64, centres [n_heads][d] fp64).  Band f of head h
+    has phase arg(c_f) + N(0, sigma^2) with sigma^2 = -2 ln R_true[h, f], so
+    that E[e^{i phase}] has modulus R_true (wrapped-normal law), and
+    magnitude |c_f| (``constant_norm``) or |c_f| * e^{0.2 N(0, 1)}.  Centres
+    are N(0, I_d) scaled to norm 4 as for the caches; R_true ~ U(r_range).
+    Phases and magnitudes are drawn with torch on ``device`` in fp32.
+    """
+    h = head_dim // 2
+    rng = _np_rng(seed, "query-samples", n_heads, head_dim)
+    centres = np.stack([_unit_norm_scaled(rng, head_dim, 4.0) for _ in range(n_heads)])
+    R_true = rng.uniform(r_range[0], r_range[1], size=(n_heads, h))
+    zc = centres[:, :h] + 1j * centres[:, h:]
+    sigma = torch.tensor(np.sqrt(-2.0 * np.log(R_true)), dtype=torch.float32, device=device)
+    mu = torch.tensor(np.angle(zc), dtype=torch.float32, device=device)
+    mag = torch.tensor(np.abs(zc), dtype=torch.float32, device=device)
+    gen = _torch_gen(device, seed, "query-samples", n_heads, head_dim, n_samples)
+    theta = mu + sigma * torch.randn((n_samples, n_heads, h), generator=gen, device=device)
+    r = mag if constant_norm else mag * torch.exp(0.2 * torch.randn((n_samples, n_heads, h),
+                                                                    generator=gen, device=device))
+    q = torch.cat([r * torch.cos(theta), r * torch.sin(theta)], dim=-1)
+    return q.to(_torch_dtype(dtype)).contiguous(), R_true, centres
+
+
 def make_cache(spec: Spec, device="cpu", seed: int = 0,
                positions: Optional[Sequence[np.ndarray]] = None,
                p_now: Optional[Sequence[int]] = None,

@@ -11,6 +11,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_calib as calib_pins
 import test_oracle_gqa as gqa_pins
 import test_oracle_pins as pins
 
@@ -46,6 +47,15 @@ MUTANTS = {
         "qc_re + (size_t)g * half, qc_im + (size_t)g * half,\n                              q_mean_norm + (size_t)g * half, q_mrl + (size_t)g * half",
         "qc_re, qc_im,\n                              q_mean_norm, q_mrl"),
     "GQA constant row gives NaN": ("z = flat ? 0.0 : (s[i] - mean) / sd", "z = (s[i] - mean) / sd"),
+    "calibration R not divided by the mean norm": ("mrl[f] = m > 0.0 ? cabs(centre) / m : 0.0;",
+                                                   "mrl[f] = cabs(centre);"),
+    "calibration interleaved band pairing": (
+        "Q[(size_t)t * d + f] + I * Q[(size_t)t * d + f + half]",
+        "Q[(size_t)t * d + 2 * f] + I * Q[(size_t)t * d + 2 * f + 1]"),
+    "calibration sum instead of mean": ("const double complex centre = sum / (double)n;",
+                                        "const double complex centre = sum;"),
+    "calibration norm of the mean instead of the mean norm": (
+        "const double m = norm_sum / (double)n;", "const double m = cabs(sum) / (double)n;"),
     "GQA statistics include non-finite scores": (
         "if (isfinite(s[i])) { sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }",
         "{ sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }"),
@@ -80,6 +90,13 @@ def _pin_calls():
         calls.append((pins.test_select_equals_bruteforce_subset_search, {"seed": seed}))
     for i in range(len(gqa_pins._golden()["examples"])):
         calls.append((gqa_pins.test_gqa_golden_examples, {"i": i}))
+    for i in range(len(calib_pins._golden()["examples"])):
+        calls.append((calib_pins.test_calib_golden_examples, {"i": i}))
+    calls += [
+        (calib_pins.test_calib_equal_and_opposite_samples, {}),
+        (calib_pins.test_calib_recovers_a_known_concentration, {}),
+        (calib_pins.test_calib_scale_and_rotation, {}),
+    ]
     calls += [
         (gqa_pins.test_gqa_z_rows_have_zero_mean_and_unit_population_variance, {}),
         (gqa_pins.test_gqa_score_is_free_of_each_query_heads_scale, {}),
