@@ -193,6 +193,46 @@ def bench_calib_stats(args, torch, synth, tri, dev):
                      "traffic": None, "alg_bytes_per_launch": nbytes, "launch_ms": ms}}), flush=True)
 
 
+def bench_distance_curve(args, torch, synth, tri, dev):
+    """One JSON line for tri_distance_curve: 1152 query heads of the qwen3_32k_gqa
+    calibration, N_DELTA distances 0..N_DELTA-1 (fp64; bound by fp64 sincos)."""
+    spec = synth.workload("qwen3_32k_gqa")
+    cal = synth._model(spec, args.seed)[2]
+    ctx = tri.tri_calibrate_load(spec.n_layers, spec.n_kv_heads, spec.head_dim, cal.qc_re, cal.qc_im,
+                                 cal.q_mean_norm, cal.q_mrl, cal.offsets, rope_theta=cal.rope_theta,
+                                 device=0, n_q_heads=spec.n_q_heads)
+    h = spec.head_dim // 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    kc_re = torch.randn((spec.heads, h), dtype=torch.float64, device=dev, generator=g)
+    kc_im = torch.randn((spec.heads, h), dtype=torch.float64, device=dev, generator=g)
+    deltas = torch.arange(args.distance_curve, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        tri.tri_distance_curve(ctx, kc_re, kc_im, deltas)
+    times = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        tri.tri_distance_curve(ctx, kc_re, kc_im, deltas, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sum(times) / len(times)
+    entries = spec.heads * spec.group * args.distance_curve
+    terms = entries * h
+    print(json.dumps({
+        "metric": "distance-preference curve entries per second",
+        "value": entries / (ms * 1e-3), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_32k_gqa query heads: 36 x 8 x 4, head_dim 128",
+                   "query_heads": spec.heads * spec.group, "deltas": args.distance_curve},
+        "roofline": {"bound": "alu", "kernel": "distance_curve_kernel",
+                     "achieved": terms / (ms * 1e-3) / 1e9, "unit": "G band terms/s",
+                     "peak": None, "frac": None, "traffic": None}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +247,9 @@ def main():
     ap.add_argument("--calib-stats", type=int, default=0, metavar="N_SAMPLES",
                     help="measure tri_calibrate_stats instead: N_SAMPLES pre-RoPE query samples of "
                          "the Qwen3-8B query heads (36 layers x 32 heads x head_dim 128, bf16)")
+    ap.add_argument("--distance-curve", type=int, default=0, metavar="N_DELTA",
+                    help="measure tri_distance_curve instead: the curves of the 1152 Qwen3-8B "
+                         "query heads (36 layers x 8 KV heads x 4) at N_DELTA distances")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -228,6 +271,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.calib_stats:
         bench_calib_stats(args, torch, synth, tri, dev)
+        return
+    if args.distance_curve:
+        bench_distance_curve(args, torch, synth, tri, dev)
         return
     spec = synth.workload(args.workload, seed=args.seed)
     print("bench: generating %s" % describe(spec), file=sys.stderr, flush=True)

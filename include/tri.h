@@ -130,6 +130,44 @@ tri_status tri_calibrate_stats(tri_dtype dtype, const void* q, int64_t n_samples
                                int32_t head_dim, double* qc_re, double* qc_im,
                                double* q_mean_norm, double* q_mrl, void* stream);
 
+/*
+ * Distance-preference curves: for every query head of the context (all
+ * layers; the G query heads of a KV head in GQA contexts) and every distance
+ * delta_j,
+ *   curve[qh][j] = sum_f Re( E[q_f] * conj(kc_f) * exp(i*w_f*delta_j) ),
+ * the RoPE logit of a query at the query head's calibrated centre E[q_f] and
+ * a key at its KV head's pre-RoPE key centre kc_f, delta_j positions earlier
+ * (delta may be negative).  Computed in fp64, one thread per entry.
+ *   kc_re, kc_im  device fp64 [n_layers*n_kv_heads][head_dim/2] key centres
+ *                 (e.g. tri_calibrate_stats of pre-RoPE key samples)
+ *   deltas        device int64 [n_delta], |delta| <= 2^40
+ *   curve         device fp64 [n_layers*n_q_heads][n_delta] output
+ * Enqueued on `stream`, no synchronisation.  Errors: TRI_E_INVAL, TRI_E_HIP.
+ * Source: dimensionstp.github.io review, section 2-1 item 2 (Q/K centres
+ * give a distance preference curve), section 2-2 (the RoPE logit as a
+ * per-band cosine series of the distance), section 6 item 2 (per-head
+ * curves show local, sink-like or retrieval-like heads).
+ */
+tri_status tri_distance_curve(const tri_ctx* ctx, const double* kc_re, const double* kc_im,
+                              const int64_t* deltas, int32_t n_delta, double* curve, void* stream);
+
+/*
+ * Future-offset sets for tri_calib_desc.offsets (host only, no GPU):
+ *   kind 0, geometric: 1, 2, 4, ... up to max_distance (the pages' default is
+ *           {1, 2, ..., 2^16}: max_distance 65536);
+ *   kind 1, linear: round(max_distance * k / count) for k = 1..count (halves
+ *           round up), at least 1.
+ * Writes min(cap, size) offsets to out (host) and returns the set's size,
+ * or -1 on bad arguments (max_distance outside [1, 2^40], count outside
+ * [1, 2^20] for kind 1, unknown kind, out NULL with cap > 0).
+ * Source: romaanj.github.io review, section "Method" (geometric offsets);
+ * dimensionstp.github.io review, section 4-3 "Future offset design" (the
+ * maximum distance and the spacing change the result; geometric spacing is
+ * reported better than linear).
+ */
+int32_t tri_offset_set(int32_t kind, int64_t max_distance, int32_t count, int64_t* out,
+                       int32_t cap);
+
 /* Frees a context (NULL is allowed).  Work enqueued with it must be complete. */
 void tri_ctx_destroy(tri_ctx* ctx);
 

@@ -89,6 +89,12 @@ class Oracle:
             ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.tri_oracle_calib_stats.restype = ctypes.c_int
         lib.tri_oracle_calib_stats.argtypes = [ctypes.c_int, ctypes.c_long, _dp, _dp, _dp, _dp, _dp]
+        lib.tri_oracle_distance_curve.restype = ctypes.c_int
+        lib.tri_oracle_distance_curve.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _i64p,
+                                                  ctypes.c_int, _dp]
+        lib.tri_oracle_offset_set.restype = ctypes.c_int
+        lib.tri_oracle_offset_set.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, _i64p,
+                                              ctypes.c_int]
         lib.tri_oracle_gather_rows.restype = None
         lib.tri_oracle_gather_rows.argtypes = [
             ctypes.c_int, _i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
@@ -177,6 +183,32 @@ class Oracle:
         if r != 0:
             raise ValueError("bad arguments to the oracle's GQA score")
         return raw, z, score
+
+    def distance_curve(self, om, qc_re, qc_im, kc_re, kc_im, deltas):
+        """Distance-preference curve sum_f Re(qc_f conj(kc_f) e^{i w_f delta}) of one head."""
+        om = _f64(om)
+        qc_re, qc_im, kc_re, kc_im = (_f64(x) for x in (qc_re, qc_im, kc_re, kc_im))
+        deltas = _i64(deltas)
+        out = np.empty(len(deltas))
+        r = self.lib.tri_oracle_distance_curve(2 * len(om), _ptr(om, _dp), _ptr(qc_re, _dp),
+                                               _ptr(qc_im, _dp), _ptr(kc_re, _dp),
+                                               _ptr(kc_im, _dp), _ptr(deltas, _i64p), len(deltas),
+                                               _ptr(out, _dp))
+        if r != 0:
+            raise ValueError("bad arguments to the oracle's distance curve")
+        return out
+
+    def offset_set(self, kind: str, max_distance: int, count: int = 0) -> np.ndarray:
+        """Future-offset set: 'geometric' (powers of two up to max_distance) or
+        'linear' (count evenly spaced offsets ending at max_distance)."""
+        k = {"geometric": 0, "linear": 1}[kind]
+        n = self.lib.tri_oracle_offset_set(k, int(max_distance), int(count),
+                                           _ptr(np.empty(1, dtype=np.int64), _i64p), 0)
+        if n < 0:
+            raise ValueError("bad offset-set arguments")
+        out = np.empty(max(n, 1), dtype=np.int64)
+        self.lib.tri_oracle_offset_set(k, int(max_distance), int(count), _ptr(out, _i64p), n)
+        return out[:n].copy()
 
     def calib_stats(self, Q):
         """(qc_re, qc_im, q_mean_norm, q_mrl), each fp64 [d/2], of one query

@@ -171,6 +171,70 @@ void tri_oracle_bound_head(int d, int n, const double* K, const double* omega,
     free(coef);
 }
 
+/* ---- distance-preference curve and offset sets -------------------------- */
+
+/*
+ * Distance-preference curve of one head [R2 section 2-1 item 2 (Q/K centres
+ * give a distance preference curve), section 2-2 (the RoPE logit as a
+ * per-band cosine series of the query-key distance), section 6 item 2 (the
+ * per-head curve as an analysis tool)]: with the pre-RoPE query centre
+ * qc_f and key centre kc_f of every band,
+ *   curve[j] = sum_f Re( qc_f * conj(kc_f) * exp(i*w_f*deltas[j]) ),
+ * the logit of a query at the centre and a key at the centre deltas[j]
+ * positions before it.  Returns 0, or -1 on bad arguments.
+ */
+int tri_oracle_distance_curve(int d, const double* omega, const double* qc_re,
+                              const double* qc_im, const double* kc_re, const double* kc_im,
+                              const int64_t* deltas, int n_delta, double* curve)
+{
+    if (d < 2 || n_delta < 0) return -1;
+    const int half = d / 2;
+    for (int j = 0; j < n_delta; ++j) {
+        double s = 0.0;
+        for (int f = 0; f < half; ++f) {
+            const double complex q = qc_re[f] + I * qc_im[f];
+            const double complex k = kc_re[f] + I * kc_im[f];
+            s += creal(q * conj(k) * cexp(I * omega[f] * (double)deltas[j]));
+        }
+        curve[j] = s;
+    }
+    return 0;
+}
+
+/*
+ * Future-offset sets [R1 Method (geometric offsets {1, 2, 4, ..., 2^16});
+ * R2 section 4-3 "Future offset design" (the maximum distance and the
+ * spacing change the result, geometric spacing beats linear)].
+ *   kind 0, geometric: 1, 2, 4, ... up to max_distance (powers of two)
+ *   kind 1, linear:    max_distance * k / count for k = 1..count (rounded
+ *                      to the nearest integer, at least 1)
+ * Writes at most `cap` offsets and returns how many the set has, or -1 on
+ * bad arguments.
+ */
+int tri_oracle_offset_set(int kind, int64_t max_distance, int count, int64_t* out, int cap)
+{
+    if (max_distance < 1) return -1;
+    int n = 0;
+    if (kind == 0) {
+        for (int64_t x = 1; x <= max_distance; x *= 2) {
+            if (n < cap) out[n] = x;
+            ++n;
+        }
+        return n;
+    }
+    if (kind == 1) {
+        if (count < 1) return -1;
+        for (int k = 1; k <= count; ++k) {
+            int64_t x = (int64_t)floor((double)max_distance * (double)k / (double)count + 0.5);
+            if (x < 1) x = 1;
+            if (n < cap) out[n] = x;
+            ++n;
+        }
+        return n;
+    }
+    return -1;
+}
+
 /* ---- calibration statistics from query samples --------------------------- */
 
 /*

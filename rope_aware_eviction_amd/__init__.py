@@ -32,7 +32,8 @@ TRI_F32, TRI_BF16 = 0, 1
 
 EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last_hip_error",
             "tri_scores_count", "tri_score", "tri_score_workspace_bytes", "tri_score_ws",
-            "tri_select_topb", "tri_compact_kv", "tri_calibrate_stats")
+            "tri_select_topb", "tri_compact_kv", "tri_calibrate_stats", "tri_distance_curve",
+            "tri_offset_set")
 
 
 class TriError(RuntimeError):
@@ -93,6 +94,11 @@ def library() -> ctypes.CDLL:
         lib.tri_calibrate_stats.restype = ctypes.c_int
         lib.tri_calibrate_stats.argtypes = [ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_int32, vp, vp, vp, vp, vp]
+        lib.tri_distance_curve.restype = ctypes.c_int
+        lib.tri_distance_curve.argtypes = [vp, vp, vp, vp, ctypes.c_int32, vp, vp]
+        lib.tri_offset_set.restype = ctypes.c_int32
+        lib.tri_offset_set.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
         lib.tri_select_topb.restype = ctypes.c_int
         lib.tri_select_topb.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
                                         ctypes.c_int32, ctypes.c_int32, vp, vp]
@@ -203,6 +209,39 @@ def tri_calibrate_stats(q: torch.Tensor, stream=None):
                                          *(o.data_ptr() for o in outs), _stream_ptr(stream)),
            "tri_calibrate_stats")
     return tuple(outs)
+
+
+def tri_distance_curve(ctx: Context, kc_re: torch.Tensor, kc_im: torch.Tensor,
+                       deltas: torch.Tensor, stream=None) -> torch.Tensor:
+    """Distance-preference curves [n_layers*n_q_heads][n_delta] (fp64 GPU tensor)
+    from the context's query centres and key centres kc_re/kc_im (fp64 GPU
+    [n_layers*n_kv_heads][head_dim/2]) at distances ``deltas`` (int64 GPU)."""
+    h = ctx.n_heads
+    for t in (kc_re, kc_im):
+        if t.dtype != torch.float64 or not t.is_cuda or not t.is_contiguous() \
+                or tuple(t.shape) != (h, ctx.head_dim // 2):
+            raise ValueError("key centres must be contiguous fp64 GPU tensors [%d][%d]"
+                             % (h, ctx.head_dim // 2))
+    if deltas.dtype != torch.int64 or not deltas.is_cuda or not deltas.is_contiguous():
+        raise ValueError("deltas must be a contiguous int64 GPU tensor")
+    out = torch.empty((h * ctx.group, deltas.numel()), dtype=torch.float64, device=kc_re.device)
+    _check(library().tri_distance_curve(ctx.handle, kc_re.data_ptr(), kc_im.data_ptr(),
+                                        deltas.data_ptr(), int(deltas.numel()), out.data_ptr(),
+                                        _stream_ptr(stream)), "tri_distance_curve")
+    return out
+
+
+def offset_set(kind: str, max_distance: int, count: int = 0) -> np.ndarray:
+    """Future-offset set: 'geometric' (1, 2, 4, ... up to max_distance) or
+    'linear' (count evenly spaced offsets ending at max_distance)."""
+    k = {"geometric": 0, "linear": 1}[kind]
+    n = library().tri_offset_set(k, int(max_distance), int(count), None, 0)
+    if n < 0:
+        raise ValueError("bad offset-set arguments")
+    out = np.empty(n, dtype=np.int64)
+    library().tri_offset_set(k, int(max_distance), int(count),
+                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n)
+    return out
 
 
 def _dtype_code(t: torch.Tensor) -> int:

@@ -47,7 +47,55 @@ __global__ void calibrate_kernel(int n_heads, int head_dim, double rope_theta,
     w[i] = (float)((1.0 - q_mrl[i]) * q_mean_norm[i]);
 }
 
+// One thread per (query head, distance): the distance-preference curve
+// sum_f Re(E[q_f] * conj(kc_f) * exp(i*w_f*delta)) in fp64.
+// Source: dimensionstp.github.io "TriAttention ... Review", section 2-1
+// item 2 and section 2-2 (Q/K centres turn the RoPE logit into a curve of
+// the query-key distance), section 6 item 2 (per-head curves).
+__global__ void distance_curve_kernel(int n_q_heads, int group, int half,
+                                      const double* __restrict__ omega,
+                                      const double2* __restrict__ qc,
+                                      const double* __restrict__ kc_re,
+                                      const double* __restrict__ kc_im,
+                                      const int64_t* __restrict__ deltas, int n_delta,
+                                      double* __restrict__ curve)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)n_q_heads * n_delta) return;
+    const int qh = (int)(i / n_delta);
+    const int j = (int)(i - (int64_t)qh * n_delta);
+    const int kv = qh / group;
+    const double dl = (double)deltas[j];
+    double s = 0.0;
+    for (int f = 0; f < half; ++f) {
+        const double2 q = qc[(size_t)qh * half + f];
+        const double kr = kc_re[(size_t)kv * half + f], ki = kc_im[(size_t)kv * half + f];
+        // q * conj(k) = (q.x*kr + q.y*ki) + i*(q.y*kr - q.x*ki)
+        const double pr = q.x * kr + q.y * ki, pi = q.y * kr - q.x * ki;
+        double sn, cs;
+        sincos(omega[f] * dl, &sn, &cs);
+        s += pr * cs - pi * sn;
+    }
+    curve[i] = s;
+}
+
 }  // namespace
+
+hipError_t launch_distance_curve(int n_q_heads, int group, int head_dim, const double* omega,
+                                 const double2* qc, const double* kc_re, const double* kc_im,
+                                 const int64_t* deltas, int n_delta, double* curve,
+                                 hipStream_t stream)
+{
+    const int64_t total = (int64_t)n_q_heads * n_delta;
+    if (total <= 0) return hipSuccess;
+    const int block = 256;
+    const int64_t grid = (total + block - 1) / block;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(distance_curve_kernel, dim3((unsigned)grid), dim3(block), 0, stream,
+                       n_q_heads, group, head_dim / 2, omega, qc, kc_re, kc_im, deltas, n_delta,
+                       curve);
+    return hipGetLastError();
+}
 
 hipError_t launch_calibrate(int n_heads, int head_dim, double rope_theta, const double* inv_freq,
                             const int64_t* offsets, int n_offsets, const double* qc_re,

@@ -86,6 +86,7 @@ void tri_ctx_destroy(tri_ctx* ctx)
         (void)hipFree(ctx->omega);
         (void)hipFree(ctx->qa);
         (void)hipFree(ctx->w);
+        (void)hipFree(ctx->qc);
     }
     if (have_prev) (void)hipSetDevice(prev);
     delete ctx;
@@ -160,6 +161,7 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
     alloc((void**)&ctx->omega, sizeof(double) * half);
     alloc((void**)&ctx->qa, sizeof(double2) * nb);
     alloc((void**)&ctx->w, sizeof(float) * nb);
+    alloc((void**)&ctx->qc, sizeof(double2) * nb);
     if (d->inv_freq) alloc((void**)&r_inv, sizeof(double) * half);
     alloc((void**)&r_off, sizeof(int64_t) * d->n_offsets);
     alloc((void**)&r_re, sizeof(double) * nb);
@@ -172,6 +174,14 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
     put(r_im, d->qc_im, sizeof(double) * nb);
     put(r_m, d->q_mean_norm, sizeof(double) * nb);
     put(r_R, d->q_mrl, sizeof(double) * nb);
+    if (st == TRI_OK) {   // the query centres as loaded, interleaved (re, im)
+        std::vector<double> qc(2 * nb);
+        for (size_t i = 0; i < nb; ++i) {
+            qc[2 * i] = d->qc_re[i];
+            qc[2 * i + 1] = d->qc_im[i];
+        }
+        put(ctx->qc, qc.data(), sizeof(double2) * nb);
+    }
     if (st == TRI_OK) {
         e = tri::launch_calibrate(n_heads * group, d->head_dim, d->rope_theta, r_inv, r_off, d->n_offsets,
                                   r_re, r_im, r_m, r_R, ctx->omega, ctx->qa, ctx->w, nullptr);
@@ -188,6 +198,7 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
         (void)hipFree(ctx->omega);
         (void)hipFree(ctx->qa);
         (void)hipFree(ctx->w);
+        (void)hipFree(ctx->qc);
         delete ctx;
         (void)hipSetDevice(prev);
         return st;
@@ -208,6 +219,47 @@ tri_status tri_calibrate_stats(tri_dtype dtype, const void* q, int64_t n_samples
     hipError_t e = tri::launch_calib_stats(dtype, head_dim, q, n_samples, n_heads, qc_re, qc_im,
                                            q_mean_norm, q_mrl, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TRI_OK : hip_fail(e);
+}
+
+tri_status tri_distance_curve(const tri_ctx* ctx, const double* kc_re, const double* kc_im,
+                              const int64_t* deltas, int32_t n_delta, double* curve, void* stream)
+{
+    if (!ctx || n_delta < 0) return TRI_E_INVAL;
+    if (n_delta == 0) return TRI_OK;
+    for (const void* p : {(const void*)kc_re, (const void*)kc_im, (const void*)deltas, (const void*)curve})
+        if (!p || ((uintptr_t)p & 7u)) return TRI_E_INVAL;
+    tri_status st = check_device(ctx);
+    if (st != TRI_OK) return st;
+    hipError_t e = tri::launch_distance_curve(ctx->n_heads * ctx->group, ctx->group, ctx->head_dim,
+                                              ctx->omega, ctx->qc, kc_re, kc_im, deltas, n_delta,
+                                              curve, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e);
+}
+
+int32_t tri_offset_set(int32_t kind, int64_t max_distance, int32_t count, int64_t* out, int32_t cap)
+{
+    if (max_distance < 1 || max_distance > (int64_t(1) << 40) || cap < 0 || (cap > 0 && !out))
+        return -1;
+    int32_t n = 0;
+    auto emit = [&](int64_t x) {
+        if (n < cap) out[n] = x;
+        ++n;
+    };
+    if (kind == 0) {                     // geometric: powers of two up to max_distance
+        for (int64_t x = 1; x <= max_distance; x <<= 1) emit(x);
+        return n;
+    }
+    if (kind == 1) {                     // linear: count evenly spaced, ending at max_distance
+        if (count < 1 || count > (1 << 20)) return -1;
+        for (int32_t k = 1; k <= count; ++k) {
+            // round(max_distance * k / count) in integers: (2*m*k + count) / (2*count)
+            const __int128 num = (__int128)2 * max_distance * k + count;
+            int64_t x = (int64_t)(num / (2 * (__int128)count));
+            emit(x < 1 ? 1 : x);
+        }
+        return n;
+    }
+    return -1;
 }
 
 int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)

@@ -16,6 +16,7 @@ struct tri_ctx {
     double* omega;        // device [head_dim/2]        band frequencies
     double2* qa;          // device [n_heads][group][head_dim/2] E[q_f] * A_f (complex, fp64)
     float* w;             // device [n_heads][group][head_dim/2] (1 - R_f) * E|q_f|
+    double2* qc;          // device [n_heads][group][head_dim/2] E[q_f] as loaded (complex, fp64)
 };
 
 namespace tri {
@@ -37,6 +38,12 @@ hipError_t launch_calibrate(int n_heads, int head_dim, double rope_theta, const 
 hipError_t launch_calib_stats(tri_dtype dtype, int head_dim, const void* q, int64_t n_samples,
                               int n_heads, double* qc_re, double* qc_im, double* mean_norm,
                               double* mrl, hipStream_t stream);
+
+// Distance-preference curves: one thread per (query head, distance).
+hipError_t launch_distance_curve(int n_q_heads, int group, int head_dim, const double* omega,
+                                 const double2* qc, const double* kc_re, const double* kc_im,
+                                 const int64_t* deltas, int n_delta, double* curve,
+                                 hipStream_t stream);
 
 // Scores rows [0, len) of n_heads heads of one sequence.
 hipError_t launch_score(tri_dtype dtype, int head_dim, const void* k, int64_t cap, int len,

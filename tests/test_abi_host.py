@@ -109,3 +109,18 @@ def test_calls_reject_null_context_and_bad_shapes(lib):
     assert lib.tri_score_ws(None, tri.TRI_BF16, arr, 1, None, None, 0, None) == tri.TRI_E_INVAL
     assert lib.tri_score_workspace_bytes(None, arr, 1) == -1
     lib.tri_ctx_destroy(None)     # allowed
+
+
+def test_offset_sets_match_the_oracle(lib, oracle_lib):
+    """The library's host helper and the oracle's, written separately from the
+    same statement, agree on every set."""
+    rng = __import__("numpy").random.default_rng(40)
+    for m in [1, 2, 3, 100, 1000, 65536, 131071, 1 << 40]:
+        np.testing.assert_array_equal(tri.offset_set("geometric", m), oracle_lib.offset_set("geometric", m))
+    for _ in range(200):
+        m = int(rng.integers(1, 1 << 20))
+        c = int(rng.integers(1, 300))
+        np.testing.assert_array_equal(tri.offset_set("linear", m, c), oracle_lib.offset_set("linear", m, c))
+    assert lib.tri_offset_set(0, 0, 0, None, 0) == -1
+    assert lib.tri_offset_set(1, 10, 0, None, 0) == -1
+    assert lib.tri_offset_set(2, 10, 3, None, 0) == -1

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle_calib as calib_pins
+import test_oracle_curve as curve_pins
 import test_oracle_gqa as gqa_pins
 import test_oracle_pins as pins
 
@@ -56,6 +57,15 @@ MUTANTS = {
                                         "const double complex centre = sum;"),
     "calibration norm of the mean instead of the mean norm": (
         "const double m = norm_sum / (double)n;", "const double m = cabs(sum) / (double)n;"),
+    "curve conjugates the query instead of the key": (
+        "s += creal(q * conj(k) * cexp(I * omega[f] * (double)deltas[j]));",
+        "s += creal(conj(q) * k * cexp(I * omega[f] * (double)deltas[j]));"),
+    "curve ignores the distance": ("s += creal(q * conj(k) * cexp(I * omega[f] * (double)deltas[j]));",
+                                   "s += creal(q * conj(k));"),
+    "linear offsets truncated": ("(double)max_distance * (double)k / (double)count + 0.5)",
+                                 "(double)max_distance * (double)k / (double)count)"),
+    "geometric offsets by four": ("for (int64_t x = 1; x <= max_distance; x *= 2) {",
+                                  "for (int64_t x = 1; x <= max_distance; x *= 4) {"),
     "GQA statistics include non-finite scores": (
         "if (isfinite(s[i])) { sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }",
         "{ sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }"),
@@ -90,6 +100,12 @@ def _pin_calls():
         calls.append((pins.test_select_equals_bruteforce_subset_search, {"seed": seed}))
     for i in range(len(gqa_pins._golden()["examples"])):
         calls.append((gqa_pins.test_gqa_golden_examples, {"i": i}))
+    calls += [
+        (curve_pins.test_curve_is_the_rope_logit_of_the_centres, {}),
+        (curve_pins.test_curve_at_zero_distance_is_the_dot_product_and_hand_example, {}),
+        (curve_pins.test_score_trig_term_of_a_key_at_the_centre_averages_the_curve, {}),
+        (curve_pins.test_offset_sets, {}),
+    ]
     for i in range(len(calib_pins._golden()["examples"])):
         calls.append((calib_pins.test_calib_golden_examples, {"i": i}))
     calls += [
