@@ -95,6 +95,10 @@ class Oracle:
         lib.tri_oracle_offset_set.restype = ctypes.c_int
         lib.tri_oracle_offset_set.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, _i64p,
                                               ctypes.c_int]
+        lib.tri_oracle_select_shared.restype = ctypes.c_int
+        lib.tri_oracle_select_shared.argtypes = [
+            ctypes.c_int, _i32p, ctypes.c_int, _dp, _i64p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, _i32p, _i32p]
         lib.tri_oracle_gather_rows.restype = None
         lib.tri_oracle_gather_rows.argtypes = [
             ctypes.c_int, _i32p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
@@ -234,6 +238,25 @@ class Oracle:
         if r == 0:
             return None
         return kept[:r].copy()
+
+    def select_shared(self, scores, pos, lens, total: int, floor: int, window: int):
+        """Head-specific budgets of one layer: ``scores``/``pos`` [H][stride],
+        ``lens`` [H] keys in use per head.  Returns a list of H ascending kept
+        slot arrays, or None when the layer does not fire."""
+        scores = _f64(np.atleast_2d(scores))
+        pos = _i64(np.atleast_2d(pos))
+        H, stride = scores.shape
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        kept = np.empty(H * total, dtype=np.int32)
+        count = np.empty(H, dtype=np.int32)
+        r = self.lib.tri_oracle_select_shared(H, _ptr(lens, _i32p), stride, _ptr(scores, _dp),
+                                              _ptr(pos, _i64p), int(total), int(floor),
+                                              int(window), _ptr(kept, _i32p), _ptr(count, _i32p))
+        if r < 0:
+            raise ValueError("bad arguments to the oracle's shared select")
+        if r == 0:
+            return None
+        return [kept[h * total:h * total + count[h]].copy() for h in range(H)]
 
     def gather_rows(self, kept, rows: np.ndarray) -> np.ndarray:
         """dst[r] = rows[kept[r]] (bytes copied exactly)."""

@@ -385,6 +385,89 @@ int tri_oracle_select_head(int n, const double* score, const int64_t* pos,
     return budget;
 }
 
+/* ---- head-specific budgets: one shared budget per layer ------------------ */
+
+typedef struct { double s; int32_t head; int64_t p; int32_t slot; int reserved; } ranked_h;
+
+/* Layer order: reserved keys first, then score descending (NaN below every
+ * number), then lower head, lower position, lower slot. */
+static int by_layer_rank(const void* a_, const void* b_)
+{
+    const ranked_h* a = (const ranked_h*)a_;
+    const ranked_h* b = (const ranked_h*)b_;
+    if (a->reserved != b->reserved) return a->reserved ? -1 : 1;
+    int an = isnan(a->s), bn = isnan(b->s);
+    if (an != bn) return an ? 1 : -1;   /* NaN below every number */
+    if (!an) {
+        if (a->s > b->s) return -1;
+        if (a->s < b->s) return 1;
+    }
+    if (a->head != b->head) return a->head < b->head ? -1 : 1;
+    if (a->p != b->p) return (a->p < b->p) ? -1 : 1;   /* then the lower position */
+    return a->slot < b->slot ? -1 : (a->slot > b->slot ? 1 : 0);
+}
+
+/*
+ * Head-specific budgets for the n_head KV heads of one layer [R1 "Future
+ * work": refined compression strategies including head-specific budgets].
+ * Reading: the heads share `total` slots (a per-head budget times the
+ * heads); every head first keeps its `floor` best keys (its own order of
+ * tri_oracle_select_head), and the remaining slots go to the best remaining
+ * keys of the whole layer, one threshold across heads, ties to the lower
+ * head and then the lower position.
+ *   head h has n[h] keys: score[h*stride + i], pos[h*stride + i], i < n[h]
+ *   the layer fires iff sum n[h] > total + n_head * window
+ * When it fires, writes head h's kept slots in ascending order to
+ * kept[h*total + r], r < count[h], and returns total; otherwise returns 0
+ * and writes nothing.  Returns -1 on bad arguments (floor * n_head > total
+ * among them).
+ */
+int tri_oracle_select_shared(int n_head, const int* n, int stride, const double* score,
+                             const int64_t* pos, int total, int floor_, int window,
+                             int32_t* kept, int32_t* count)
+{
+    if (n_head < 1 || total < 1 || floor_ < 0 || window < 0) return -1;
+    if ((int64_t)floor_ * n_head > total) return -1;
+    int64_t all = 0;
+    for (int h = 0; h < n_head; ++h) {
+        if (n[h] < 0 || n[h] > stride) return -1;
+        all += n[h];
+    }
+    if (all <= (int64_t)total + (int64_t)n_head * window) return 0;
+
+    ranked_h* r = (ranked_h*)malloc(sizeof(ranked_h) * (size_t)all);
+    ranked* one = (ranked*)malloc(sizeof(ranked) * (size_t)(stride > 0 ? stride : 1));
+    int64_t m = 0;
+    for (int h = 0; h < n_head; ++h) {
+        /* the head's own order decides which of its keys are reserved */
+        for (int i = 0; i < n[h]; ++i) {
+            one[i].s = score[(size_t)h * stride + i];
+            one[i].p = pos[(size_t)h * stride + i];
+            one[i].slot = i;
+        }
+        qsort(one, (size_t)n[h], sizeof(ranked), by_rank);
+        for (int j = 0; j < n[h]; ++j) {
+            r[m].s = one[j].s;
+            r[m].head = h;
+            r[m].p = one[j].p;
+            r[m].slot = one[j].slot;
+            r[m].reserved = j < floor_;
+            ++m;
+        }
+    }
+    qsort(r, (size_t)all, sizeof(ranked_h), by_layer_rank);
+    for (int h = 0; h < n_head; ++h) count[h] = 0;
+    for (int j = 0; j < total; ++j) {
+        const int h = r[j].head;
+        kept[(size_t)h * total + count[h]++] = r[j].slot;
+    }
+    for (int h = 0; h < n_head; ++h)
+        qsort(kept + (size_t)h * total, (size_t)count[h], sizeof(int32_t), by_int32);
+    free(one);
+    free(r);
+    return total;
+}
+
 /* Gathers rows: dst[r] = src[kept[r]] for r < n_kept (row_bytes each).
  * The eviction keeps exactly the selected rows, in ascending slot order. */
 void tri_oracle_gather_rows(int n_kept, const int32_t* kept, int64_t row_bytes,

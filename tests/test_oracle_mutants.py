@@ -15,6 +15,7 @@ import test_oracle_calib as calib_pins
 import test_oracle_curve as curve_pins
 import test_oracle_gqa as gqa_pins
 import test_oracle_pins as pins
+import test_oracle_shared as shared_pins
 
 MUTANTS = {
     "conjugate on the query": ("q * conj(k[f])", "conj(q) * k[f]"),
@@ -33,9 +34,10 @@ MUTANTS = {
     "ties go to the later position": ("if (a->p != b->p) return a->p < b->p ? -1 : 1;",
                                       "if (a->p != b->p) return a->p < b->p ? 1 : -1;"),
     "ties by slot instead of position": ("if (a->p != b->p) return a->p < b->p ? -1 : 1;", ""),
-    "NaN ranks highest": ("if (an != bn) return an ? 1 : -1;", "if (an != bn) return an ? -1 : 1;"),
-    "keeps the lowest scores": ("if (a->s > b->s) return -1;\n        if (a->s < b->s) return 1;",
-                                "if (a->s > b->s) return 1;\n        if (a->s < b->s) return -1;"),
+    "NaN ranks highest": ("const ranked* b = (const ranked*)b_;\n    int an = isnan(a->s), bn = isnan(b->s);\n    if (an != bn) return an ? 1 : -1;",
+                          "const ranked* b = (const ranked*)b_;\n    int an = isnan(a->s), bn = isnan(b->s);\n    if (an != bn) return an ? -1 : 1;"),
+    "keeps the lowest scores": ("if (an != bn) return an ? 1 : -1;\n    if (!an) {\n        if (a->s > b->s) return -1;\n        if (a->s < b->s) return 1;\n    }\n    if (a->p != b->p)",
+                                "if (an != bn) return an ? 1 : -1;\n    if (!an) {\n        if (a->s > b->s) return 1;\n        if (a->s < b->s) return -1;\n    }\n    if (a->p != b->p)"),
     "fire rule off by one": ("if ((int64_t)n <= (int64_t)budget + (int64_t)window) return 0;",
                              "if ((int64_t)n < (int64_t)budget + (int64_t)window) return 0;"),
     "kept list left in rank order": ("qsort(kept, (size_t)budget, sizeof(int32_t), by_int32);", ""),
@@ -66,6 +68,19 @@ MUTANTS = {
                                  "(double)max_distance * (double)k / (double)count)"),
     "geometric offsets by four": ("for (int64_t x = 1; x <= max_distance; x *= 2) {",
                                   "for (int64_t x = 1; x <= max_distance; x *= 4) {"),
+    "shared budget ranks NaN highest": ("if (an != bn) return an ? 1 : -1;   /* NaN below every number */",
+                                        "if (an != bn) return an ? -1 : 1;"),
+    "shared budget ties to the later position": ("if (a->p != b->p) return (a->p < b->p) ? -1 : 1;",
+                                                 "if (a->p != b->p) return (a->p < b->p) ? 1 : -1;"),
+    "shared budget ignores the floor": ("r[m].reserved = j < floor_;", "r[m].reserved = 0;"),
+    "shared budget ties to the higher head": ("if (a->head != b->head) return a->head < b->head ? -1 : 1;",
+                                              "if (a->head != b->head) return a->head < b->head ? 1 : -1;"),
+    "shared budget reserves the worst keys": ("r[m].reserved = j < floor_;", "r[m].reserved = j >= n[h] - floor_;"),
+    "shared budget fire rule without the window": (
+        "if (all <= (int64_t)total + (int64_t)n_head * window) return 0;",
+        "if (all <= (int64_t)total) return 0;"),
+    "shared budget kept lists unsorted": (
+        "qsort(kept + (size_t)h * total, (size_t)count[h], sizeof(int32_t), by_int32);", ";"),
     "GQA statistics include non-finite scores": (
         "if (isfinite(s[i])) { sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }",
         "{ sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }"),
@@ -106,6 +121,12 @@ def _pin_calls():
         (curve_pins.test_score_trig_term_of_a_key_at_the_centre_averages_the_curve, {}),
         (curve_pins.test_offset_sets, {}),
     ]
+    for i in range(len(shared_pins._golden()["examples"])):
+        calls.append((shared_pins.test_shared_golden_examples, {"i": i}))
+    calls += [(shared_pins.test_floor_equal_to_budget_is_the_per_head_top_b, {}),
+              (shared_pins.test_one_head_is_the_plain_top_b, {})]
+    for seed in range(10):
+        calls.append((shared_pins.test_shared_selection_properties, {"seed": seed}))
     for i in range(len(calib_pins._golden()["examples"])):
         calls.append((calib_pins.test_calib_golden_examples, {"i": i}))
     calls += [
