@@ -34,7 +34,8 @@
  *     enqueued.  The device current on the calling thread must be the
  *     context's device.
  *   - A head fires iff len > budget + window; the calls with a budget skip
- *     sequences that do not fire.
+ *     sequences that do not fire.  With head-specific budgets
+ *     (tri_select_shared) a whole layer fires or not; see there.
  */
 #ifndef TRI_H
 #define TRI_H
@@ -83,11 +84,18 @@ typedef struct tri_ctx tri_ctx;   /* opaque; immutable after tri_calibrate_load 
 /* One sequence's cache.  Device pointers, caller-owned. */
 typedef struct {
     void* k;          /* [n_layers][n_kv_heads][cap][head_dim], 16-byte aligned */
-    void* v;          /* same shape and dtype as k, 16-byte aligned (read by tri_compact_kv only) */
-    int32_t* pos;     /* [n_layers][n_kv_heads][cap] (read and written by tri_compact_kv only) */
+    void* v;          /* same shape and dtype as k, 16-byte aligned (read by the compaction calls only) */
+    int32_t* pos;     /* [n_layers][n_kv_heads][cap] (read and written by the compaction calls only) */
     int32_t cap;      /* rows allocated per head, >= len */
-    int32_t len;      /* rows in use per head; tri_compact_kv sets it to budget when it fires */
+    int32_t len;      /* rows in use per head (with head_len: an upper bound on every head's rows,
+                         and the per-head stride of the score layout); tri_compact_kv sets it to
+                         budget when it fires */
     int64_t p_now;    /* position of the newest cached token; future queries sit at p_now + delta */
+    int32_t* head_len;/* NULL: every head holds len rows.  Otherwise device int32
+                         [n_layers][n_kv_heads], 4-byte aligned: head (l, h) holds rows
+                         [0, min(head_len[l][h], len)) (a ragged cache, as head-specific budgets
+                         leave it).  Read by tri_score / tri_score_ws / tri_select_shared, written
+                         by tri_compact_kv_counts; tri_select_topb and tri_compact_kv need NULL. */
 } tri_seq;
 
 /*
@@ -197,7 +205,9 @@ int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
  *   scores  device fp32, tri_scores_count() slots: the scores of sequence s
  *           start after those of sequences 0..s-1, each sequence laid out
  *           [n_layers][n_kv_heads][len]
- * Reads K rows [0, len) of every head; positions are not read.
+ * Reads K rows [0, len) of every head (with head_len, the head's own rows;
+ * score slots past a head's length are left untouched); positions are not
+ * read.
  * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP.
  * Source: romaanj.github.io review, section "Method" (trig term per band
  * ||E[q_f]||*||k_f||*cos(w_f*distance + phase difference), norm term,
@@ -239,7 +249,7 @@ tri_status tri_score_ws(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs
 /*
  * Selects, for every head of every firing sequence, the `budget` keys with
  * the largest scores; equal scores go to the lower slot; NaN ranks below
- * every number and -0 equals +0.  Writes the kept slots in ascending order
+ * every number and -0 equals +0.  Needs head_len == NULL.  Writes the kept slots in ascending order
  * to kept[s][layer][kv_head][0..budget) (device int32, n_seq * n_layers *
  * n_kv_heads * budget slots; entries of sequences that do not fire are left
  * untouched).
@@ -255,7 +265,8 @@ tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_se
                            int32_t* kept, void* stream);
 
 /*
- * Evicts in place: for every head of every firing sequence, rows r < budget
+ * Evicts in place (head_len must be NULL): for every head of every firing
+ * sequence, rows r < budget
  * of K, V and positions become the rows at kept[r] (stable: the kept rows
  * keep their slot order).  Then sets seqs[s].len = budget for every firing
  * sequence (at enqueue time).  Rows [budget, cap) hold unspecified data
@@ -269,6 +280,66 @@ tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_se
  */
 tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, int32_t n_seq,
                           const int32_t* kept, int32_t budget, int32_t window, void* stream);
+
+/* Device workspace bytes tri_select_shared needs: 16 bytes per layer and KV
+ * head of every sequence plus 16 per layer, rounded up.  -1 on bad arguments. */
+int64_t tri_select_shared_workspace_bytes(const tri_ctx* ctx, int32_t n_seq);
+
+/*
+ * Head-specific budgets: the KV heads of a layer share one budget of
+ * total = budget * n_kv_heads slots instead of holding `budget` each.
+ * Reading: every head first reserves its `floor` best keys (its own order:
+ * higher score, then lower slot; a head with at most `floor` keys reserves
+ * all); the remaining slots go to the best remaining keys of the whole layer
+ * under one threshold, equal scores to the lower head and then the lower
+ * slot.  NaN ranks below every number; -0 equals +0.
+ * A layer fires iff the sum of its heads' lengths exceeds
+ * total + n_kv_heads * window.  For layer l of sequence s:
+ *   kept_count[s][l][h]  number of keys head h keeps, or -1 if the layer
+ *                        does not fire (then its kept rows hold unspecified
+ *                        data: they serve as scratch)
+ *   kept[s][l][h][0..kept_count)  the kept slots, ascending (stride total)
+ * so the sum of the counts of a firing layer is exactly total.
+ *   scores     device fp32, layout of tri_score: [n_layers][n_kv_heads][len]
+ *              per sequence; entries at or past a head's length are not read
+ *   budget     >= 1 (slots per head on average);  window >= 0
+ *   floor      in [0, budget] (keys every head keeps for itself)
+ *   kept       device int32, n_seq * n_layers * n_kv_heads * total slots
+ *   kept_count device int32, n_seq * n_layers * n_kv_heads slots (always written)
+ *   workspace  device, 16-byte aligned, >= tri_select_shared_workspace_bytes
+ * The firing decision is taken on the device (head lengths may live only
+ * there).  n_kv_heads <= 128.  Calls sharing a workspace must not overlap.
+ * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED (n_kv_heads > 128), TRI_E_HIP.
+ * Source: romaanj.github.io review, section "Future work" (refined
+ * compression with head-specific budgets); section "Method" and figure 4
+ * caption for the top-scoring keys surviving.
+ */
+tri_status tri_select_shared(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
+                             const float* scores, int32_t budget, int32_t floor, int32_t window,
+                             int32_t* kept, int32_t* kept_count, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/*
+ * Evicts in place with a kept count per head: for every head whose
+ * kept_count c >= 0, rows r < c of K, V and positions become the rows at
+ * kept[r] (stable), and head_len of that head becomes c; heads with
+ * c == -1 are left as they are.  seqs[s].len is not changed (it stays an
+ * upper bound on every head's rows; a caller that knows a smaller bound may
+ * lower it).  Rows [c, cap) hold unspecified data afterwards.  Not
+ * failure-atomic.
+ *   kept        device int32 [n_seq][n_layers][n_kv_heads][kept_stride],
+ *               every list strictly ascending within the head's rows
+ *   kept_count  device int32 [n_seq][n_layers][n_kv_heads], -1 or in
+ *               [0, kept_stride]
+ *   every sequence needs head_len != NULL
+ * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP.
+ * Source: dimensionstp.github.io review, section 3-2 item 5 (evict the rest)
+ * and section 6 item 1 (cache compaction); romaanj.github.io review,
+ * section "Future work" (head-specific budgets).
+ */
+tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
+                                 int32_t n_seq, const int32_t* kept, int32_t kept_stride,
+                                 const int32_t* kept_count, void* stream);
 
 #ifdef __cplusplus
 }

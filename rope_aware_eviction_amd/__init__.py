@@ -33,7 +33,8 @@ TRI_F32, TRI_BF16 = 0, 1
 EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last_hip_error",
             "tri_scores_count", "tri_score", "tri_score_workspace_bytes", "tri_score_ws",
             "tri_select_topb", "tri_compact_kv", "tri_calibrate_stats", "tri_distance_curve",
-            "tri_offset_set")
+            "tri_offset_set", "tri_select_shared_workspace_bytes", "tri_select_shared",
+            "tri_compact_kv_counts")
 
 
 class TriError(RuntimeError):
@@ -59,7 +60,8 @@ class _CalibDesc(ctypes.Structure):
 
 class _Seq(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
-                ("cap", ctypes.c_int32), ("len", ctypes.c_int32), ("p_now", ctypes.c_int64)]
+                ("cap", ctypes.c_int32), ("len", ctypes.c_int32), ("p_now", ctypes.c_int64),
+                ("head_len", ctypes.c_void_p)]
 
 
 _lib = None
@@ -105,6 +107,15 @@ def library() -> ctypes.CDLL:
         lib.tri_compact_kv.restype = ctypes.c_int
         lib.tri_compact_kv.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
                                        ctypes.c_int32, ctypes.c_int32, vp]
+        lib.tri_select_shared_workspace_bytes.restype = ctypes.c_int64
+        lib.tri_select_shared_workspace_bytes.argtypes = [vp, ctypes.c_int32]
+        lib.tri_select_shared.restype = ctypes.c_int
+        lib.tri_select_shared.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                          vp, ctypes.c_int64, vp]
+        lib.tri_compact_kv_counts.restype = ctypes.c_int
+        lib.tri_compact_kv_counts.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq),
+                                              ctypes.c_int32, vp, ctypes.c_int32, vp, vp]
         _lib = lib
     return _lib
 
@@ -152,13 +163,17 @@ class Context:
 class Seq:
     """One sequence's cache: K, V [n_layers][n_kv_heads][cap][head_dim] (float32
     or bfloat16), positions int32 [n_layers][n_kv_heads][cap], the length in
-    use and the newest position.  ``len`` is updated by tri_compact_kv."""
+    use and the newest position.  ``len`` is updated by tri_compact_kv.
+    ``head_len`` (optional int32 GPU tensor [n_layers][n_kv_heads]) gives
+    every head its own length up to ``len`` (a ragged cache); the shared-budget
+    compaction writes it."""
 
     def __init__(self, k: torch.Tensor, v: Optional[torch.Tensor], pos: Optional[torch.Tensor],
-                 len: int, p_now: int):
+                 len: int, p_now: int, head_len: Optional[torch.Tensor] = None):
         self.k, self.v, self.pos = k, v, pos
         self.len = int(len)
         self.p_now = int(p_now)
+        self.head_len = head_len
 
     @property
     def cap(self) -> int:
@@ -271,9 +286,15 @@ def _seq_array(ctx: Context, seqs: Sequence[Seq], need_kv: bool):
             if s.pos is None or s.pos.dtype != torch.int32 or tuple(s.pos.shape) != tuple(k.shape[:3]) \
                     or not s.pos.is_contiguous():
                 raise ValueError("seq %d: pos must be int32 [n_layers][n_kv_heads][cap]" % i)
+        hl = getattr(s, "head_len", None)
+        if hl is not None and not (hl.is_cuda and hl.dtype == torch.int32 and hl.is_contiguous()
+                                   and tuple(hl.shape) == (ctx.n_layers, ctx.n_kv_heads)):
+            raise ValueError("seq %d: head_len must be a contiguous int32 GPU tensor "
+                             "[n_layers][n_kv_heads]" % i)
         arr[i] = _Seq(k.data_ptr(), s.v.data_ptr() if s.v is not None else None,
                       s.pos.data_ptr() if s.pos is not None else None,
-                      int(k.shape[2]), int(s.len), int(s.p_now))
+                      int(k.shape[2]), int(s.len), int(s.p_now),
+                      hl.data_ptr() if hl is not None else None)
     return arr, (TRI_BF16 if dtype is None else dtype)
 
 
@@ -361,3 +382,68 @@ def prune_step(ctx: Context, seqs: List[Seq], budget: int, window: int, scores: 
     tri_score(ctx, seqs, scores, stream, workspace)
     tri_select_topb(ctx, seqs, scores, budget, window, kept, stream)
     tri_compact_kv(ctx, seqs, kept, budget, window, stream)
+
+
+def select_shared_workspace_bytes(ctx: Context, n_seq: int) -> int:
+    """Device workspace bytes tri_select_shared needs for n_seq sequences."""
+    n = library().tri_select_shared_workspace_bytes(ctx.handle, int(n_seq))
+    if n < 0:
+        raise ValueError("bad arguments for tri_select_shared_workspace_bytes")
+    return int(n)
+
+
+def tri_select_shared(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, budget: int,
+                      floor: int, window: int, kept: torch.Tensor, kept_count: torch.Tensor,
+                      workspace: torch.Tensor, stream=None):
+    """Head-specific budgets: the heads of a layer share budget * n_kv_heads
+    slots, each keeping at least its ``floor`` best keys.  Writes kept slots
+    into ``kept`` int32 [n_seq][n_layers][n_kv_heads][budget * n_kv_heads] and
+    per-head counts (-1: the layer does not fire) into ``kept_count`` int32
+    [n_seq][n_layers][n_kv_heads]."""
+    arr, _ = _seq_array(ctx, seqs, need_kv=False)
+    total = int(budget) * ctx.n_kv_heads
+    if kept.dtype != torch.int32 or not kept.is_cuda or not kept.is_contiguous() \
+            or kept.numel() < len(seqs) * ctx.n_heads * total:
+        raise ValueError("kept must be a contiguous int32 GPU tensor of n_seq*n_heads*total")
+    if kept_count.dtype != torch.int32 or not kept_count.is_cuda \
+            or not kept_count.is_contiguous() or kept_count.numel() < len(seqs) * ctx.n_heads:
+        raise ValueError("kept_count must be a contiguous int32 GPU tensor of n_seq*n_heads")
+    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous() \
+            or scores.numel() < scores_count(ctx, seqs):
+        raise ValueError("scores must be a contiguous fp32 GPU tensor")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(library().tri_select_shared(ctx.handle, arr, len(seqs), scores.data_ptr(), int(budget),
+                                       int(floor), int(window), kept.data_ptr(),
+                                       kept_count.data_ptr(), workspace.data_ptr(), nbytes,
+                                       _stream_ptr(stream)), "tri_select_shared")
+
+
+def tri_compact_kv_counts(ctx: Context, seqs: Sequence[Seq], kept: torch.Tensor,
+                          kept_stride: int, kept_count: torch.Tensor, stream=None):
+    """Compacts every head with a kept count >= 0 in place and writes the count
+    into the sequence's ``head_len`` (which every sequence needs)."""
+    arr, dtype = _seq_array(ctx, seqs, need_kv=True)
+    if kept.dtype != torch.int32 or not kept.is_cuda or not kept.is_contiguous() \
+            or kept.numel() < len(seqs) * ctx.n_heads * kept_stride:
+        raise ValueError("kept must be a contiguous int32 GPU tensor of n_seq*n_heads*kept_stride")
+    if kept_count.dtype != torch.int32 or not kept_count.is_cuda \
+            or not kept_count.is_contiguous() or kept_count.numel() < len(seqs) * ctx.n_heads:
+        raise ValueError("kept_count must be a contiguous int32 GPU tensor of n_seq*n_heads")
+    _check(library().tri_compact_kv_counts(ctx.handle, dtype, arr, len(seqs), kept.data_ptr(),
+                                           int(kept_stride), kept_count.data_ptr(),
+                                           _stream_ptr(stream)), "tri_compact_kv_counts")
+
+
+def prune_step_shared(ctx: Context, seqs: List[Seq], budget: int, floor: int, window: int,
+                      scores: torch.Tensor, kept: torch.Tensor, kept_count: torch.Tensor,
+                      select_workspace: torch.Tensor, stream=None,
+                      workspace: Optional[torch.Tensor] = None):
+    """One prune step with head-specific budgets (score, shared select,
+    compaction with per-head counts) on one stream, no host sync.  Every
+    sequence needs ``head_len``."""
+    tri_score(ctx, seqs, scores, stream, workspace)
+    tri_select_shared(ctx, seqs, scores, budget, floor, window, kept, kept_count,
+                      select_workspace, stream)
+    tri_compact_kv_counts(ctx, seqs, kept, int(budget) * ctx.n_kv_heads, kept_count, stream)

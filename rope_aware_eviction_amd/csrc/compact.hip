@@ -53,7 +53,9 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
                                                          int32_t* __restrict__ pos, int64_t cap,
                                                          int len,
                                                          const int32_t* __restrict__ kept,
-                                                         int budget, int n_heads)
+                                                         int budget, int kept_stride, int n_heads,
+                                                         const int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ head_len)
 {
     constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
     constexpr int kRowsPerStep = kBlock / kChunks;
@@ -67,9 +69,14 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
     for (int stream_id = blockIdx.x; stream_id < 2 * n_heads; stream_id += gridDim.x) {
         const int head = stream_id >> 1;
         const bool is_v = (stream_id & 1) != 0;
+        // rows this head keeps: `budget`, or its own count (-1: the head is
+        // left as it is; head_len takes the new count)
+        const int n_keep = counts ? min(counts[head], kept_stride) : budget;
+        if (n_keep < 0) continue;
+        if (counts && !is_v && threadIdx.x == 0) head_len[head] = n_keep;
         unsigned char* rows = (is_v ? v : k) + (size_t)head * (size_t)cap * ROWB;
         int32_t* hpos = pos + (size_t)head * (size_t)cap;
-        const int32_t* idx = kept + (size_t)head * (size_t)budget;
+        const int32_t* idx = kept + (size_t)head * (size_t)kept_stride;
         const __amdgpu_buffer_rsrc_t rrows =
             __builtin_amdgcn_make_buffer_rsrc(rows, 0, len * ROWB, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rpos =
@@ -99,8 +106,8 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int r = t0 + u * kRowsPerStep + rs;
-                const int src = r < budget ? srcs[u] : r;
-                const bool mv = r < budget && src != r && (unsigned)src < (unsigned)len;
+                const int src = r < n_keep ? srcs[u] : r;
+                const bool mv = r < n_keep && src != r && (unsigned)src < (unsigned)len;
                 const uint32_t from = mv ? (uint32_t)src * ROWB + 16u * c : kDrop;
                 t.dst[u] = mv ? (uint32_t)r * ROWB + 16u * c : kDrop;
                 t.buf[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrows, from, 0, kNT));
@@ -109,8 +116,8 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
             for (int q = 0; q < kPosPerThread; ++q) {
                 const int i = q * kBlock + tid;
                 const int r = t0 + i;
-                const int src = (i < kTile && r < budget) ? s_idx[r - c0] : r;
-                const bool mv = !is_v && i < kTile && r < budget && src != r && (unsigned)src < (unsigned)len;
+                const int src = (i < kTile && r < n_keep) ? s_idx[r - c0] : r;
+                const bool mv = !is_v && i < kTile && r < n_keep && src != r && (unsigned)src < (unsigned)len;
                 t.pdst[q] = mv ? (uint32_t)r * 4u : kDrop;
                 t.pval[q] = __builtin_amdgcn_raw_buffer_load_b32(rpos, mv ? (uint32_t)src * 4u : kDrop, 0, 0);
             }
@@ -124,8 +131,8 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
                 __builtin_amdgcn_raw_buffer_store_b32(t.pval[q], rpos, t.pdst[q], 0, 0);
         };
 
-        for (int c0 = 0; c0 < budget; c0 += kIdxChunk) {
-            const int c1 = min(budget, c0 + kIdxChunk);
+        for (int c0 = 0; c0 < n_keep; c0 += kIdxChunk) {
+            const int c1 = min(n_keep, c0 + kIdxChunk);
             __syncthreads();                               // previous chunk's index reads done
             for (int i = c0 + tid; i < c1; i += kBlock) s_idx[i - c0] = idx[i];
             __syncthreads();
@@ -158,7 +165,8 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
 
 template <int ROWB>
 hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_heads,
-                  const int32_t* kept, int budget, hipStream_t stream)
+                  const int32_t* kept, int budget, int kept_stride, const int32_t* counts,
+                  int32_t* head_len, hipStream_t stream)
 {
     // Each workgroup walks whole K or V streams one after another, at most
     // one workgroup per compute unit, every workgroup the same number of
@@ -181,22 +189,27 @@ hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_he
     const int grid = (streams + per_block - 1) / per_block;
     hipLaunchKernelGGL(compact_kernel<ROWB>, dim3(grid), dim3(kBlock), 0, stream,
                        static_cast<unsigned char*>(k), static_cast<unsigned char*>(v), pos, cap,
-                       len, kept, budget, n_heads);
+                       len, kept, budget, kept_stride, n_heads, counts, head_len);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
-                          int n_heads, const int32_t* kept, int budget, hipStream_t stream)
+                          int n_heads, const int32_t* kept, int budget, int kept_stride,
+                          const int32_t* counts, int32_t* head_len, hipStream_t stream)
 {
-    if (n_heads <= 0 || budget <= 0) return hipSuccess;
+    if (n_heads <= 0 || kept_stride <= 0 || (!counts && budget <= 0)) return hipSuccess;
+    if (counts && !head_len) return hipErrorInvalidValue;
     // buffer offsets are 32-bit: a head's rows must span less than 2 GiB
     if ((int64_t)len * row_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     switch (row_bytes) {
-    case 128: return launch<128>(k, v, pos, cap, len, n_heads, kept, budget, stream);
-    case 256: return launch<256>(k, v, pos, cap, len, n_heads, kept, budget, stream);
-    case 512: return launch<512>(k, v, pos, cap, len, n_heads, kept, budget, stream);
+    case 128: return launch<128>(k, v, pos, cap, len, n_heads, kept, budget, kept_stride, counts,
+                                 head_len, stream);
+    case 256: return launch<256>(k, v, pos, cap, len, n_heads, kept, budget, kept_stride, counts,
+                                 head_len, stream);
+    case 512: return launch<512>(k, v, pos, cap, len, n_heads, kept, budget, kept_stride, counts,
+                                 head_len, stream);
     default: return hipErrorInvalidValue;
     }
 }

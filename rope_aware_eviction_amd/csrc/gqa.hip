@@ -169,7 +169,7 @@ template <int D, bool BF16, int G>
 __global__ __launch_bounds__(kBlock) void gqa_score_kernel(
     const unsigned char* __restrict__ k, int64_t cap, int len, int tiles_per_head, double p_now,
     const double* __restrict__ omega, const double2* __restrict__ qa, const float* __restrict__ w,
-    float* __restrict__ raw, double* __restrict__ partial)
+    float* __restrict__ raw, double* __restrict__ partial, const int32_t* __restrict__ head_len)
 {
     using S = GqaShape<D, BF16, G>;
     constexpr int kHalf = S::kHalf, LPR = S::LPR, E = S::E, GR = S::GR, kUnroll = S::kUnroll;
@@ -184,6 +184,10 @@ __global__ __launch_bounds__(kBlock) void gqa_score_kernel(
 
     const int head = blockIdx.x / tiles_per_head;
     const int tile = blockIdx.x - head * tiles_per_head;
+    // rows in use of this head: all `len`, or its own length (ragged heads);
+    // tiles past it are skipped and left out of the statistics
+    const int n_h = head_len ? max(0, min(head_len[head], len)) : len;
+    if (tile * kTileRows >= n_h) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void gqa_score_kernel(
     const int g0 = tid / LPR;  // row within a workgroup step
     const unsigned char* base = k + (size_t)head * (size_t)cap * kRowBytes + EB * j;
     const int tile_start = tile * kTileRows;
-    const int row_end = min(len, tile_start + kTileRows);
+    const int row_end = min(n_h, tile_start + kTileRows);
 
     Chunk<BF16, EB> re[kUnroll], im[kUnroll];
     auto load_row = [&](int u, int row) {
@@ -318,14 +322,17 @@ __global__ __launch_bounds__(kBlock) void gqa_score_kernel(
 // tiles t, t + 64, ... in order, then a fixed butterfly combines the lanes,
 // so the result does not depend on scheduling
 __global__ __launch_bounds__(64) void gqa_stats_kernel(const double* __restrict__ partial,
-                                                       int tiles_per_head, int group,
+                                                       int tiles_per_head, int group, int len,
+                                                       const int32_t* __restrict__ head_len,
                                                        double2* __restrict__ stats)
 {
     const int head = blockIdx.x;
     const int lane = threadIdx.x;
+    const int n_h = head_len ? max(0, min(head_len[head], len)) : len;
+    const int tiles = (n_h + kTileRows - 1) / kTileRows;   // tiles the score kernel wrote
     for (int g = 0; g < group; ++g) {
         double s1 = 0.0, s2 = 0.0, cnt = 0.0, big = 0.0;
-        for (int tile = lane; tile < tiles_per_head; tile += 64) {
+        for (int tile = lane; tile < tiles; tile += 64) {
             const double* p = partial + (((size_t)head * tiles_per_head + tile) * group + g) * 4;
             s1 += p[0];
             s2 += p[1];
@@ -353,7 +360,8 @@ template <int G>
 __global__ __launch_bounds__(kBlock) void gqa_norm_kernel(const float* __restrict__ raw,
                                                           const double2* __restrict__ stats,
                                                           int len, int tiles_per_head,
-                                                          float* __restrict__ scores)
+                                                          float* __restrict__ scores,
+                                                          const int32_t* __restrict__ head_len)
 {
     __shared__ double s_mean[G], s_inv[G];   // s_inv = 0: flat row, z = 0
     const int head = blockIdx.x / tiles_per_head;
@@ -364,7 +372,8 @@ __global__ __launch_bounds__(kBlock) void gqa_norm_kernel(const float* __restric
         s_inv[threadIdx.x] = st.y > 0.0 ? 1.0 / st.y : 0.0;
     }
     __syncthreads();
-    const int row_end = min(len, (tile + 1) * kTileRows);
+    const int n_h = head_len ? max(0, min(head_len[head], len)) : len;
+    const int row_end = min(n_h, (tile + 1) * kTileRows);
     for (int r = tile * kTileRows + threadIdx.x; r < row_end; r += kBlock) {
         const float* p = raw + ((size_t)head * len + r) * G;
         float x[G];
@@ -386,34 +395,36 @@ __global__ __launch_bounds__(kBlock) void gqa_norm_kernel(const float* __restric
 template <int D, bool BF16, int G>
 hipError_t launch_g(const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
                     const double* omega, const double2* qa, const float* w, float* raw,
-                    double* partial, double2* stats, float* scores, hipStream_t stream)
+                    double* partial, double2* stats, float* scores, const int32_t* head_len,
+                    hipStream_t stream)
 {
     const int tiles = (len + kTileRows - 1) / kTileRows;
     const int64_t grid = (int64_t)tiles * n_heads;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gqa_score_kernel<D, BF16, G>), dim3((unsigned)grid), dim3(kBlock), 0,
                        stream, static_cast<const unsigned char*>(k), cap, len, tiles,
-                       (double)p_now, omega, qa, w, raw, partial);
+                       (double)p_now, omega, qa, w, raw, partial, head_len);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gqa_stats_kernel, dim3(n_heads), dim3(64), 0, stream, partial, tiles, G,
-                       stats);
+                       len, head_len, stats);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gqa_norm_kernel<G>), dim3((unsigned)grid), dim3(kBlock), 0, stream, raw,
-                       stats, len, tiles, scores);
+                       stats, len, tiles, scores, head_len);
     return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_d(int group, const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
                     const double* omega, const double2* qa, const float* w, float* raw,
-                    double* partial, double2* stats, float* scores, hipStream_t stream)
+                    double* partial, double2* stats, float* scores, const int32_t* head_len,
+                    hipStream_t stream)
 {
 #define TRI_GQA_CASE(G)                                                                           \
     case G:                                                                                       \
         return launch_g<D, BF16, G>(k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,      \
-                                    stats, scores, stream);
+                                    stats, scores, head_len, stream);
     switch (group) {
         TRI_GQA_CASE(2)
         TRI_GQA_CASE(3)
@@ -440,7 +451,7 @@ int64_t gqa_workspace_bytes(int64_t n_heads, int64_t len, int group)
 hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void* k, int64_t cap,
                             int len, int n_heads, int64_t p_now, const double* omega,
                             const double2* qa, const float* w, void* workspace, float* scores,
-                            hipStream_t stream)
+                            const int32_t* head_len, hipStream_t stream)
 {
     if (len <= 0 || n_heads <= 0) return hipSuccess;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
@@ -452,16 +463,16 @@ hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void
                                                 up((int64_t)n_heads * tiles * group * 4 * 8));
     if (dtype == TRI_BF16 && head_dim == 128)
         return launch_d<128, true>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                   stats, scores, stream);
+                                   stats, scores, head_len, stream);
     if (dtype == TRI_F32 && head_dim == 64)
         return launch_d<64, false>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                   stats, scores, stream);
+                                   stats, scores, head_len, stream);
     if (dtype == TRI_BF16 && head_dim == 64)
         return launch_d<64, true>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                  stats, scores, stream);
+                                  stats, scores, head_len, stream);
     if (dtype == TRI_F32 && head_dim == 128)
         return launch_d<128, false>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                    stats, scores, stream);
+                                    stats, scores, head_len, stream);
     return hipErrorInvalidValue;
 }
 

@@ -88,7 +88,7 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(kBlock) void score_kernel(
     const unsigned char* __restrict__ k, int64_t cap, int len, int tiles_per_head, double p_now,
     const double* __restrict__ omega, const double2* __restrict__ qa, const float* __restrict__ w,
-    float* __restrict__ scores)
+    float* __restrict__ scores, const int32_t* __restrict__ head_len)
 {
     constexpr int kHalf = D / 2;
     constexpr int kElem = Elem<BF16>::kSize;
@@ -104,12 +104,15 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
 
     const int head = blockIdx.x / tiles_per_head;
     const int tile = blockIdx.x - head * tiles_per_head;
+    // rows in use of this head: all `len`, or its own length (ragged heads)
+    const int n_h = head_len ? max(0, min(head_len[head], len)) : len;
+    if (tile * kTileRows >= n_h) return;   // whole workgroup: nothing of this head here
     const int tid = threadIdx.x;
     const int j = tid % LPR;   // lane within the row
     const int g = tid / LPR;   // row group within the workgroup
     const unsigned char* base = k + (size_t)head * (size_t)cap * kRowBytes + 16 * j;
     float* out = scores + (size_t)head * (size_t)len;
-    const int row_end = min(len, (tile + 1) * kTileRows);
+    const int row_end = min(n_h, (tile + 1) * kTileRows);
 
     // K is streamed once: non-temporal loads keep it from displacing the
     // scores and constants in the caches.  Rows past the end of the tile
@@ -187,14 +190,14 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
 template <int D, bool BF16>
 hipError_t launch(const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
                   const double* omega, const double2* qa, const float* w, float* scores,
-                  hipStream_t stream)
+                  const int32_t* head_len, hipStream_t stream)
 {
     const int tiles = (len + kTileRows - 1) / kTileRows;
     const int64_t grid = (int64_t)tiles * n_heads;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((score_kernel<D, BF16>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        static_cast<const unsigned char*>(k), cap, len, tiles, (double)p_now, omega,
-                       qa, w, scores);
+                       qa, w, scores, head_len);
     return hipGetLastError();
 }
 
@@ -202,17 +205,17 @@ hipError_t launch(const void* k, int64_t cap, int len, int n_heads, int64_t p_no
 
 hipError_t launch_score(tri_dtype dtype, int head_dim, const void* k, int64_t cap, int len,
                         int n_heads, int64_t p_now, const double* omega, const double2* qa,
-                        const float* w, float* scores, hipStream_t stream)
+                        const float* w, float* scores, const int32_t* head_len, hipStream_t stream)
 {
     if (len <= 0 || n_heads <= 0) return hipSuccess;
     if (dtype == TRI_BF16 && head_dim == 128)
-        return launch<128, true>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+        return launch<128, true>(k, cap, len, n_heads, p_now, omega, qa, w, scores, head_len, stream);
     if (dtype == TRI_F32 && head_dim == 64)
-        return launch<64, false>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+        return launch<64, false>(k, cap, len, n_heads, p_now, omega, qa, w, scores, head_len, stream);
     if (dtype == TRI_BF16 && head_dim == 64)
-        return launch<64, true>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+        return launch<64, true>(k, cap, len, n_heads, p_now, omega, qa, w, scores, head_len, stream);
     if (dtype == TRI_F32 && head_dim == 128)
-        return launch<128, false>(k, cap, len, n_heads, p_now, omega, qa, w, scores, stream);
+        return launch<128, false>(k, cap, len, n_heads, p_now, omega, qa, w, scores, head_len, stream);
     return hipErrorInvalidValue;
 }
 

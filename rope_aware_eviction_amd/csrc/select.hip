@@ -83,8 +83,11 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v)
 }
 
 template <bool kInLds>
-__global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict__ scores, int n,
-                                                        int budget, int32_t* __restrict__ kept)
+__global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict__ scores,
+                                                        int stride, int budget,
+                                                        int32_t* __restrict__ kept,
+                                                        int kept_stride,
+                                                        const int32_t* __restrict__ head_len)
 {
     extern __shared__ uint32_t smem[];
     uint32_t* hist = smem;                             // [kHistBins]
@@ -93,11 +96,15 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict_
     __shared__ uint32_t s_wgt[kWaves], s_weq[kWaves];
     __shared__ uint32_t s_digit, s_above;
 
+    // keys of this head: all `stride`, or its own length (ragged heads); a
+    // head with at most `budget` keys keeps them all and gets no list
+    const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
+    if (n <= budget) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const float* sc = scores + (size_t)blockIdx.x * (size_t)n;
-    int32_t* out = kept + (size_t)blockIdx.x * (size_t)budget;
+    const float* sc = scores + (size_t)blockIdx.x * (size_t)stride;
+    int32_t* out = kept + (size_t)blockIdx.x * (size_t)kept_stride;
 
     // stage keys (when they fit) and find the key range of the head
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -327,8 +334,10 @@ __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane)
 // slot order".
 template <int KPT, int NT>
 __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict__ scores,
-                                                        int n, int budget,
-                                                        int32_t* __restrict__ kept)
+                                                        int stride, int budget,
+                                                        int32_t* __restrict__ kept,
+                                                        int kept_stride,
+                                                        const int32_t* __restrict__ head_len)
 {
     constexpr int kW = NT / 64;
     __shared__ uint32_t hist[1 << kRegDigitBits];
@@ -337,11 +346,15 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
     __shared__ uint32_t s_digit, s_above, s_inbin, s_ncand;
     __shared__ uint32_t s_T, s_need, s_tie;
 
+    // keys of this head: all `stride`, or its own length (ragged heads); a
+    // head with at most `budget` keys keeps them all and gets no list
+    const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
+    if (n <= budget) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const float* sc = scores + (size_t)blockIdx.x * (size_t)n;
-    int32_t* out = kept + (size_t)blockIdx.x * (size_t)budget;
+    const float* sc = scores + (size_t)blockIdx.x * (size_t)stride;
+    int32_t* out = kept + (size_t)blockIdx.x * (size_t)kept_stride;
     const int seg0 = wave * (64 * KPT) + lane;     // slot of key[0]
 
     // Slots past the head's end hold key 0, below every real key (ordered_key
@@ -526,21 +539,319 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Head-specific budgets: the n_kv heads of a layer share total = budget *
+// n_kv slots.  Every head reserves its `floor` best keys (found per head by
+// the selection above, run with budget = floor); the remaining slots go to
+// the best remaining keys of the layer, ties to the lower head and then the
+// lower slot.
+//
+// A head's reserved set is exactly "key > Th, or key == Th and slot <= Sh",
+// where Th is the smallest key on its reserved list and Sh the largest
+// reserved slot holding Th: the list holds every key above its smallest key
+// and the lowest slots among the keys equal to it.  So the reserved set is
+// a pointwise test and needs no flag array.
+//
+// shared_layer_kernel (one workgroup per layer) takes the firing decision,
+// derives (Th, Sh) per head, then runs the offset radix select of the
+// register-resident kernel over the layer's unreserved keys, re-reading
+// them from memory each pass, for rem = total - (reserved keys) slots.  When
+// equal keys straddle the threshold it counts them per head and hands them
+// out in head order.  shared_write_kernel (one workgroup per head) then
+// writes each head's kept list in slot order and its count.
+
+constexpr int kMaxSharedHeads = 128;
+
+__device__ __forceinline__ int wave_max_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Calls f(key, unreserved) for every key of the layer's heads (slot
+// i < s_n[h]), kBatch loads in flight per thread; head h's reserved set is
+// key > s_th[h], or key == s_th[h] and i <= s_sh[h].
+template <typename F>
+__device__ __forceinline__ void for_layer_keys(const float* sc, int stride, int n_kv,
+                                               const int* s_n, const uint32_t* s_th,
+                                               const int* s_sh, int tid, F&& f)
+{
+    for (int h = 0; h < n_kv; ++h) {
+        const int n = s_n[h];
+        const uint32_t th = s_th[h];
+        const int sh = s_sh[h];
+        const float* hs = sc + (size_t)h * (size_t)stride;
+        for (int i0 = tid; i0 < n; i0 += kBlock * kBatch) {
+            float x[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) x[u] = hs[min(i0 + u * kBlock, n - 1)];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = i0 + u * kBlock;
+                const uint32_t key = ordered_key(x[u]);
+                if (i < n) f(key, !(key > th || (key == th && i <= sh)));
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void shared_layer_kernel(
+    const float* __restrict__ scores, int stride, int n_kv, const int32_t* __restrict__ head_len,
+    int total, int floor_, int window, const int32_t* __restrict__ kept,
+    uint4* __restrict__ ws_head, uint4* __restrict__ ws_layer)
+{
+    __shared__ uint32_t hist[1 << kRegDigitBits];
+    __shared__ int s_n[kMaxSharedHeads];
+    __shared__ uint32_t s_Th[kMaxSharedHeads];
+    __shared__ int s_Sh[kMaxSharedHeads];
+    __shared__ uint32_t s_eq[kMaxSharedHeads];
+    __shared__ uint32_t s_wa[kWaves], s_wb[kWaves], s_run[kWaves];
+    __shared__ uint32_t s_digit, s_above, s_inbin;
+
+    const int layer = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const float* sc = scores + (size_t)layer * (size_t)n_kv * (size_t)stride;
+    const int32_t* lists = kept + (size_t)layer * (size_t)n_kv * (size_t)total;
+    uint4* wh = ws_head + (size_t)layer * (size_t)n_kv;
+
+    for (int h = tid; h < n_kv; h += kBlock) {
+        s_n[h] = head_len ? max(0, min(head_len[(size_t)layer * n_kv + h], stride)) : stride;
+        s_eq[h] = 0u;
+    }
+    __syncthreads();
+    int64_t all = 0;
+    for (int h = 0; h < n_kv; ++h) all += s_n[h];
+    if (all <= (int64_t)total + (int64_t)n_kv * window) {      // the layer keeps every key
+        if (tid == 0) ws_layer[layer] = make_uint4(0u, 0u, 0u, 0u);
+        return;
+    }
+
+    // reserved sets: (Th, Sh) per head from its reserved list
+    for (int h = wave; h < n_kv; h += kWaves) {
+        const int n = s_n[h];
+        uint32_t th;
+        int sh;
+        if (floor_ == 0) {
+            th = kTopKey;                 // no key is above it: nothing reserved
+            sh = -1;
+        } else if (n <= floor_) {
+            th = 0u;                      // every real key is above it: all reserved
+            sh = -1;
+        } else {
+            const int32_t* l = lists + (size_t)h * (size_t)total;
+            const float* hs = sc + (size_t)h * (size_t)stride;
+            uint32_t mn = 0xFFFFFFFFu;
+            for (int j = lane; j < floor_; j += 64)
+                mn = min(mn, ordered_key(hs[min(max(l[j], 0), n - 1)]));
+            mn = wave_min(mn);
+            int mx = -1;
+            for (int j = lane; j < floor_; j += 64) {
+                const int slot = min(max(l[j], 0), n - 1);
+                if (ordered_key(hs[slot]) == mn) mx = max(mx, slot);
+            }
+            th = mn;
+            sh = wave_max_i(mx);
+        }
+        if (lane == 0) {
+            s_Th[h] = th;
+            s_Sh[h] = sh;
+        }
+    }
+    __syncthreads();
+    int64_t reserved = 0;
+    for (int h = 0; h < n_kv; ++h) reserved += min(s_n[h], floor_);
+    uint32_t rem = (uint32_t)((int64_t)total - reserved);   // floor * n_kv <= total
+
+    uint32_t T = kTopKey, need_eq = 0u;
+    bool tie = false;
+    if (rem > 0u) {
+        // key range of the unreserved keys (more than rem of them: the layer fires)
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        for_layer_keys(sc, stride, n_kv, s_n, s_Th, s_Sh, tid, [&](uint32_t key, bool unres) {
+            if (unres) {
+                lo = min(lo, key);
+                hi = max(hi, key);
+            }
+        });
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) {
+            s_wa[wave] = lo;
+            s_wb[wave] = hi;
+        }
+        __syncthreads();
+        uint32_t kmin = s_wa[0], kmax = s_wb[0];
+        for (int x = 1; x < kWaves; ++x) {
+            kmin = min(kmin, s_wa[x]);
+            kmax = max(kmax, s_wb[x]);
+        }
+        if (kmin == kmax) {
+            T = kmin;
+            need_eq = rem;
+            tie = true;
+        } else {
+            uint32_t base = kmin;
+            int wb = 32 - __clz((int)(kmax - kmin));    // live keys: [base, base + 2^wb)
+            for (;;) {
+                const int nb = min(kRegDigitBits, wb);
+                const int shift = wb - nb;
+                const uint32_t nbins = 1u << nb;
+                const uint32_t span = wb >= 32 ? 0xFFFFFFFFu : (1u << wb) - 1u;
+                __syncthreads();                         // previous readers of hist / s_*
+                for (uint32_t b = tid; b < nbins; b += kBlock) hist[b] = 0u;
+                __syncthreads();
+                for_layer_keys(sc, stride, n_kv, s_n, s_Th, s_Sh, tid, [&](uint32_t key, bool unres) {
+                    const uint32_t off = key - base;
+                    if (off <= span && unres) atomicAdd(&hist[off >> shift], 1u);
+                });
+                __syncthreads();
+                find_digit<kBlock>(hist, nbins, rem, tid, lane, wave, s_run, &s_digit, &s_above,
+                                   &s_inbin);
+                __syncthreads();
+                const uint32_t d = s_digit & (nbins - 1u);
+                const uint32_t in_bin = s_inbin;
+                rem -= s_above;
+                base += d << shift;
+                wb = shift;
+                if (rem == in_bin) {                     // the whole bin is kept
+                    T = base;
+                    tie = false;
+                    break;
+                }
+                if (wb == 0) {                           // one key value straddles
+                    T = base;
+                    need_eq = rem;
+                    tie = true;
+                    break;
+                }
+            }
+        }
+        if (tie) {
+            // equal keys per head, handed out in head order
+            for (int h = 0; h < n_kv; ++h) {
+                const int n = s_n[h];
+                const uint32_t th = s_Th[h];
+                const int sh = s_Sh[h];
+                const float* hs = sc + (size_t)h * (size_t)stride;
+                uint32_t c = 0u;
+                for (int i = tid; i < n; i += kBlock) {
+                    const uint32_t key = ordered_key(hs[i]);
+                    c += (key == T && !(key > th || (key == th && i <= sh))) ? 1u : 0u;
+                }
+                c = wave_sum(c);
+                if (lane == 0 && c) atomicAdd(&s_eq[h], c);
+            }
+            __syncthreads();
+        }
+    }
+    if (tid == 0) {
+        uint32_t left = need_eq;
+        for (int h = 0; h < n_kv; ++h) {
+            const uint32_t take = tie ? min(s_eq[h], left) : 0u;
+            left -= take;
+            wh[h] = make_uint4(s_Th[h], (uint32_t)s_Sh[h], take, 0u);
+        }
+        ws_layer[layer] = make_uint4(T, tie ? 1u : 0u, 1u, 0u);
+    }
+}
+
+// One workgroup per head: the kept list of the head in slot order and its
+// count (-1 when the layer does not fire).  Wave w owns slots
+// [w*seg, (w+1)*seg); a counting sweep gives every wave its offset.
+__global__ __launch_bounds__(kBlock) void shared_write_kernel(
+    const float* __restrict__ scores, int stride, int n_kv, const int32_t* __restrict__ head_len,
+    int total, const uint4* __restrict__ ws_head, const uint4* __restrict__ ws_layer,
+    int32_t* __restrict__ kept, int32_t* __restrict__ kept_count)
+{
+    __shared__ uint32_t s_wgt[kWaves], s_weq[kWaves];
+    const int lh = blockIdx.x;
+    const int layer = lh / n_kv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const uint4 lw = ws_layer[layer];
+    if (lw.z == 0u) {
+        if (tid == 0) kept_count[lh] = -1;
+        return;
+    }
+    const uint4 hw = ws_head[lh];
+    const uint32_t th = hw.x;
+    const int sh = (int)hw.y;
+    const uint32_t take = hw.z;
+    const uint32_t T = lw.x;
+    const bool tie = lw.y != 0u;
+    const int n = head_len ? max(0, min(head_len[lh], stride)) : stride;
+    const float* sc = scores + (size_t)lh * (size_t)stride;
+    int32_t* out = kept + (size_t)lh * (size_t)total;
+
+    // gt: kept outright (reserved, or above the layer threshold);
+    // eq: unreserved and equal to T when equal keys straddle it
+    auto classify = [&](int i, bool& gt, bool& eq) {
+        const uint32_t key = i < n ? ordered_key(sc[i]) : 0u;
+        const bool res = i < n && (key > th || (key == th && i <= sh));
+        gt = res || (i < n && (tie ? key > T : key >= T));
+        eq = !res && tie && i < n && key == T;
+    };
+    const int seg = ((n + kWaves - 1) / kWaves + 63) & ~63;
+    const int s0 = wave * seg;
+    const int s1 = min(n, s0 + seg);
+    uint32_t cgt = 0u, ceq = 0u;
+    for (int i0 = s0; i0 < s1; i0 += 64) {
+        bool gt, eq;
+        classify(i0 + lane < s1 ? i0 + lane : n, gt, eq);
+        cgt += (uint32_t)__popcll(__ballot(gt));
+        ceq += (uint32_t)__popcll(__ballot(eq));
+    }
+    if (lane == 0) {
+        s_wgt[wave] = cgt;
+        s_weq[wave] = ceq;
+    }
+    __syncthreads();
+    uint32_t gt_before = 0u, eq_before = 0u, gt_all = 0u, eq_all = 0u;
+    for (int x = 0; x < kWaves; ++x) {
+        if (x < wave) {
+            gt_before += s_wgt[x];
+            eq_before += s_weq[x];
+        }
+        gt_all += s_wgt[x];
+        eq_all += s_weq[x];
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int i0 = s0; i0 < s1; i0 += 64) {
+        const int i = i0 + lane;
+        bool gt, eq;
+        classify(i < s1 ? i : n, gt, eq);
+        const unsigned long long mgt = __ballot(gt);
+        const unsigned long long meq = __ballot(eq);
+        const uint32_t my_gt = gt_before + (uint32_t)__popcll(mgt & below);
+        const uint32_t my_eq = eq_before + (uint32_t)__popcll(meq & below);
+        const uint32_t at = my_gt + min(my_eq, take);
+        if ((gt || (eq && my_eq < take)) && at < (uint32_t)total) out[at] = i;
+        gt_before += (uint32_t)__popcll(mgt);
+        eq_before += (uint32_t)__popcll(meq);
+    }
+    if (tid == 0) kept_count[lh] = (int32_t)min(gt_all + min(eq_all, take), (uint32_t)total);
+}
+
 }  // namespace
 
 hipError_t launch_select(const float* scores, int n, int n_heads, int budget, int32_t* kept,
-                         hipStream_t stream)
+                         int kept_stride, const int32_t* head_len, hipStream_t stream)
 {
     if (n_heads <= 0 || n <= budget) return hipSuccess;
     if (n <= kBlock * 8) {
         hipLaunchKernelGGL((select_reg_kernel<8, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
-                           scores, n, budget, kept);
+                           scores, n, budget, kept, kept_stride, head_len);
     } else if (n <= kBlock * 16) {
         hipLaunchKernelGGL((select_reg_kernel<16, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
-                           scores, n, budget, kept);
+                           scores, n, budget, kept, kept_stride, head_len);
     } else if (n <= kBlock * 32) {
         hipLaunchKernelGGL((select_reg_kernel<32, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
-                           scores, n, budget, kept);
+                           scores, n, budget, kept, kept_stride, head_len);
     } else if (n <= kLdsKeysMax) {
         const size_t lds = (size_t)(kHistBins + n) * sizeof(uint32_t);
         static bool attr_set = false;
@@ -552,12 +863,46 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
             attr_set = true;
         }
         hipLaunchKernelGGL(select_kernel<true>, dim3(n_heads), dim3(kBlock), lds, stream, scores, n,
-                           budget, kept);
+                           budget, kept, kept_stride, head_len);
     } else {
         const size_t lds = (size_t)kHistBins * sizeof(uint32_t);
         hipLaunchKernelGGL(select_kernel<false>, dim3(n_heads), dim3(kBlock), lds, stream, scores,
-                           n, budget, kept);
+                           n, budget, kept, kept_stride, head_len);
     }
+    return hipGetLastError();
+}
+
+
+int64_t shared_workspace_bytes(int64_t n_seq, int64_t n_layers, int64_t n_kv)
+{
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    return up(n_seq * n_layers * n_kv * 16) + up(n_seq * n_layers * 16);
+}
+
+hipError_t launch_select_shared(const float* scores, int stride, int n_layers, int n_kv,
+                                const int32_t* head_len, int budget, int floor_, int window,
+                                int32_t* kept, int32_t* kept_count, void* ws_head, void* ws_layer,
+                                hipStream_t stream)
+{
+    if (n_layers <= 0 || n_kv <= 0) return hipSuccess;
+    if (n_kv > kMaxSharedHeads) return hipErrorInvalidValue;
+    const int64_t total = (int64_t)budget * n_kv;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (floor_ > 0 && stride > floor_) {
+        // each head's reserved list, into the head's kept row (stride total)
+        hipError_t e = launch_select(scores, stride, n_layers * n_kv, floor_, kept, (int)total,
+                                     head_len, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(shared_layer_kernel, dim3(n_layers), dim3(kBlock), 0, stream, scores,
+                       stride, n_kv, head_len, (int)total, floor_, window, kept,
+                       static_cast<uint4*>(ws_head), static_cast<uint4*>(ws_layer));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(shared_write_kernel, dim3(n_layers * n_kv), dim3(kBlock), 0, stream,
+                       scores, stride, n_kv, head_len, (int)total,
+                       static_cast<const uint4*>(ws_head), static_cast<const uint4*>(ws_layer),
+                       kept, kept_count);
     return hipGetLastError();
 }
 

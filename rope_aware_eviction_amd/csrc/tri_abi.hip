@@ -46,6 +46,7 @@ tri_status check_seqs(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq, bo
         const tri_seq& q = seqs[s];
         if (q.cap < 0 || q.len < 0 || q.len > q.cap) return TRI_E_INVAL;
         if (q.p_now < -(int64_t(1) << 52) || q.p_now > (int64_t(1) << 52)) return TRI_E_INVAL;
+        if ((uintptr_t)q.head_len & 3u) return TRI_E_INVAL;
         if (q.len == 0) continue;
         if (!q.k || !aligned16(q.k)) return TRI_E_INVAL;
         if (need_kv && (!q.v || !aligned16(q.v) || !q.pos || ((uintptr_t)q.pos & 3u)))
@@ -57,6 +58,14 @@ tri_status check_seqs(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq, bo
 bool fires(const tri_seq& q, int32_t budget, int32_t window)
 {
     return (int64_t)q.len > (int64_t)budget + (int64_t)window;
+}
+
+// Uniform budgets keep every head at one length: no per-head lengths.
+bool any_ragged(const tri_seq* seqs, int32_t n_seq)
+{
+    for (int32_t s = 0; s < n_seq; ++s)
+        if (seqs[s].head_len) return true;
+    return false;
 }
 
 }  // namespace
@@ -308,11 +317,11 @@ tri_status tri_score_ws(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs
             hipError_t e;
             if (ctx->group == 1) {
                 e = tri::launch_score(dtype, ctx->head_dim, q.k, q.cap, q.len, ctx->n_heads, q.p_now,
-                                      ctx->omega, ctx->qa, ctx->w, scores + off, hs);
+                                      ctx->omega, ctx->qa, ctx->w, scores + off, q.head_len, hs);
             } else {
                 e = tri::launch_gqa_score(dtype, ctx->head_dim, ctx->group, q.k, q.cap, q.len,
                                           ctx->n_heads, q.p_now, ctx->omega, ctx->qa, ctx->w, ws,
-                                          scores + off, hs);
+                                          scores + off, q.head_len, hs);
                 ws += tri::gqa_workspace_bytes(ctx->n_heads, q.len, ctx->group);
             }
             if (e != hipSuccess) return hip_fail(e);
@@ -335,7 +344,7 @@ tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_se
 {
     tri_status st = check_seqs(ctx, seqs, n_seq, false);
     if (st != TRI_OK) return st;
-    if (budget < 1 || window < 0) return TRI_E_INVAL;
+    if (budget < 1 || window < 0 || any_ragged(seqs, n_seq)) return TRI_E_INVAL;
     bool any = false;
     for (int32_t s = 0; s < n_seq; ++s) any = any || fires(seqs[s], budget, window);
     if (!any) return TRI_OK;
@@ -348,7 +357,8 @@ tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_se
         const tri_seq& q = seqs[s];
         if (fires(q, budget, window)) {
             hipError_t e = tri::launch_select(scores + off, q.len, ctx->n_heads, budget,
-                                              kept + (int64_t)s * ctx->n_heads * budget, hs);
+                                              kept + (int64_t)s * ctx->n_heads * budget, budget,
+                                              nullptr, hs);
             if (e != hipSuccess) return hip_fail(e);
         }
         off += (int64_t)ctx->n_heads * q.len;
@@ -362,7 +372,7 @@ tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, in
     tri_status st = check_seqs(ctx, seqs, n_seq, true);
     if (st != TRI_OK) return st;
     if (!supported(ctx->head_dim, dtype)) return TRI_E_UNSUPPORTED;
-    if (budget < 1 || window < 0) return TRI_E_INVAL;
+    if (budget < 1 || window < 0 || any_ragged(seqs, n_seq)) return TRI_E_INVAL;
     bool any = false;
     for (int32_t s = 0; s < n_seq; ++s) any = any || fires(seqs[s], budget, window);
     if (!any) return TRI_OK;
@@ -375,9 +385,84 @@ tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, in
         tri_seq& q = seqs[s];
         if (!fires(q, budget, window)) continue;
         hipError_t e = tri::launch_compact(row_bytes, q.k, q.v, q.pos, q.cap, q.len, ctx->n_heads,
-                                           kept + (int64_t)s * ctx->n_heads * budget, budget, hs);
+                                           kept + (int64_t)s * ctx->n_heads * budget, budget,
+                                           budget, nullptr, nullptr, hs);
         if (e != hipSuccess) return hip_fail(e);
         q.len = budget;
+    }
+    return TRI_OK;
+}
+
+int64_t tri_select_shared_workspace_bytes(const tri_ctx* ctx, int32_t n_seq)
+{
+    if (!ctx || n_seq < 0) return -1;
+    return tri::shared_workspace_bytes(n_seq, ctx->n_layers, ctx->n_kv_heads);
+}
+
+tri_status tri_select_shared(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
+                             const float* scores, int32_t budget, int32_t floor, int32_t window,
+                             int32_t* kept, int32_t* kept_count, void* workspace,
+                             int64_t workspace_bytes, void* stream)
+{
+    tri_status st = check_seqs(ctx, seqs, n_seq, false);
+    if (st != TRI_OK) return st;
+    if (budget < 1 || window < 0 || floor < 0 || floor > budget) return TRI_E_INVAL;
+    if ((int64_t)budget * ctx->n_kv_heads > INT32_MAX) return TRI_E_INVAL;
+    if (ctx->n_kv_heads > 128) return TRI_E_UNSUPPORTED;
+    if (n_seq == 0) return TRI_OK;
+    const int64_t need = tri::shared_workspace_bytes(n_seq, ctx->n_layers, ctx->n_kv_heads);
+    if (!kept || !kept_count || ((uintptr_t)kept & 3u) || ((uintptr_t)kept_count & 3u) ||
+        !workspace || !aligned16(workspace) || workspace_bytes < need)
+        return TRI_E_INVAL;
+    bool any_keys = false;
+    for (int32_t s = 0; s < n_seq; ++s) any_keys = any_keys || seqs[s].len > 0;
+    if (any_keys && (!scores || ((uintptr_t)scores & 3u))) return TRI_E_INVAL;
+    st = check_device(ctx);
+    if (st != TRI_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int64_t total = (int64_t)budget * ctx->n_kv_heads;
+    const int64_t heads = ctx->n_heads;                      // n_layers * n_kv_heads
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    uint4* ws_head = reinterpret_cast<uint4*>(ws);
+    uint4* ws_layer = reinterpret_cast<uint4*>(ws + ((n_seq * heads * 16 + 255) & ~int64_t(255)));
+    int64_t off = 0;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        const tri_seq& q = seqs[s];
+        hipError_t e = tri::launch_select_shared(
+            scores ? scores + off : nullptr, q.len, ctx->n_layers, ctx->n_kv_heads, q.head_len,
+            budget, floor, window, kept + s * heads * total, kept_count + s * heads,
+            ws_head + s * heads, ws_layer + (int64_t)s * ctx->n_layers, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        off += heads * q.len;
+    }
+    return TRI_OK;
+}
+
+tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
+                                 int32_t n_seq, const int32_t* kept, int32_t kept_stride,
+                                 const int32_t* kept_count, void* stream)
+{
+    tri_status st = check_seqs(ctx, seqs, n_seq, true);
+    if (st != TRI_OK) return st;
+    if (!supported(ctx->head_dim, dtype)) return TRI_E_UNSUPPORTED;
+    if (kept_stride < 1) return TRI_E_INVAL;
+    if (n_seq == 0) return TRI_OK;
+    for (int32_t s = 0; s < n_seq; ++s)
+        if (!seqs[s].head_len) return TRI_E_INVAL;
+    if (!kept || !kept_count || ((uintptr_t)kept & 3u) || ((uintptr_t)kept_count & 3u))
+        return TRI_E_INVAL;
+    st = check_device(ctx);
+    if (st != TRI_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int row_bytes = ctx->head_dim * elem_size(dtype);
+    const int64_t heads = ctx->n_heads;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        tri_seq& q = seqs[s];
+        if (q.len == 0) continue;        // no rows: every count is 0 or -1 and head_len stays
+        hipError_t e = tri::launch_compact(row_bytes, q.k, q.v, q.pos, q.cap, q.len, ctx->n_heads,
+                                           kept + s * heads * kept_stride, 0, kept_stride,
+                                           kept_count + s * heads, q.head_len, hs);
+        if (e != hipSuccess) return hip_fail(e);
     }
     return TRI_OK;
 }

@@ -48,7 +48,8 @@ hipError_t launch_distance_curve(int n_q_heads, int group, int head_dim, const d
 // Scores rows [0, len) of n_heads heads of one sequence.
 hipError_t launch_score(tri_dtype dtype, int head_dim, const void* k, int64_t cap, int len,
                         int n_heads, int64_t p_now, const double* omega, const double2* qa,
-                        const float* w, float* scores, hipStream_t stream);
+                        const float* w, float* scores, const int32_t* head_len,
+                        hipStream_t stream);
 
 // GQA (group >= 2): G raw scores per key, per-query-head statistics, then
 // the normalized max into `scores`.  `workspace` holds gqa_workspace_bytes.
@@ -56,14 +57,27 @@ int64_t gqa_workspace_bytes(int64_t n_heads, int64_t len, int group);
 hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void* k, int64_t cap,
                             int len, int n_heads, int64_t p_now, const double* omega,
                             const double2* qa, const float* w, void* workspace, float* scores,
-                            hipStream_t stream);
+                            const int32_t* head_len, hipStream_t stream);
 
 // Top-`budget` of each of n_heads score rows of length n.
+// Heads of `n` keys (stride n; with head_len, head h has its own length up
+// to n and heads of at most `budget` keys get no list); kept lists of head h
+// start at kept + h * kept_stride.
 hipError_t launch_select(const float* scores, int n, int n_heads, int budget, int32_t* kept,
-                         hipStream_t stream);
+                         int kept_stride, const int32_t* head_len, hipStream_t stream);
 
-// In-place stable gather of the first `budget` rows of every head.
+// Head-specific budgets over one sequence's n_layers x n_kv heads.
+int64_t shared_workspace_bytes(int64_t n_seq, int64_t n_layers, int64_t n_kv);
+hipError_t launch_select_shared(const float* scores, int stride, int n_layers, int n_kv,
+                                const int32_t* head_len, int budget, int floor_, int window,
+                                int32_t* kept, int32_t* kept_count, void* ws_head, void* ws_layer,
+                                hipStream_t stream);
+
+// In-place stable gather of the first `budget` rows of every head (kept
+// lists at stride kept_stride); with counts, head h keeps counts[h] rows
+// (-1: untouched) and head_len[h] takes that count.
 hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
-                          int n_heads, const int32_t* kept, int budget, hipStream_t stream);
+                          int n_heads, const int32_t* kept, int budget, int kept_stride,
+                          const int32_t* counts, int32_t* head_len, hipStream_t stream);
 
 }  // namespace tri

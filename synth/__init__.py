@@ -441,6 +441,30 @@ def pruned_positions(seed: int, n: int, start: int = 0, max_gap: int = 7) -> np.
     return start + np.cumsum(rng.integers(1, max_gap + 1, size=n)) - 1
 
 
+def head_lengths(kind: str, n_layers: int, n_kv_heads: int, n: int, seed: int = 0) -> np.ndarray:
+    """Per-head lengths int32 [n_layers][n_kv_heads], each in [0, n], of a
+    ragged cache (the state head-specific budgets leave behind).
+
+    kinds: ``full`` (every head n), ``ragged`` (U{n/2..n}), ``extreme``
+    (each head one of 0, 1, U{1..64}, n, U{0..n}, equally likely).
+    """
+    rng = _np_rng(seed, "head-lengths", kind, n_layers, n_kv_heads, n)
+    shape = (n_layers, n_kv_heads)
+    if kind == "full":
+        out = np.full(shape, n)
+    elif kind == "ragged":
+        out = rng.integers(n // 2, n + 1, size=shape)
+    elif kind == "extreme":
+        pick = rng.integers(0, 5, size=shape)
+        choices = np.stack([np.zeros(shape, dtype=np.int64), np.ones(shape, dtype=np.int64),
+                            rng.integers(1, 65, size=shape), np.full(shape, n),
+                            rng.integers(0, n + 1, size=shape)])
+        out = np.minimum(np.take_along_axis(choices, pick[None], 0)[0], n)
+    else:
+        raise KeyError(kind)
+    return np.ascontiguousarray(out, dtype=np.int32)
+
+
 # --------------------------------------------------------------------------
 # inputs for the select-only and compact-only checks
 

@@ -108,7 +108,29 @@ def test_calls_reject_null_context_and_bad_shapes(lib):
     assert lib.tri_scores_count(None, arr, 1) == -1
     assert lib.tri_score_ws(None, tri.TRI_BF16, arr, 1, None, None, 0, None) == tri.TRI_E_INVAL
     assert lib.tri_score_workspace_bytes(None, arr, 1) == -1
+    assert lib.tri_select_shared_workspace_bytes(None, 1) == -1
+    assert lib.tri_select_shared(None, arr, 1, None, 4, 1, 0, None, None, None, 0,
+                                 None) == tri.TRI_E_INVAL
+    assert lib.tri_compact_kv_counts(None, tri.TRI_BF16, arr, 1, None, 4, None,
+                                     None) == tri.TRI_E_INVAL
     lib.tri_ctx_destroy(None)     # allowed
+
+
+def test_seq_struct_layout_matches_the_header(tmp_path):
+    # the binding's ctypes mirror of tri_seq must agree with the C compiler's
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "tri.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(tri_seq), '
+                   'offsetof(tri_seq, len), offsetof(tri_seq, p_now), '
+                   'offsetof(tri_seq, head_len), sizeof(tri_calib_desc)); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(tri._Seq), tri._Seq.len.offset, tri._Seq.p_now.offset,
+            tri._Seq.head_len.offset, ctypes.sizeof(tri._CalibDesc)]
+    assert got == want
 
 
 def test_offset_sets_match_the_oracle(lib, oracle_lib):
