@@ -20,6 +20,10 @@ Prints one JSON line.  Extra modes:
                      (for rocprofv3 counter runs; see --summarize-pmc)
   --summarize-pmc D  turn rocprofv3 counter CSVs under D into the traffic
                      summary that later runs report as roofline.traffic
+  --shared-floor F   head-specific budgets: the KV heads of a layer share
+                     budget * n_kv_heads slots, each keeping at least its F
+                     best keys (shared select and counted compaction)
+  --calib-stats N, --distance-curve N   time those calls instead
 """
 from __future__ import annotations
 
@@ -102,6 +106,41 @@ def cpu_baseline(cache, n_heads_sample: int):
     return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d heads x %d keys (full score+select+gather per head), %.1f s wall"
                       % (n_heads_sample, sp.heads, n, dt)}
+
+
+def cpu_baseline_shared(cache, n_layers_sample: int, floor: int):
+    """The oracle's shared-budget prune (score every head of a layer, select
+    over the layer, gather) on the first n_layers_sample layers."""
+    import numpy as np
+    import oracle
+
+    orc = oracle.load()
+    sp, cal = cache.spec, cache.calib
+    threads = min(len(os.sched_getaffinity(0)), 64)
+    om = orc.omega(sp.head_dim, sp.rope_theta)
+    n, G = cache.lens[0], sp.group
+    layers = []
+    for l in range(n_layers_sample):
+        heads = []
+        for h in range(sp.n_kv_heads):
+            q = slice(h * G, (h + 1) * G) if G > 1 else h
+            heads.append(dict(
+                K=cache.k[0][l, h, :n].float().cpu().numpy(),
+                V=cache.v[0][l, h, :n].cpu().view(__import__("torch").int16).numpy(),
+                pos=cache.pos[0][l, h, :n].cpu().numpy(), p_now=cache.p_now[0], om=om,
+                offsets=cal.offsets, qc_re=cal.qc_re[l, q], qc_im=cal.qc_im[l, q],
+                q_mean_norm=cal.q_mean_norm[l, q], q_mrl=cal.q_mrl[l, q]))
+        layers.append(heads)
+    t0 = time.perf_counter()
+    for heads in layers:
+        orc.prune_layer_shared(heads, sp.budget * sp.n_kv_heads, floor, sp.window,
+                               threads=min(threads, len(heads)))
+    dt = time.perf_counter() - t0
+    keys = n_layers_sample * sp.n_kv_heads * n
+    return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": min(threads, sp.n_kv_heads),
+            "kind": "oracle",
+            "sample": "%d of %d layers x %d KV heads x %d keys (score, shared select, gather), "
+                      "%.1f s wall" % (n_layers_sample, sp.n_layers, sp.n_kv_heads, n, dt)}
 
 
 def load_traffic(spec):
@@ -247,6 +286,8 @@ def main():
     ap.add_argument("--calib-stats", type=int, default=0, metavar="N_SAMPLES",
                     help="measure tri_calibrate_stats instead: N_SAMPLES pre-RoPE query samples of "
                          "the Qwen3-8B query heads (36 layers x 32 heads x head_dim 128, bf16)")
+    ap.add_argument("--shared-floor", type=int, default=-1, metavar="F",
+                    help="head-specific budgets with a per-head floor of F keys (default: off)")
     ap.add_argument("--distance-curve", type=int, default=0, metavar="N_DELTA",
                     help="measure tri_distance_curve instead: the curves of the 1152 Qwen3-8B "
                          "query heads (36 layers x 8 KV heads x 4) at N_DELTA distances")
@@ -285,16 +326,48 @@ def main():
     H, B, W = spec.heads, spec.budget, spec.window
     total = sum(H * n for n in cache.lens)
     scores = torch.empty(total, dtype=torch.float32, device=dev)
-    kept = torch.empty(spec.n_seq * H * B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    shared = args.shared_floor >= 0
+    F = args.shared_floor
+    if shared:
+        # head-specific budgets: kept lists of up to budget * n_kv_heads per head,
+        # per-head counts and lengths
+        kstride = B * spec.n_kv_heads
+        kept = torch.empty(spec.n_seq * H * kstride, dtype=torch.int32, device=dev)
+        counts = torch.empty(spec.n_seq * H, dtype=torch.int32, device=dev)
+        head_len = [torch.full((spec.n_layers, spec.n_kv_heads), n, dtype=torch.int32, device=dev)
+                    for n in cache.lens]
+        sel_ws = torch.empty(tri.select_shared_workspace_bytes(ctx, spec.n_seq), dtype=torch.uint8,
+                             device=dev)
+        cmp_ws = torch.empty(tri.compact_counts_workspace_bytes(ctx), dtype=torch.uint8, device=dev)
+    else:
+        kept = torch.empty(spec.n_seq * H * B, dtype=torch.int32, device=dev)
 
     def seqs():
-        return [tri.Seq(cache.k[s], cache.v[s], cache.pos[s], cache.lens[s], cache.p_now[s])
+        return [tri.Seq(cache.k[s], cache.v[s], cache.pos[s], cache.lens[s], cache.p_now[s],
+                        head_len[s] if shared else None)
                 for s in range(spec.n_seq)]
 
     # GQA contexts score through a workspace (G raw scores per key)
     ws_bytes = tri.score_workspace_bytes(ctx, seqs())
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+
+    def select(s):
+        if shared:
+            tri.tri_select_shared(ctx, s, scores, B, F, W, kept, counts, sel_ws, stream)
+        else:
+            tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
+
+    def compact(s):
+        if shared:
+            tri.tri_compact_kv_counts(ctx, s, kept, kstride, counts, cmp_ws, stream)
+        else:
+            tri.tri_compact_kv(ctx, s, kept, B, W, stream)
+
+    def step(s):
+        tri.tri_score(ctx, s, scores, stream, ws)
+        select(s)
+        compact(s)
 
     if args.pmc_steps:
         # counter runs: one plain 1 GiB device copy (the scale for the byte
@@ -306,7 +379,7 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         for _ in range(args.pmc_steps):
-            tri.prune_step(ctx, seqs(), B, W, scores, kept, workspace=ws)
+            step(seqs())
         torch.cuda.synchronize()
         print("pmc steps done", file=sys.stderr, flush=True)
         return
@@ -319,12 +392,15 @@ def main():
             k.copy_(k0)
             v.copy_(v0)
             p.copy_(p0)
+        if shared:
+            for hl, n in zip(head_len, cache.lens):
+                hl.fill_(n)
         flush.sum(dtype=torch.int64)      # reads 512 MiB: evicts the cache, leaves it clean
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         restore()
-        tri.prune_step(ctx, seqs(), B, W, scores, kept, workspace=ws)
+        step(seqs())
     torch.cuda.synchronize()
     print("bench: warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -334,9 +410,7 @@ def main():
         s = seqs()
         e = ev[i]
         e[0].record(stream)
-        tri.tri_score(ctx, s, scores, stream, ws)
-        tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
-        tri.tri_compact_kv(ctx, s, kept, B, W, stream)
+        step(s)
         e[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -353,9 +427,9 @@ def main():
         e[0].record(stream)
         tri.tri_score(ctx, s, scores, stream, ws)
         e[1].record(stream)
-        tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
+        select(s)
         e[2].record(stream)
-        tri.tri_compact_kv(ctx, s, kept, B, W, stream)
+        compact(s)
         e[3].record(stream)
     torch.cuda.synchronize()
     t_score = [e[0].elapsed_time(e[1]) for e in pev]
@@ -368,8 +442,10 @@ def main():
     score_gbs = bytes_score / (mean(t_score) * 1e-3) / 1e9
     pass_gbs = bytes_pass / (ms * 1e-3) / 1e9
 
-    # sanity: every head fired and kept exactly B
-    assert all(q.len == B for q in seqs()) or True
+    if shared:
+        # every layer fired: the counts of a layer sum to its shared total
+        c = counts.view(-1, spec.n_kv_heads)
+        assert bool((c.sum(1) == B * spec.n_kv_heads).all()), "a layer did not keep its total"
 
     out = {
         "metric": METRIC,
@@ -386,7 +462,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(spec), "layers": spec.n_layers, "kv_heads": spec.n_kv_heads,
                    "head_dim": spec.head_dim, "cached_keys": list(spec.lengths)[:1] if spec.n_seq == 1 else "ragged",
-                   "budget": B, "window": W, "storage": spec.dtype, "offsets": len(spec.offsets)},
+                   "budget": B, "window": W, "storage": spec.dtype, "offsets": len(spec.offsets),
+                   "budgets": ("shared per layer (budget x %d KV heads), floor %d per head"
+                               % (spec.n_kv_heads, F)) if shared else "uniform per head"},
         "roofline": {"bound": "hbm", "kernel": SCORE_KERNEL if spec.group == 1 else
                      "GQA score phase (gqa_score_kernel, gqa_stats_kernel, gqa_norm_kernel)",
                      "achieved": score_gbs, "peak": HBM_PEAK_GBS,
@@ -404,7 +482,11 @@ def main():
         restore()
         torch.cuda.synchronize()
         print("bench: oracle baseline on %d heads" % args.cpu_heads, file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cache, min(args.cpu_heads, spec.heads))
+        if shared:
+            out["cpu_baseline"] = cpu_baseline_shared(
+                cache, max(1, min(args.cpu_heads // spec.n_kv_heads, spec.n_layers)), F)
+        else:
+            out["cpu_baseline"] = cpu_baseline(cache, min(args.cpu_heads, spec.heads))
     print(json.dumps(out), flush=True)
 
 

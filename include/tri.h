@@ -281,8 +281,9 @@ tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_se
 tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, int32_t n_seq,
                           const int32_t* kept, int32_t budget, int32_t window, void* stream);
 
-/* Device workspace bytes tri_select_shared needs: 16 bytes per layer and KV
- * head of every sequence plus 16 per layer, rounded up.  -1 on bad arguments. */
+/* Device workspace bytes tri_select_shared needs: per sequence, 16 bytes
+ * and two 16 KB histograms per (layer, KV head) plus 192 bytes per layer,
+ * rounded up (9.4 MB for 36 layers x 8 KV heads).  -1 on bad arguments. */
 int64_t tri_select_shared_workspace_bytes(const tri_ctx* ctx, int32_t n_seq);
 
 /*
@@ -332,6 +333,8 @@ tri_status tri_select_shared(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_
  *   kept_count  device int32 [n_seq][n_layers][n_kv_heads], -1 or in
  *               [0, kept_stride]
  *   every sequence needs head_len != NULL
+ *   workspace   device, 4-byte aligned, >= tri_compact_kv_counts_workspace_bytes;
+ *               calls sharing a workspace must not overlap
  * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP.
  * Source: dimensionstp.github.io review, section 3-2 item 5 (evict the rest)
  * and section 6 item 1 (cache compaction); romaanj.github.io review,
@@ -339,7 +342,14 @@ tri_status tri_select_shared(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_
  */
 tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
                                  int32_t n_seq, const int32_t* kept, int32_t kept_stride,
-                                 const int32_t* kept_count, void* stream);
+                                 const int32_t* kept_count, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+/* Device workspace bytes tri_compact_kv_counts needs (it orders the column
+ * parts of the heads' K and V rows there, longest first):
+ * 8 + 32 * n_layers * n_kv_heads, whatever the number of sequences.  -1 on
+ * bad arguments. */
+int64_t tri_compact_kv_counts_workspace_bytes(const tri_ctx* ctx);
 
 #ifdef __cplusplus
 }

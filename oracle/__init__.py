@@ -287,6 +287,37 @@ class Oracle:
         return dict(score=score, kept=kept, K=self.gather_rows(kept, K),
                     V=self.gather_rows(kept, V), pos=self.gather_rows(kept, np.asarray(pos)))
 
+    def prune_layer_shared(self, heads, total: int, floor: int, window: int, threads: int = 1):
+        """One layer's prune step with head-specific budgets: scores every
+        head (``heads``: dicts of K, V, pos, p_now, om, offsets and the head's
+        calibration arrays, [G][d/2] for a GQA group), selects with
+        select_shared over the layer and gathers each head's kept rows.
+        Returns a list of dicts (kept, K, V, pos) per head, or None when the
+        layer does not fire."""
+        def score(j):
+            args = (j["K"], j["pos"], j["p_now"], j["om"], j["offsets"], j["qc_re"], j["qc_im"],
+                    j["q_mean_norm"], j["q_mrl"])
+            if np.ndim(j["qc_re"]) == 2:
+                return self.gqa_head(*args)[2]
+            return self.score_head(*args)[2]
+        if threads > 1:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                sc = list(ex.map(score, heads))
+        else:
+            sc = [score(j) for j in heads]
+        lens = [len(x) for x in sc]
+        stride = max(lens) if lens else 0
+        S = np.full((len(heads), max(stride, 1)), -np.inf)
+        P = np.zeros((len(heads), max(stride, 1)), dtype=np.int64)
+        for h, (x, j) in enumerate(zip(sc, heads)):
+            S[h, :len(x)] = x
+            P[h, :len(x)] = j["pos"]
+        kept = self.select_shared(S, P, lens, total, floor, window)
+        if kept is None:
+            return None
+        return [dict(kept=k, K=self.gather_rows(k, j["K"]), V=self.gather_rows(k, j["V"]),
+                     pos=self.gather_rows(k, j["pos"])) for k, j in zip(kept, heads)]
+
     def prune_heads_parallel(self, jobs, threads: int):
         """Runs ``prune_head(**job)`` for every job on ``threads`` host threads
         (the C calls release the GIL).  Returns the results in job order."""

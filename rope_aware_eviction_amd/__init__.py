@@ -34,7 +34,7 @@ EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last
             "tri_scores_count", "tri_score", "tri_score_workspace_bytes", "tri_score_ws",
             "tri_select_topb", "tri_compact_kv", "tri_calibrate_stats", "tri_distance_curve",
             "tri_offset_set", "tri_select_shared_workspace_bytes", "tri_select_shared",
-            "tri_compact_kv_counts")
+            "tri_compact_kv_counts", "tri_compact_kv_counts_workspace_bytes")
 
 
 class TriError(RuntimeError):
@@ -115,7 +115,10 @@ def library() -> ctypes.CDLL:
                                           vp, ctypes.c_int64, vp]
         lib.tri_compact_kv_counts.restype = ctypes.c_int
         lib.tri_compact_kv_counts.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq),
-                                              ctypes.c_int32, vp, ctypes.c_int32, vp, vp]
+                                              ctypes.c_int32, vp, ctypes.c_int32, vp, vp,
+                                              ctypes.c_int64, vp]
+        lib.tri_compact_kv_counts_workspace_bytes.restype = ctypes.c_int64
+        lib.tri_compact_kv_counts_workspace_bytes.argtypes = [vp]
         _lib = lib
     return _lib
 
@@ -420,10 +423,20 @@ def tri_select_shared(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, b
                                        _stream_ptr(stream)), "tri_select_shared")
 
 
+def compact_counts_workspace_bytes(ctx: Context) -> int:
+    """Device workspace bytes tri_compact_kv_counts needs."""
+    n = library().tri_compact_kv_counts_workspace_bytes(ctx.handle)
+    if n < 0:
+        raise ValueError("bad context")
+    return int(n)
+
+
 def tri_compact_kv_counts(ctx: Context, seqs: Sequence[Seq], kept: torch.Tensor,
-                          kept_stride: int, kept_count: torch.Tensor, stream=None):
+                          kept_stride: int, kept_count: torch.Tensor,
+                          workspace: torch.Tensor, stream=None):
     """Compacts every head with a kept count >= 0 in place and writes the count
-    into the sequence's ``head_len`` (which every sequence needs)."""
+    into the sequence's ``head_len`` (which every sequence needs).
+    ``workspace``: a contiguous GPU tensor of compact_counts_workspace_bytes."""
     arr, dtype = _seq_array(ctx, seqs, need_kv=True)
     if kept.dtype != torch.int32 or not kept.is_cuda or not kept.is_contiguous() \
             or kept.numel() < len(seqs) * ctx.n_heads * kept_stride:
@@ -431,19 +444,24 @@ def tri_compact_kv_counts(ctx: Context, seqs: Sequence[Seq], kept: torch.Tensor,
     if kept_count.dtype != torch.int32 or not kept_count.is_cuda \
             or not kept_count.is_contiguous() or kept_count.numel() < len(seqs) * ctx.n_heads:
         raise ValueError("kept_count must be a contiguous int32 GPU tensor of n_seq*n_heads")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
     _check(library().tri_compact_kv_counts(ctx.handle, dtype, arr, len(seqs), kept.data_ptr(),
                                            int(kept_stride), kept_count.data_ptr(),
-                                           _stream_ptr(stream)), "tri_compact_kv_counts")
+                                           workspace.data_ptr(), nbytes, _stream_ptr(stream)),
+           "tri_compact_kv_counts")
 
 
 def prune_step_shared(ctx: Context, seqs: List[Seq], budget: int, floor: int, window: int,
                       scores: torch.Tensor, kept: torch.Tensor, kept_count: torch.Tensor,
-                      select_workspace: torch.Tensor, stream=None,
-                      workspace: Optional[torch.Tensor] = None):
+                      select_workspace: torch.Tensor, compact_workspace: torch.Tensor,
+                      stream=None, workspace: Optional[torch.Tensor] = None):
     """One prune step with head-specific budgets (score, shared select,
     compaction with per-head counts) on one stream, no host sync.  Every
     sequence needs ``head_len``."""
     tri_score(ctx, seqs, scores, stream, workspace)
     tri_select_shared(ctx, seqs, scores, budget, floor, window, kept, kept_count,
                       select_workspace, stream)
-    tri_compact_kv_counts(ctx, seqs, kept, int(budget) * ctx.n_kv_heads, kept_count, stream)
+    tri_compact_kv_counts(ctx, seqs, kept, int(budget) * ctx.n_kv_heads, kept_count,
+                          compact_workspace, stream)

@@ -24,6 +24,16 @@
 // count them exactly.  The head's kept list is staged in LDS so index reads
 // stay off the memory counter.  Rows are moved with non-temporal accesses:
 // every byte is touched once.
+//
+// Counted lists (head-specific budgets) differ in length from head to head,
+// by up to the whole shared total, so a fixed assignment of streams to
+// workgroups leaves most of them idle while a few move the long streams.
+// There every stream is cut into 128-byte column parts of its rows (a row's
+// column c only ever comes from column c of another row, so the parts are
+// independent and each keeps the hazard rule above on its own), a small
+// kernel orders the parts by size class (largest first) and the workgroups
+// take parts from that order through an atomic counter: the longest parts
+// start first and the short ones fill in.
 #include <algorithm>
 
 #include "tri_internal.h"
@@ -47,7 +57,7 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int ROWB>
+template <int ROWB, int PARTS>
 __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restrict__ k,
                                                          unsigned char* __restrict__ v,
                                                          int32_t* __restrict__ pos, int64_t cap,
@@ -55,25 +65,42 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
                                                          const int32_t* __restrict__ kept,
                                                          int budget, int kept_stride, int n_heads,
                                                          const int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ head_len)
+                                                         int32_t* __restrict__ head_len,
+                                                         uint32_t* __restrict__ queue)
 {
     constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
-    constexpr int kRowsPerStep = kBlock / kChunks;
+    constexpr int kCpp = kChunks / PARTS;               // chunks per column part
+    static_assert(kCpp * PARTS == kChunks, "parts split the row evenly");
+    constexpr int kRowsPerStep = kBlock / kCpp;
     constexpr int kTile = kRowsPerStep * kUnroll;
     constexpr int kPosPerThread = (kTile + kBlock - 1) / kBlock;
     constexpr int kStores = kUnroll + kPosPerThread;    // memory stores per thread per tile
     static_assert(kIdxChunk % kTile == 0, "tiles never straddle an index chunk");
 
     __shared__ int32_t s_idx[kIdxChunk];
+    __shared__ int s_item;
 
-    for (int stream_id = blockIdx.x; stream_id < 2 * n_heads; stream_id += gridDim.x) {
+    // queue: [0] the counter, [1] the number of parts, [2..] their order
+    const int n_items = queue ? (int)queue[1] : 2 * n_heads * PARTS;
+    auto next_item = [&](int item) {
+        if (!queue) return item + (int)gridDim.x;
+        __syncthreads();                                   // every thread has read s_item
+        if (threadIdx.x == 0) s_item = (int)atomicAdd(&queue[0], 1u);
+        __syncthreads();
+        return s_item;
+    };
+    for (int item = queue ? next_item(0) : (int)blockIdx.x; item < n_items; item = next_item(item)) {
+        const int work = queue ? (int)queue[2 + item] : item;
+        const int stream_id = work / PARTS;
+        const int part = work - stream_id * PARTS;
         const int head = stream_id >> 1;
         const bool is_v = (stream_id & 1) != 0;
+        const bool moves_pos = !is_v && part == 0;      // positions travel with K's first part
         // rows this head keeps: `budget`, or its own count (-1: the head is
         // left as it is; head_len takes the new count)
         const int n_keep = counts ? min(counts[head], kept_stride) : budget;
         if (n_keep < 0) continue;
-        if (counts && !is_v && threadIdx.x == 0) head_len[head] = n_keep;
+        if (counts && moves_pos && threadIdx.x == 0) head_len[head] = n_keep;
         unsigned char* rows = (is_v ? v : k) + (size_t)head * (size_t)cap * ROWB;
         int32_t* hpos = pos + (size_t)head * (size_t)cap;
         const int32_t* idx = kept + (size_t)head * (size_t)kept_stride;
@@ -83,8 +110,8 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
             __builtin_amdgcn_make_buffer_rsrc(hpos, 0, len * 4, kBufferWord3);
 
         const int tid = threadIdx.x;
-        const int c = tid % kChunks;
-        const int rs = tid / kChunks;
+        const int c = part * kCpp + tid % kCpp;
+        const int rs = tid / kCpp;
 
         // one tile's data in flight: rows, their destinations, positions
         struct Tile {
@@ -117,7 +144,7 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
                 const int i = q * kBlock + tid;
                 const int r = t0 + i;
                 const int src = (i < kTile && r < n_keep) ? s_idx[r - c0] : r;
-                const bool mv = !is_v && i < kTile && r < n_keep && src != r && (unsigned)src < (unsigned)len;
+                const bool mv = moves_pos && i < kTile && r < n_keep && src != r && (unsigned)src < (unsigned)len;
                 t.pdst[q] = mv ? (uint32_t)r * 4u : kDrop;
                 t.pval[q] = __builtin_amdgcn_raw_buffer_load_b32(rpos, mv ? (uint32_t)src * 4u : kDrop, 0, 0);
             }
@@ -163,10 +190,46 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
     }
 }
 
+// Orders the column parts of the K and V streams of heads with a count >= 0
+// by size class (bit length of the count), largest first, into queue[2..];
+// queue[1] gets their number and the counter queue[0] is cleared.  Work item
+// w is part w % parts of stream w / parts.  One workgroup.
+__global__ __launch_bounds__(kBlock) void order_kernel(const int32_t* __restrict__ counts,
+                                                       int n_heads, int parts,
+                                                       uint32_t* __restrict__ queue)
+{
+    __shared__ uint32_t s_start[33];
+    const int tid = threadIdx.x;
+    if (tid < 33) s_start[tid] = 0u;
+    __syncthreads();
+    auto cls = [](int c) { return c <= 0 ? 0 : 32 - __clz(c); };   // 0..31
+    const int items = 2 * n_heads * parts;
+    for (int i = tid; i < items; i += kBlock) {
+        const int c = counts[(i / parts) >> 1];
+        if (c >= 0) atomicAdd(&s_start[cls(c)], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t at = 0u;
+        for (int b = 31; b >= 0; --b) {
+            const uint32_t m = s_start[b];
+            s_start[b] = at;
+            at += m;
+        }
+        queue[0] = 0u;
+        queue[1] = at;
+    }
+    __syncthreads();
+    for (int i = tid; i < items; i += kBlock) {
+        const int c = counts[(i / parts) >> 1];
+        if (c >= 0) queue[2 + atomicAdd(&s_start[cls(c)], 1u)] = (uint32_t)i;
+    }
+}
+
 template <int ROWB>
 hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_heads,
                   const int32_t* kept, int budget, int kept_stride, const int32_t* counts,
-                  int32_t* head_len, hipStream_t stream)
+                  int32_t* head_len, uint32_t* queue, hipStream_t stream)
 {
     // Each workgroup walks whole K or V streams one after another, at most
     // one workgroup per compute unit, every workgroup the same number of
@@ -185,31 +248,49 @@ hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_he
     }();
     if (cus <= 0) return hipErrorInvalidDevice;
     const int streams = 2 * n_heads;
+    if (queue) {
+        // counted lists: 128-byte column parts, one workgroup per compute
+        // unit taking parts in order
+        constexpr int kParts = ROWB / 128;
+        hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kBlock), 0, stream, counts, n_heads,
+                           kParts, queue);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((compact_kernel<ROWB, kParts>), dim3(std::min(streams * kParts, cus)),
+                           dim3(kBlock), 0, stream, static_cast<unsigned char*>(k),
+                           static_cast<unsigned char*>(v), pos, cap, len, kept, budget,
+                           kept_stride, n_heads, counts, head_len, queue);
+        return hipGetLastError();
+    }
     const int per_block = (streams + cus - 1) / cus;
     const int grid = (streams + per_block - 1) / per_block;
-    hipLaunchKernelGGL(compact_kernel<ROWB>, dim3(grid), dim3(kBlock), 0, stream,
+    hipLaunchKernelGGL((compact_kernel<ROWB, 1>), dim3(grid), dim3(kBlock), 0, stream,
                        static_cast<unsigned char*>(k), static_cast<unsigned char*>(v), pos, cap,
-                       len, kept, budget, kept_stride, n_heads, counts, head_len);
+                       len, kept, budget, kept_stride, n_heads, counts, head_len, queue);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// counter, item count and one entry per column part (at most 512 / 128 per stream)
+int64_t compact_queue_bytes(int64_t n_heads) { return 8 + 4 * 2 * 4 * n_heads; }
+
 hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
                           int n_heads, const int32_t* kept, int budget, int kept_stride,
-                          const int32_t* counts, int32_t* head_len, hipStream_t stream)
+                          const int32_t* counts, int32_t* head_len, uint32_t* queue,
+                          hipStream_t stream)
 {
     if (n_heads <= 0 || kept_stride <= 0 || (!counts && budget <= 0)) return hipSuccess;
-    if (counts && !head_len) return hipErrorInvalidValue;
+    if (counts && (!head_len || !queue)) return hipErrorInvalidValue;
     // buffer offsets are 32-bit: a head's rows must span less than 2 GiB
     if ((int64_t)len * row_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     switch (row_bytes) {
     case 128: return launch<128>(k, v, pos, cap, len, n_heads, kept, budget, kept_stride, counts,
-                                 head_len, stream);
+                                 head_len, queue, stream);
     case 256: return launch<256>(k, v, pos, cap, len, n_heads, kept, budget, kept_stride, counts,
-                                 head_len, stream);
+                                 head_len, queue, stream);
     case 512: return launch<512>(k, v, pos, cap, len, n_heads, kept, budget, kept_stride, counts,
-                                 head_len, stream);
+                                 head_len, queue, stream);
     default: return hipErrorInvalidValue;
     }
 }

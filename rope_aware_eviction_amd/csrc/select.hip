@@ -332,12 +332,18 @@ __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane)
 // either "keep every key >= Tlo" (exactly B keys) or, when equal keys
 // straddle the threshold, "keep keys > T and the first need_eq keys == T in
 // slot order".
-template <int KPT, int NT>
+//
+// RESERVE (head-specific budgets, budget = the per-head floor): instead of
+// the kept list, writes rec[head] = {Th, Sh, min, max}: the kept set as the
+// pointwise test "key > Th, or key == Th and slot <= Sh", and the range of
+// the keys outside it (min > max when there are none).
+template <int KPT, int NT, bool RESERVE = false>
 __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict__ scores,
                                                         int stride, int budget,
                                                         int32_t* __restrict__ kept,
                                                         int kept_stride,
-                                                        const int32_t* __restrict__ head_len)
+                                                        const int32_t* __restrict__ head_len,
+                                                        uint4* __restrict__ rec = nullptr)
 {
     constexpr int kW = NT / 64;
     __shared__ uint32_t hist[1 << kRegDigitBits];
@@ -349,12 +355,16 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
     // keys of this head: all `stride`, or its own length (ragged heads); a
     // head with at most `budget` keys keeps them all and gets no list
     const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
-    if (n <= budget) return;
+    if (n <= budget) {
+        // RESERVE: every key is reserved (Th = 0 lies below every real key)
+        if (RESERVE && threadIdx.x == 0) rec[blockIdx.x] = make_uint4(0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0u);
+        return;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const float* sc = scores + (size_t)blockIdx.x * (size_t)stride;
-    int32_t* out = kept + (size_t)blockIdx.x * (size_t)kept_stride;
+    int32_t* out = RESERVE ? nullptr : kept + (size_t)blockIdx.x * (size_t)kept_stride;
     const int seg0 = wave * (64 * KPT) + lane;     // slot of key[0]
 
     // Slots past the head's end hold key 0, below every real key (ordered_key
@@ -394,6 +404,12 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             kmin = min(kmin, s_wa[x]);
             kmax = max(kmax, s_wb[x]);
         }
+    }
+
+    if (RESERVE && budget == 0) {
+        // nothing reserved (no key lies above kTopKey); the range of all keys
+        if (tid == 0) rec[blockIdx.x] = make_uint4(kTopKey, 0xFFFFFFFFu, kmin, kmax);
+        return;
     }
 
     // Decision: tie = false -> keep key >= T (exactly budget keys);
@@ -479,6 +495,65 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
         }
     }
 
+    if constexpr (RESERVE) {
+        // (Th, Sh): "key >= T" is "key > T - 1"; with a tie, Sh is the slot
+        // of the need_eq-th key equal to T in slot order
+        const unsigned long long below_r = (1ull << lane) - 1ull;
+        uint32_t th = T - 1u;
+        int sh = -1;
+        if (tie) {
+            th = T;
+            uint32_t ceq = 0u;
+#pragma unroll
+            for (int c = 0; c < KPT; ++c) ceq += key[c] == T ? 1u : 0u;
+            ceq = wave_sum(ceq);
+            __syncthreads();
+            if (lane == 0) s_wb[wave] = ceq;
+            if (tid == 0) s_T = 0xFFFFFFFFu;           // Sh + 1 (0: no key equal to T reserved)
+            __syncthreads();
+            uint32_t eq_before = 0u;
+            for (int x = 0; x < wave; ++x) eq_before += s_wb[x];
+#pragma unroll
+            for (int c = 0; c < KPT; ++c) {
+                const bool eq = key[c] == T;
+                const unsigned long long meq = __ballot(eq);
+                const uint32_t my_eq = eq_before + (uint32_t)__popcll(meq & below_r);
+                if (eq && my_eq + 1u == need_eq) s_T = (uint32_t)(seg0 + 64 * c);
+                eq_before += (uint32_t)__popcll(meq);
+            }
+            __syncthreads();
+            sh = need_eq == 0u ? -1 : (int)s_T;
+        }
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+            const uint32_t k = key[c];
+            const bool res = k > th || (k == th && seg0 + 64 * c <= sh);
+            if (k != 0u && !res) {
+                lo = min(lo, k);
+                hi = max(hi, k);
+            }
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        __syncthreads();
+        if (lane == 0) {
+            s_wa[wave] = lo;
+            s_wb[wave] = hi;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int x = 1; x < kW; ++x) {
+                lo = min(lo, s_wa[x]);
+                hi = max(hi, s_wb[x]);
+            }
+            lo = min(lo, s_wa[0]);
+            hi = max(hi, s_wb[0]);
+            rec[blockIdx.x] = make_uint4(th, (uint32_t)sh, lo, hi);
+        }
+        return;
+    }
+
     // ---- output sweeps
     // an opaque copy of T keeps the compiler from carrying the counting
     // sweep's comparison masks over into the writing sweep
@@ -553,15 +628,50 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
 // and the lowest slots among the keys equal to it.  So the reserved set is
 // a pointwise test and needs no flag array.
 //
-// shared_layer_kernel (one workgroup per layer) takes the firing decision,
-// derives (Th, Sh) per head, then runs the offset radix select of the
-// register-resident kernel over the layer's unreserved keys, re-reading
-// them from memory each pass, for rem = total - (reserved keys) slots.  When
-// equal keys straddle the threshold it counts them per head and hands them
-// out in head order.  shared_write_kernel (one workgroup per head) then
-// writes each head's kept list in slot order and its count.
+// The layer-wide threshold is an offset radix select (12-bit digits, as in
+// the register-resident kernel) over the layer's unreserved keys, spread
+// over one workgroup per head so that every compute unit works: each pass
+// is one launch in which every head histograms its own unreserved keys into
+// a histogram of its own in the workspace; the next launch sums the layer's
+// histograms (every workgroup of the layer does the same sum and takes the
+// same decision) and picks the digit.  Three passes cover any key range
+// (12 + 12 + 8 bits).  When equal keys straddle the threshold, the bin
+// counts of the deciding pass give each head's equal keys, handed out in
+// head order.
+//   shared_reserve_kernel  (Th, Sh) and the range of the unreserved keys
+//   shared_pass_kernel     decide the previous pass, histogram the next
+//   shared_write_kernel    decide the last pass, write each head's list
 
 constexpr int kMaxSharedHeads = 128;
+constexpr int kSharedBins = 1 << kRegDigitBits;
+static_assert(kSharedBins % kBlock == 0, "whole bins per thread");
+
+// Selection state of one layer after a pass (identical in every workgroup
+// of the layer; the first head's workgroup stores it for the next launch).
+struct LayerState {
+    uint32_t fired;      // the layer prunes
+    uint32_t done;       // T decided
+    uint32_t base;       // unreserved keys still in play: [base, base + 2^wb)
+    uint32_t wb;
+    uint32_t rem;        // slots still to fill from the keys in play
+    uint32_t T;          // keep unreserved keys >= T (tie: > T, plus need_eq == T)
+    uint32_t tie;
+    uint32_t need_eq;
+    uint32_t res_pass;   // tie: pass that decided it (0: every unreserved key equals T)
+    uint32_t eq_bin;     // tie: bin of T in that pass's histograms
+    uint32_t pad0, pad1, pad2, pad3, pad4, pad5;
+};
+static_assert(sizeof(LayerState) == 64, "layer state layout");
+
+__device__ __forceinline__ int head_rows(const int32_t* head_len, int64_t idx, int stride)
+{
+    return head_len ? max(0, min(head_len[idx], stride)) : stride;
+}
+
+__device__ __forceinline__ bool is_reserved(uint32_t key, int i, uint32_t th, int sh)
+{
+    return key > th || (key == th && i <= sh);
+}
 
 __device__ __forceinline__ int wave_max_i(int v)
 {
@@ -570,271 +680,411 @@ __device__ __forceinline__ int wave_max_i(int v)
     return v;
 }
 
-// Calls f(key, unreserved) for every key of the layer's heads (slot
-// i < s_n[h]), kBatch loads in flight per thread; head h's reserved set is
-// key > s_th[h], or key == s_th[h] and i <= s_sh[h].
-template <typename F>
-__device__ __forceinline__ void for_layer_keys(const float* sc, int stride, int n_kv,
-                                               const int* s_n, const uint32_t* s_th,
-                                               const int* s_sh, int tid, F&& f)
+// Block-wide min / max over uint32 (every thread gets the result).
+__device__ __forceinline__ uint32_t block_min(uint32_t v, uint32_t* s_w, int lane, int wave)
 {
-    for (int h = 0; h < n_kv; ++h) {
-        const int n = s_n[h];
-        const uint32_t th = s_th[h];
-        const int sh = s_sh[h];
-        const float* hs = sc + (size_t)h * (size_t)stride;
-        for (int i0 = tid; i0 < n; i0 += kBlock * kBatch) {
-            float x[kBatch];
+    v = wave_min(v);
+    __syncthreads();
+    if (lane == 0) s_w[wave] = v;
+    __syncthreads();
+    uint32_t r = s_w[0];
+    for (int x = 1; x < kWaves; ++x) r = min(r, s_w[x]);
+    return r;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* s_w, int lane, int wave)
+{
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) s_w[wave] = v;
+    __syncthreads();
+    uint32_t r = s_w[0];
+    for (int x = 1; x < kWaves; ++x) r = max(r, s_w[x]);
+    return r;
+}
+
+// Calls f(i, key) for the n keys of one head, kHeadBatch loads in flight per
+// thread.
+constexpr int kHeadBatch = 8;
+template <typename F>
+__device__ __forceinline__ void for_head_keys(const float* sc, int n, int tid, F&& f)
+{
+    for (int i0 = tid; i0 < n; i0 += kBlock * kHeadBatch) {
+        float x[kHeadBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) x[u] = hs[min(i0 + u * kBlock, n - 1)];
+        for (int u = 0; u < kHeadBatch; ++u) x[u] = sc[min(i0 + u * kBlock, n - 1)];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int i = i0 + u * kBlock;
-                const uint32_t key = ordered_key(x[u]);
-                if (i < n) f(key, !(key > th || (key == th && i <= sh)));
-            }
+        for (int u = 0; u < kHeadBatch; ++u) {
+            const int i = i0 + u * kBlock;
+            if (i < n) f(i, ordered_key(x[u]));
         }
     }
 }
 
-__global__ __launch_bounds__(kBlock) void shared_layer_kernel(
-    const float* __restrict__ scores, int stride, int n_kv, const int32_t* __restrict__ head_len,
-    int total, int floor_, int window, const int32_t* __restrict__ kept,
-    uint4* __restrict__ ws_head, uint4* __restrict__ ws_layer)
+// One workgroup per head: (Th, Sh) from the head's reserved list and the
+// key range of its unreserved keys -> rec[head] = {Th, Sh, min, max}
+// (min > max when nothing is unreserved).
+__global__ __launch_bounds__(kBlock) void shared_reserve_kernel(
+    const float* __restrict__ scores, int stride, const int32_t* __restrict__ head_len,
+    int total, int floor_, const int32_t* __restrict__ kept, uint4* __restrict__ rec)
 {
-    __shared__ uint32_t hist[1 << kRegDigitBits];
-    __shared__ int s_n[kMaxSharedHeads];
-    __shared__ uint32_t s_Th[kMaxSharedHeads];
-    __shared__ int s_Sh[kMaxSharedHeads];
-    __shared__ uint32_t s_eq[kMaxSharedHeads];
-    __shared__ uint32_t s_wa[kWaves], s_wb[kWaves], s_run[kWaves];
-    __shared__ uint32_t s_digit, s_above, s_inbin;
-
-    const int layer = blockIdx.x;
+    __shared__ uint32_t s_w[kWaves];
+    const int head = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const float* sc = scores + (size_t)layer * (size_t)n_kv * (size_t)stride;
-    const int32_t* lists = kept + (size_t)layer * (size_t)n_kv * (size_t)total;
-    uint4* wh = ws_head + (size_t)layer * (size_t)n_kv;
-
-    for (int h = tid; h < n_kv; h += kBlock) {
-        s_n[h] = head_len ? max(0, min(head_len[(size_t)layer * n_kv + h], stride)) : stride;
-        s_eq[h] = 0u;
+    const int n = head_rows(head_len, head, stride);
+    const float* sc = scores + (size_t)head * (size_t)stride;
+    uint32_t th;
+    int sh;
+    if (floor_ == 0) {
+        th = kTopKey;                     // no key is above it: nothing reserved
+        sh = -1;
+    } else if (n <= floor_) {
+        th = 0u;                          // every real key is above it: all reserved
+        sh = -1;
+    } else {
+        const int32_t* l = kept + (size_t)head * (size_t)total;
+        uint32_t mn = 0xFFFFFFFFu;
+        for (int j = tid; j < floor_; j += kBlock) mn = min(mn, ordered_key(sc[min(max(l[j], 0), n - 1)]));
+        th = block_min(mn, s_w, lane, wave);
+        int mx = -1;
+        for (int j = tid; j < floor_; j += kBlock) {
+            const int slot = min(max(l[j], 0), n - 1);
+            if (ordered_key(sc[slot]) == th) mx = max(mx, slot);
+        }
+        sh = (int)block_max((uint32_t)(mx + 1), s_w, lane, wave) - 1;
     }
-    __syncthreads();
-    int64_t all = 0;
-    for (int h = 0; h < n_kv; ++h) all += s_n[h];
-    if (all <= (int64_t)total + (int64_t)n_kv * window) {      // the layer keeps every key
-        if (tid == 0) ws_layer[layer] = make_uint4(0u, 0u, 0u, 0u);
-        return;
-    }
-
-    // reserved sets: (Th, Sh) per head from its reserved list
-    for (int h = wave; h < n_kv; h += kWaves) {
-        const int n = s_n[h];
-        uint32_t th;
-        int sh;
-        if (floor_ == 0) {
-            th = kTopKey;                 // no key is above it: nothing reserved
-            sh = -1;
-        } else if (n <= floor_) {
-            th = 0u;                      // every real key is above it: all reserved
-            sh = -1;
-        } else {
-            const int32_t* l = lists + (size_t)h * (size_t)total;
-            const float* hs = sc + (size_t)h * (size_t)stride;
-            uint32_t mn = 0xFFFFFFFFu;
-            for (int j = lane; j < floor_; j += 64)
-                mn = min(mn, ordered_key(hs[min(max(l[j], 0), n - 1)]));
-            mn = wave_min(mn);
-            int mx = -1;
-            for (int j = lane; j < floor_; j += 64) {
-                const int slot = min(max(l[j], 0), n - 1);
-                if (ordered_key(hs[slot]) == mn) mx = max(mx, slot);
-            }
-            th = mn;
-            sh = wave_max_i(mx);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for_head_keys(sc, n, tid, [&](int i, uint32_t key) {
+        if (!is_reserved(key, i, th, sh)) {
+            lo = min(lo, key);
+            hi = max(hi, key);
         }
-        if (lane == 0) {
-            s_Th[h] = th;
-            s_Sh[h] = sh;
-        }
-    }
-    __syncthreads();
-    int64_t reserved = 0;
-    for (int h = 0; h < n_kv; ++h) reserved += min(s_n[h], floor_);
-    uint32_t rem = (uint32_t)((int64_t)total - reserved);   // floor * n_kv <= total
-
-    uint32_t T = kTopKey, need_eq = 0u;
-    bool tie = false;
-    if (rem > 0u) {
-        // key range of the unreserved keys (more than rem of them: the layer fires)
-        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-        for_layer_keys(sc, stride, n_kv, s_n, s_Th, s_Sh, tid, [&](uint32_t key, bool unres) {
-            if (unres) {
-                lo = min(lo, key);
-                hi = max(hi, key);
-            }
-        });
-        lo = wave_min(lo);
-        hi = wave_max(hi);
-        if (lane == 0) {
-            s_wa[wave] = lo;
-            s_wb[wave] = hi;
-        }
-        __syncthreads();
-        uint32_t kmin = s_wa[0], kmax = s_wb[0];
-        for (int x = 1; x < kWaves; ++x) {
-            kmin = min(kmin, s_wa[x]);
-            kmax = max(kmax, s_wb[x]);
-        }
-        if (kmin == kmax) {
-            T = kmin;
-            need_eq = rem;
-            tie = true;
-        } else {
-            uint32_t base = kmin;
-            int wb = 32 - __clz((int)(kmax - kmin));    // live keys: [base, base + 2^wb)
-            for (;;) {
-                const int nb = min(kRegDigitBits, wb);
-                const int shift = wb - nb;
-                const uint32_t nbins = 1u << nb;
-                const uint32_t span = wb >= 32 ? 0xFFFFFFFFu : (1u << wb) - 1u;
-                __syncthreads();                         // previous readers of hist / s_*
-                for (uint32_t b = tid; b < nbins; b += kBlock) hist[b] = 0u;
-                __syncthreads();
-                for_layer_keys(sc, stride, n_kv, s_n, s_Th, s_Sh, tid, [&](uint32_t key, bool unres) {
-                    const uint32_t off = key - base;
-                    if (off <= span && unres) atomicAdd(&hist[off >> shift], 1u);
-                });
-                __syncthreads();
-                find_digit<kBlock>(hist, nbins, rem, tid, lane, wave, s_run, &s_digit, &s_above,
-                                   &s_inbin);
-                __syncthreads();
-                const uint32_t d = s_digit & (nbins - 1u);
-                const uint32_t in_bin = s_inbin;
-                rem -= s_above;
-                base += d << shift;
-                wb = shift;
-                if (rem == in_bin) {                     // the whole bin is kept
-                    T = base;
-                    tie = false;
-                    break;
-                }
-                if (wb == 0) {                           // one key value straddles
-                    T = base;
-                    need_eq = rem;
-                    tie = true;
-                    break;
-                }
-            }
-        }
-        if (tie) {
-            // equal keys per head, handed out in head order
-            for (int h = 0; h < n_kv; ++h) {
-                const int n = s_n[h];
-                const uint32_t th = s_Th[h];
-                const int sh = s_Sh[h];
-                const float* hs = sc + (size_t)h * (size_t)stride;
-                uint32_t c = 0u;
-                for (int i = tid; i < n; i += kBlock) {
-                    const uint32_t key = ordered_key(hs[i]);
-                    c += (key == T && !(key > th || (key == th && i <= sh))) ? 1u : 0u;
-                }
-                c = wave_sum(c);
-                if (lane == 0 && c) atomicAdd(&s_eq[h], c);
-            }
-            __syncthreads();
-        }
-    }
-    if (tid == 0) {
-        uint32_t left = need_eq;
-        for (int h = 0; h < n_kv; ++h) {
-            const uint32_t take = tie ? min(s_eq[h], left) : 0u;
-            left -= take;
-            wh[h] = make_uint4(s_Th[h], (uint32_t)s_Sh[h], take, 0u);
-        }
-        ws_layer[layer] = make_uint4(T, tie ? 1u : 0u, 1u, 0u);
-    }
+    });
+    lo = block_min(lo, s_w, lane, wave);
+    hi = block_max(hi, s_w, lane, wave);
+    if (tid == 0) rec[head] = make_uint4(th, (uint32_t)sh, lo, hi);
 }
 
-// One workgroup per head: the kept list of the head in slot order and its
-// count (-1 when the layer does not fire).  Wave w owns slots
-// [w*seg, (w+1)*seg); a counting sweep gives every wave its offset.
+// State after the reserve step: the firing rule, the slots left and the
+// range of the layer's unreserved keys.
+__device__ __forceinline__ LayerState layer_init(const uint4* __restrict__ rec_l,
+                                                 const int32_t* __restrict__ hl_l, int stride,
+                                                 int n_kv, int total, int floor_, int window)
+{
+    LayerState S = {};
+    int64_t all = 0, reserved = 0;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int h = 0; h < n_kv; ++h) {
+        const int n = head_rows(hl_l, h, stride);
+        all += n;
+        reserved += min(n, floor_);
+        const uint4 r = rec_l[h];
+        lo = min(lo, r.z);
+        hi = max(hi, r.w);
+    }
+    S.fired = all > (int64_t)total + (int64_t)n_kv * window ? 1u : 0u;
+    if (!S.fired) {
+        S.done = 1u;
+        return S;
+    }
+    S.rem = (uint32_t)((int64_t)total - reserved);        // floor * n_kv <= total
+    if (S.rem == 0u) {                                     // the reserved keys fill the layer
+        S.done = 1u;
+        S.T = kTopKey;
+    } else if (lo == hi) {                                 // one unreserved key value
+        S.done = 1u;
+        S.T = lo;
+        S.tie = 1u;
+        S.need_eq = S.rem;
+        S.res_pass = 0u;
+    } else {
+        S.base = lo;
+        S.wb = (uint32_t)(32 - __clz((int)(hi - lo)));
+    }
+    return S;
+}
+
+// Decides pass `pass` from the layer's per-head histograms (hist_l: n_kv
+// rows of kSharedBins).  Every thread of the workgroup calls it.
+__device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
+                                              const uint32_t* __restrict__ hist_l, int n_kv,
+                                              uint32_t* lhist, uint32_t* s_run, uint32_t* s_dig,
+                                              int tid, int lane, int wave)
+{
+    const int nb = min(kRegDigitBits, (int)S.wb);
+    const int shift = (int)S.wb - nb;
+    const uint32_t nbins = 1u << nb;
+    // thread t sums bins t + j*kBlock over the heads, eight heads' loads in
+    // flight at a time (the sums are latency-bound, not bandwidth-bound)
+    constexpr int kBinsPerThread = kSharedBins / kBlock;
+    uint32_t acc[kBinsPerThread];
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) acc[j] = 0u;
+    int h = 0;
+    for (; h + 8 <= n_kv; h += 8) {
+        uint32_t v[8][kBinsPerThread];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < kBinsPerThread; ++j) {
+                const uint32_t b = (uint32_t)(tid + j * kBlock);
+                v[u][j] = b < nbins ? hist_l[(size_t)(h + u) * kSharedBins + b] : 0u;
+            }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < kBinsPerThread; ++j) acc[j] += v[u][j];
+    }
+    for (; h < n_kv; ++h)
+#pragma unroll
+        for (int j = 0; j < kBinsPerThread; ++j) {
+            const uint32_t b = (uint32_t)(tid + j * kBlock);
+            acc[j] += b < nbins ? hist_l[(size_t)h * kSharedBins + b] : 0u;
+        }
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) {
+        const uint32_t b = (uint32_t)(tid + j * kBlock);
+        if (b < nbins) lhist[b] = acc[j];
+    }
+    __syncthreads();
+    find_digit<kBlock>(lhist, nbins, S.rem, tid, lane, wave, s_run, &s_dig[0], &s_dig[1],
+                       &s_dig[2]);
+    __syncthreads();
+    const uint32_t d = s_dig[0] & (nbins - 1u);
+    const uint32_t in_bin = s_dig[2];
+    S.rem -= s_dig[1];
+    S.base += d << shift;
+    S.wb = (uint32_t)shift;
+    // the whole bin is kept, or the bin is one key value that straddles
+    // (selects rather than branches keep the state in registers)
+    const bool whole = S.rem == in_bin;
+    const bool straddle = !whole && shift == 0;
+    S.done = (whole || straddle) ? 1u : 0u;
+    S.T = (whole || straddle) ? S.base : S.T;
+    S.tie = straddle ? 1u : S.tie;
+    S.need_eq = straddle ? S.rem : S.need_eq;
+    S.res_pass = straddle ? pass : S.res_pass;
+    S.eq_bin = straddle ? d : S.eq_bin;
+    __syncthreads();                     // lhist and s_dig are reused
+}
+
+// Launch `pass` (1..3): decide pass-1 (or set up the layer when pass == 1),
+// then histogram this head's unreserved keys for pass `pass`.
+__global__ __launch_bounds__(kBlock) void shared_pass_kernel(
+    int pass, const float* __restrict__ scores, int stride, int n_layers, int n_kv,
+    const int32_t* __restrict__ head_len, int total, int floor_, int window,
+    const uint4* __restrict__ rec, uint32_t* __restrict__ hist, LayerState* __restrict__ state)
+{
+    __shared__ uint32_t lhist[kSharedBins];
+    __shared__ uint32_t s_run[kWaves], s_dig[3];
+    const int head = blockIdx.x;
+    const int layer = head / n_kv;
+    const int h = head - layer * n_kv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const size_t heads = (size_t)n_layers * (size_t)n_kv;
+    LayerState S;
+    if (pass == 1) {
+        S = layer_init(rec + (size_t)layer * n_kv, head_len ? head_len + (size_t)layer * n_kv : nullptr,
+                       stride, n_kv, total, floor_, window);
+    } else {
+        S = state[(size_t)(pass - 2) * n_layers + layer];
+        if (!S.done)
+            layer_resolve(S, (uint32_t)(pass - 1),
+                          hist + (size_t)((pass - 2) & 1) * heads * kSharedBins +
+                              (size_t)layer * n_kv * kSharedBins,
+                          n_kv, lhist, s_run, s_dig, tid, lane, wave);
+    }
+    if (h == 0 && tid == 0) state[(size_t)(pass - 1) * n_layers + layer] = S;
+    if (S.done) return;
+
+    const int nb = min(kRegDigitBits, (int)S.wb);
+    const int shift = (int)S.wb - nb;
+    const uint32_t nbins = 1u << nb;
+    const uint32_t span = S.wb >= 32u ? 0xFFFFFFFFu : (1u << S.wb) - 1u;
+    for (uint32_t b = tid; b < nbins; b += kBlock) lhist[b] = 0u;
+    __syncthreads();
+    const uint4 r = rec[head];
+    const uint32_t th = r.x;
+    const int sh = (int)r.y;
+    const uint32_t base = S.base;
+    const int n = head_rows(head_len, head, stride);
+    for_head_keys(scores + (size_t)head * (size_t)stride, n, tid, [&](int i, uint32_t key) {
+        const uint32_t off = key - base;
+        if (off <= span && !is_reserved(key, i, th, sh)) atomicAdd(&lhist[off >> shift], 1u);
+    });
+    __syncthreads();
+    uint32_t* out = hist + (size_t)((pass - 1) & 1) * heads * kSharedBins + (size_t)head * kSharedBins;
+    for (uint32_t b = tid; b < nbins; b += kBlock) out[b] = lhist[b];
+}
+
+// One workgroup per head: decide the last pass if needed, then the kept list
+// of the head in slot order and its count (-1 when the layer does not fire).
+// KPT > 0: the head's keys sit in registers as in the register-resident
+// selection (lane l of wave w holds slots w*64*KPT + c*64 + l); KPT == 0:
+// wave w owns slots [w*seg, (w+1)*seg) and reads them from memory twice.  A
+// counting sweep gives every wave its offset in the list.
+template <int KPT>
 __global__ __launch_bounds__(kBlock) void shared_write_kernel(
-    const float* __restrict__ scores, int stride, int n_kv, const int32_t* __restrict__ head_len,
-    int total, const uint4* __restrict__ ws_head, const uint4* __restrict__ ws_layer,
+    const float* __restrict__ scores, int stride, int n_layers, int n_kv,
+    const int32_t* __restrict__ head_len, int total, int floor_, const uint4* __restrict__ rec,
+    const uint32_t* __restrict__ hist, const LayerState* __restrict__ state,
     int32_t* __restrict__ kept, int32_t* __restrict__ kept_count)
 {
+    __shared__ uint32_t lhist[kSharedBins];
+    __shared__ uint32_t s_run[kWaves], s_dig[3];
     __shared__ uint32_t s_wgt[kWaves], s_weq[kWaves];
     const int lh = blockIdx.x;
     const int layer = lh / n_kv;
+    const int hh = lh - layer * n_kv;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const uint4 lw = ws_layer[layer];
-    if (lw.z == 0u) {
+    const size_t heads = (size_t)n_layers * (size_t)n_kv;
+    LayerState S = state[(size_t)2 * n_layers + layer];
+    if (!S.done)
+        layer_resolve(S, 3u, hist + (size_t)layer * n_kv * kSharedBins, n_kv, lhist, s_run, s_dig,
+                      tid, lane, wave);
+    if (!S.fired) {
         if (tid == 0) kept_count[lh] = -1;
         return;
     }
-    const uint4 hw = ws_head[lh];
-    const uint32_t th = hw.x;
-    const int sh = (int)hw.y;
-    const uint32_t take = hw.z;
-    const uint32_t T = lw.x;
-    const bool tie = lw.y != 0u;
-    const int n = head_len ? max(0, min(head_len[lh], stride)) : stride;
+    // equal keys taken by this head: what is left after the lower heads
+    uint32_t take = 0u;
+    if (S.tie) {
+        const int32_t* hl_l = head_len ? head_len + (size_t)layer * n_kv : nullptr;
+        const uint32_t* bins = hist + (size_t)((S.res_pass - 1u) & 1u) * heads * kSharedBins +
+                               (size_t)layer * n_kv * kSharedBins + S.eq_bin;
+        uint32_t left = S.need_eq;
+        for (int h = 0; h <= hh; ++h) {
+            uint32_t eq;
+            if (S.res_pass == 0u) {
+                const int n = head_rows(hl_l, h, stride);
+                eq = (uint32_t)(n - min(n, floor_));
+            } else {
+                eq = bins[(size_t)h * kSharedBins];
+            }
+            const uint32_t t = min(eq, left);
+            if (h == hh) take = t;
+            left -= t;
+        }
+    }
+    const uint4 r = rec[lh];
+    const uint32_t th = r.x;
+    const int sh = (int)r.y;
+    const uint32_t T = S.T;
+    const bool tie = S.tie != 0u;
+    const int n = head_rows(head_len, lh, stride);
     const float* sc = scores + (size_t)lh * (size_t)stride;
     int32_t* out = kept + (size_t)lh * (size_t)total;
+    const unsigned long long below = (1ull << lane) - 1ull;
 
     // gt: kept outright (reserved, or above the layer threshold);
-    // eq: unreserved and equal to T when equal keys straddle it
-    auto classify = [&](int i, bool& gt, bool& eq) {
-        const uint32_t key = i < n ? ordered_key(sc[i]) : 0u;
-        const bool res = i < n && (key > th || (key == th && i <= sh));
-        gt = res || (i < n && (tie ? key > T : key >= T));
-        eq = !res && tie && i < n && key == T;
+    // eq: unreserved and equal to T when equal keys straddle it.  Key 0
+    // marks a slot past the head's end.
+    auto classify = [&](int i, uint32_t key, bool& gt, bool& eq) {
+        const bool real = key != 0u;
+        const bool res = real && is_reserved(key, i, th, sh);
+        gt = res || (real && (tie ? key > T : key >= T));
+        eq = !res && tie && real && key == T;
     };
-    const int seg = ((n + kWaves - 1) / kWaves + 63) & ~63;
-    const int s0 = wave * seg;
-    const int s1 = min(n, s0 + seg);
-    uint32_t cgt = 0u, ceq = 0u;
-    for (int i0 = s0; i0 < s1; i0 += 64) {
-        bool gt, eq;
-        classify(i0 + lane < s1 ? i0 + lane : n, gt, eq);
-        cgt += (uint32_t)__popcll(__ballot(gt));
-        ceq += (uint32_t)__popcll(__ballot(eq));
-    }
-    if (lane == 0) {
-        s_wgt[wave] = cgt;
-        s_weq[wave] = ceq;
-    }
-    __syncthreads();
-    uint32_t gt_before = 0u, eq_before = 0u, gt_all = 0u, eq_all = 0u;
-    for (int x = 0; x < kWaves; ++x) {
-        if (x < wave) {
-            gt_before += s_wgt[x];
-            eq_before += s_weq[x];
+
+    if constexpr (KPT > 0) {
+        static_assert(KPT <= 32, "one bit per key in a 32-bit mask");
+        const int seg0 = wave * (64 * KPT) + lane;
+        // classify every key once; bit c of gtb / eqb is key c's class
+        uint32_t gtb = 0u, eqb = 0u;
+        {
+            const __amdgpu_buffer_rsrc_t rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void*)sc, 0, n * 4, kBufferWord3);
+            uint32_t x[KPT];
+#pragma unroll
+            for (int c = 0; c < KPT; ++c)
+                x[c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (seg0 + 64 * c) * 4, 0, 0);
+#pragma unroll
+            for (int c = 0; c < KPT; ++c) {
+                const uint32_t key = seg0 + 64 * c < n ? ordered_key(__uint_as_float(x[c])) : 0u;
+                bool gt, eq;
+                classify(seg0 + 64 * c, key, gt, eq);
+                gtb |= (gt ? 1u : 0u) << c;
+                eqb |= (eq ? 1u : 0u) << c;
+            }
         }
-        gt_all += s_wgt[x];
-        eq_all += s_weq[x];
+        uint32_t cgt = (uint32_t)__popc(gtb), ceq = (uint32_t)__popc(eqb);
+        cgt = wave_sum(cgt);
+        ceq = wave_sum(ceq);
+        if (lane == 0) {
+            s_wgt[wave] = cgt;
+            s_weq[wave] = ceq;
+        }
+        __syncthreads();
+        uint32_t gt_before = 0u, eq_before = 0u, gt_all = 0u, eq_all = 0u;
+        for (int x = 0; x < kWaves; ++x) {
+            if (x < wave) {
+                gt_before += s_wgt[x];
+                eq_before += s_weq[x];
+            }
+            gt_all += s_wgt[x];
+            eq_all += s_weq[x];
+        }
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+            const bool gt = (gtb >> c) & 1u;
+            const bool eq = (eqb >> c) & 1u;
+            const unsigned long long mgt = __ballot(gt);
+            const unsigned long long meq = __ballot(eq);
+            const uint32_t my_gt = gt_before + (uint32_t)__popcll(mgt & below);
+            const uint32_t my_eq = eq_before + (uint32_t)__popcll(meq & below);
+            const uint32_t at = my_gt + min(my_eq, take);
+            if ((gt || (eq && my_eq < take)) && at < (uint32_t)total) out[at] = seg0 + 64 * c;
+            gt_before += (uint32_t)__popcll(mgt);
+            eq_before += (uint32_t)__popcll(meq);
+        }
+        if (tid == 0) kept_count[lh] = (int32_t)min(gt_all + min(eq_all, take), (uint32_t)total);
+    } else {
+        const int seg = ((n + kWaves - 1) / kWaves + 63) & ~63;
+        const int s0 = wave * seg;
+        const int s1 = min(n, s0 + seg);
+        auto key_at = [&](int i) { return i < s1 ? ordered_key(sc[i]) : 0u; };
+        uint32_t cgt = 0u, ceq = 0u;
+        for (int i0 = s0; i0 < s1; i0 += 64) {
+            bool gt, eq;
+            classify(i0 + lane, key_at(i0 + lane), gt, eq);
+            cgt += (uint32_t)__popcll(__ballot(gt));
+            ceq += (uint32_t)__popcll(__ballot(eq));
+        }
+        if (lane == 0) {
+            s_wgt[wave] = cgt;
+            s_weq[wave] = ceq;
+        }
+        __syncthreads();
+        uint32_t gt_before = 0u, eq_before = 0u, gt_all = 0u, eq_all = 0u;
+        for (int x = 0; x < kWaves; ++x) {
+            if (x < wave) {
+                gt_before += s_wgt[x];
+                eq_before += s_weq[x];
+            }
+            gt_all += s_wgt[x];
+            eq_all += s_weq[x];
+        }
+        for (int i0 = s0; i0 < s1; i0 += 64) {
+            const int i = i0 + lane;
+            bool gt, eq;
+            classify(i, key_at(i), gt, eq);
+            const unsigned long long mgt = __ballot(gt);
+            const unsigned long long meq = __ballot(eq);
+            const uint32_t my_gt = gt_before + (uint32_t)__popcll(mgt & below);
+            const uint32_t my_eq = eq_before + (uint32_t)__popcll(meq & below);
+            const uint32_t at = my_gt + min(my_eq, take);
+            if ((gt || (eq && my_eq < take)) && at < (uint32_t)total) out[at] = i;
+            gt_before += (uint32_t)__popcll(mgt);
+            eq_before += (uint32_t)__popcll(meq);
+        }
+        if (tid == 0) kept_count[lh] = (int32_t)min(gt_all + min(eq_all, take), (uint32_t)total);
     }
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int i0 = s0; i0 < s1; i0 += 64) {
-        const int i = i0 + lane;
-        bool gt, eq;
-        classify(i < s1 ? i : n, gt, eq);
-        const unsigned long long mgt = __ballot(gt);
-        const unsigned long long meq = __ballot(eq);
-        const uint32_t my_gt = gt_before + (uint32_t)__popcll(mgt & below);
-        const uint32_t my_eq = eq_before + (uint32_t)__popcll(meq & below);
-        const uint32_t at = my_gt + min(my_eq, take);
-        if ((gt || (eq && my_eq < take)) && at < (uint32_t)total) out[at] = i;
-        gt_before += (uint32_t)__popcll(mgt);
-        eq_before += (uint32_t)__popcll(meq);
-    }
-    if (tid == 0) kept_count[lh] = (int32_t)min(gt_all + min(eq_all, take), (uint32_t)total);
 }
 
 }  // namespace
@@ -873,36 +1123,72 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
 }
 
 
+// Workspace of one sequence: per-head records, two banks of per-head
+// histograms, the layer states of three passes.
 int64_t shared_workspace_bytes(int64_t n_seq, int64_t n_layers, int64_t n_kv)
 {
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
-    return up(n_seq * n_layers * n_kv * 16) + up(n_seq * n_layers * 16);
+    const int64_t heads = n_layers * n_kv;
+    return n_seq * (up(heads * 16) + up(2 * heads * kSharedBins * 4) +
+                    up(3 * n_layers * (int64_t)sizeof(LayerState)));
 }
 
 hipError_t launch_select_shared(const float* scores, int stride, int n_layers, int n_kv,
                                 const int32_t* head_len, int budget, int floor_, int window,
-                                int32_t* kept, int32_t* kept_count, void* ws_head, void* ws_layer,
+                                int32_t* kept, int32_t* kept_count, void* workspace,
                                 hipStream_t stream)
 {
     if (n_layers <= 0 || n_kv <= 0) return hipSuccess;
     if (n_kv > kMaxSharedHeads) return hipErrorInvalidValue;
     const int64_t total = (int64_t)budget * n_kv;
-    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (floor_ > 0 && stride > floor_) {
-        // each head's reserved list, into the head's kept row (stride total)
-        hipError_t e = launch_select(scores, stride, n_layers * n_kv, floor_, kept, (int)total,
-                                     head_len, stream);
+    const int64_t heads = (int64_t)n_layers * n_kv;
+    if (total > 0x7FFFFFFF || heads > 0x7FFFFFFF) return hipErrorInvalidValue;
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    uint4* rec = reinterpret_cast<uint4*>(ws);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + up(heads * 16));
+    LayerState* state = reinterpret_cast<LayerState*>(ws + up(heads * 16) +
+                                                      up(2 * heads * kSharedBins * 4));
+    const dim3 grid((unsigned)heads), block(kBlock);
+    hipError_t e = hipSuccess;
+    if (stride <= kBlock * 32) {
+        // register-resident: the floor selection writes the reserved sets directly
+#define TRI_RESERVE(KPT)                                                                          \
+        hipLaunchKernelGGL((select_reg_kernel<KPT, kBlock, true>), grid, block, 0, stream, scores, \
+                           stride, floor_, nullptr, 0, head_len, rec)
+        if (stride <= kBlock * 8) TRI_RESERVE(8);
+        else if (stride <= kBlock * 16) TRI_RESERVE(16);
+        else TRI_RESERVE(32);
+#undef TRI_RESERVE
+    } else {
+        if (floor_ > 0 && stride > floor_) {
+            // each head's reserved list, into the head's kept row (stride total)
+            e = launch_select(scores, stride, (int)heads, floor_, kept, (int)total, head_len,
+                              stream);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(shared_reserve_kernel, grid, block, 0, stream, scores, stride,
+                           head_len, (int)total, floor_, kept, rec);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    for (int pass = 1; pass <= 3; ++pass) {
+        hipLaunchKernelGGL(shared_pass_kernel, grid, block, 0, stream, pass, scores, stride,
+                           n_layers, n_kv, head_len, (int)total, floor_, window,
+                           static_cast<const uint4*>(rec), hist, state);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(shared_layer_kernel, dim3(n_layers), dim3(kBlock), 0, stream, scores,
-                       stride, n_kv, head_len, (int)total, floor_, window, kept,
-                       static_cast<uint4*>(ws_head), static_cast<uint4*>(ws_layer));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(shared_write_kernel, dim3(n_layers * n_kv), dim3(kBlock), 0, stream,
-                       scores, stride, n_kv, head_len, (int)total,
-                       static_cast<const uint4*>(ws_head), static_cast<const uint4*>(ws_layer),
-                       kept, kept_count);
+#define TRI_WRITE(KPT)                                                                            \
+    hipLaunchKernelGGL(shared_write_kernel<KPT>, grid, block, 0, stream, scores, stride,           \
+                       n_layers, n_kv, head_len, (int)total, floor_,                               \
+                       static_cast<const uint4*>(rec), static_cast<const uint32_t*>(hist),         \
+                       static_cast<const LayerState*>(state), kept, kept_count)
+    if (stride <= kBlock * 8) TRI_WRITE(8);
+    else if (stride <= kBlock * 16) TRI_WRITE(16);
+    else if (stride <= kBlock * 32) TRI_WRITE(32);
+    else TRI_WRITE(0);
+#undef TRI_WRITE
     return hipGetLastError();
 }
 

@@ -386,7 +386,7 @@ tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, in
         if (!fires(q, budget, window)) continue;
         hipError_t e = tri::launch_compact(row_bytes, q.k, q.v, q.pos, q.cap, q.len, ctx->n_heads,
                                            kept + (int64_t)s * ctx->n_heads * budget, budget,
-                                           budget, nullptr, nullptr, hs);
+                                           budget, nullptr, nullptr, nullptr, hs);
         if (e != hipSuccess) return hip_fail(e);
         q.len = budget;
     }
@@ -423,24 +423,30 @@ tri_status tri_select_shared(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_
     const int64_t total = (int64_t)budget * ctx->n_kv_heads;
     const int64_t heads = ctx->n_heads;                      // n_layers * n_kv_heads
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    uint4* ws_head = reinterpret_cast<uint4*>(ws);
-    uint4* ws_layer = reinterpret_cast<uint4*>(ws + ((n_seq * heads * 16 + 255) & ~int64_t(255)));
+    const int64_t ws_seq = tri::shared_workspace_bytes(1, ctx->n_layers, ctx->n_kv_heads);
     int64_t off = 0;
     for (int32_t s = 0; s < n_seq; ++s) {
         const tri_seq& q = seqs[s];
         hipError_t e = tri::launch_select_shared(
             scores ? scores + off : nullptr, q.len, ctx->n_layers, ctx->n_kv_heads, q.head_len,
             budget, floor, window, kept + s * heads * total, kept_count + s * heads,
-            ws_head + s * heads, ws_layer + (int64_t)s * ctx->n_layers, hs);
+            ws + s * ws_seq, hs);
         if (e != hipSuccess) return hip_fail(e);
         off += heads * q.len;
     }
     return TRI_OK;
 }
 
+int64_t tri_compact_kv_counts_workspace_bytes(const tri_ctx* ctx)
+{
+    if (!ctx) return -1;
+    return tri::compact_queue_bytes(ctx->n_heads);
+}
+
 tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
                                  int32_t n_seq, const int32_t* kept, int32_t kept_stride,
-                                 const int32_t* kept_count, void* stream)
+                                 const int32_t* kept_count, void* workspace,
+                                 int64_t workspace_bytes, void* stream)
 {
     tri_status st = check_seqs(ctx, seqs, n_seq, true);
     if (st != TRI_OK) return st;
@@ -450,6 +456,9 @@ tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* s
     for (int32_t s = 0; s < n_seq; ++s)
         if (!seqs[s].head_len) return TRI_E_INVAL;
     if (!kept || !kept_count || ((uintptr_t)kept & 3u) || ((uintptr_t)kept_count & 3u))
+        return TRI_E_INVAL;
+    if (!workspace || ((uintptr_t)workspace & 3u) ||
+        workspace_bytes < tri::compact_queue_bytes(ctx->n_heads))
         return TRI_E_INVAL;
     st = check_device(ctx);
     if (st != TRI_OK) return st;
@@ -461,7 +470,8 @@ tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* s
         if (q.len == 0) continue;        // no rows: every count is 0 or -1 and head_len stays
         hipError_t e = tri::launch_compact(row_bytes, q.k, q.v, q.pos, q.cap, q.len, ctx->n_heads,
                                            kept + s * heads * kept_stride, 0, kept_stride,
-                                           kept_count + s * heads, q.head_len, hs);
+                                           kept_count + s * heads, q.head_len,
+                                           static_cast<uint32_t*>(workspace), hs);
         if (e != hipSuccess) return hip_fail(e);
     }
     return TRI_OK;

@@ -70,14 +70,17 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
 int64_t shared_workspace_bytes(int64_t n_seq, int64_t n_layers, int64_t n_kv);
 hipError_t launch_select_shared(const float* scores, int stride, int n_layers, int n_kv,
                                 const int32_t* head_len, int budget, int floor_, int window,
-                                int32_t* kept, int32_t* kept_count, void* ws_head, void* ws_layer,
+                                int32_t* kept, int32_t* kept_count, void* workspace,
                                 hipStream_t stream);
 
 // In-place stable gather of the first `budget` rows of every head (kept
 // lists at stride kept_stride); with counts, head h keeps counts[h] rows
 // (-1: untouched) and head_len[h] takes that count.
+// queue: device scratch of compact_queue_bytes(n_heads), needed with counts.
+int64_t compact_queue_bytes(int64_t n_heads);
 hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
                           int n_heads, const int32_t* kept, int budget, int kept_stride,
-                          const int32_t* counts, int32_t* head_len, hipStream_t stream);
+                          const int32_t* counts, int32_t* head_len, uint32_t* queue,
+                          hipStream_t stream);
 
 }  // namespace tri

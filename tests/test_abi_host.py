@@ -111,8 +111,9 @@ def test_calls_reject_null_context_and_bad_shapes(lib):
     assert lib.tri_select_shared_workspace_bytes(None, 1) == -1
     assert lib.tri_select_shared(None, arr, 1, None, 4, 1, 0, None, None, None, 0,
                                  None) == tri.TRI_E_INVAL
-    assert lib.tri_compact_kv_counts(None, tri.TRI_BF16, arr, 1, None, 4, None,
+    assert lib.tri_compact_kv_counts(None, tri.TRI_BF16, arr, 1, None, 4, None, None, 0,
                                      None) == tri.TRI_E_INVAL
+    assert lib.tri_compact_kv_counts_workspace_bytes(None) == -1
     lib.tri_ctx_destroy(None)     # allowed
 
 

@@ -181,7 +181,7 @@ def test_uniform_calls_reject_ragged_caches():
         tri.tri_compact_kv(ctx, [seq], kept, 10, 0)
     seq.head_len = None
     with pytest.raises(tri.TriError):     # the counted compaction needs head lengths
-        tri.tri_compact_kv_counts(ctx, [seq], kept, 10, kept[:2])
+        tri.tri_compact_kv_counts(ctx, [seq], kept, 10, kept[:2], kept)
 
 
 # ------------------------------------------------------------ compaction
@@ -216,8 +216,9 @@ def test_compact_counts_bit_exact(orc, dtype, d):
                                  np.ones((L, H, d // 2)), np.ones((L, H, d // 2)), [1], device=0)
     head_len = torch.from_numpy(hl).cuda()
     seq = tri.Seq(K, V, P, n, n - 1, head_len)
+    cws = torch.empty(tri.compact_counts_workspace_bytes(ctx), dtype=torch.uint8, device="cuda")
     tri.tri_compact_kv_counts(ctx, [seq], torch.from_numpy(kept).cuda().reshape(-1), total,
-                              torch.from_numpy(counts).cuda().reshape(-1))
+                              torch.from_numpy(counts).cuda().reshape(-1), cws)
     torch.cuda.synchronize()
     assert seq.len == n
     hl_after = head_len.cpu().numpy()
@@ -389,7 +390,8 @@ def fused_shared(orc, spec, seed, lengths, floor, sample):
     sws = None
     if spec.group > 1:
         sws = torch.empty(tri.score_workspace_bytes(ctx, [seq]), dtype=torch.uint8, device="cuda")
-    tri.prune_step_shared(ctx, [seq], B, floor, W, scores, kept, counts, ws, workspace=sws)
+    cws = torch.empty(tri.compact_counts_workspace_bytes(ctx), dtype=torch.uint8, device="cuda")
+    tri.prune_step_shared(ctx, [seq], B, floor, W, scores, kept, counts, ws, cws, workspace=sws)
     torch.cuda.synchronize()
     say("  shared prune step done, %.1fs" % (time.time() - t0))
     sc = scores.view(L, H1, n).cpu().numpy()

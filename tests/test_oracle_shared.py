@@ -92,3 +92,27 @@ def test_shared_selection_properties(oracle_lib, seed):
         worst_kept = min(_layer_key(sc[h, i], h, pos[h, i]) for h, i in free_kept)
         best_evicted = max(_layer_key(sc[h, i], h, pos[h, i]) for h, i in evicted)
         assert worst_kept > best_evicted
+
+
+def test_layer_prune_with_floor_equal_to_budget_is_the_uniform_prune(oracle_lib):
+    """prune_layer_shared with floor = budget keeps, per head, exactly what the
+    uniform per-head prune keeps (a different code path through the oracle:
+    select_head instead of the shared ranking)."""
+    import synth
+    spec = synth.workload("toy").replace(n_kv_heads=3, lengths=(300,), budget=70, window=0)
+    cache = synth.make_cache(spec, "cpu", seed=4)
+    cal = cache.calib
+    om = oracle_lib.omega(spec.head_dim, spec.rope_theta)
+    heads = []
+    for h in range(3):
+        heads.append(dict(K=cache.k[0][0, h].numpy(), V=cache.v[0][0, h].numpy(),
+                          pos=cache.pos[0][0, h].numpy(), p_now=cache.p_now[0], om=om,
+                          offsets=cal.offsets, qc_re=cal.qc_re[0, h], qc_im=cal.qc_im[0, h],
+                          q_mean_norm=cal.q_mean_norm[0, h], q_mrl=cal.q_mrl[0, h]))
+    shared = oracle_lib.prune_layer_shared(heads, 70 * 3, 70, 0, threads=2)
+    for h, j in enumerate(heads):
+        uni = oracle_lib.prune_head(j["K"], j["V"], j["pos"], j["p_now"], om, cal.offsets, j["qc_re"],
+                             j["qc_im"], j["q_mean_norm"], j["q_mrl"], 70, 0)
+        np.testing.assert_array_equal(shared[h]["kept"], uni["kept"])
+        np.testing.assert_array_equal(shared[h]["K"], uni["K"])
+        np.testing.assert_array_equal(shared[h]["pos"], uni["pos"])
