@@ -484,3 +484,86 @@ def test_fused_shared_extreme_lengths(orc):
 def test_fused_shared_gqa(orc):
     spec = synth.workload("gqa_small")
     fused_shared(orc, spec, 2, "ragged", spec.budget // 8, tuple(range(spec.n_layers)))
+
+
+def test_shared_select_and_compaction_over_several_sequences(orc):
+    """Three sequences of different lengths (one that fires nowhere) in one
+    call: the workspace slices per sequence, the kept and count layouts, and
+    the counted compaction's reused queue."""
+    L, H, B, F, W = 2, 8, 300, 40, 16
+    lens = [3000, 2500, 200]
+    total = B * H
+    ctx = dummy_ctx(L, H, d=64)
+    seqs, hls, scs, pristine = [], [], [], []
+    for s, n in enumerate(lens):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(77 + s)
+        K = torch.randn((L, H, n, 64), generator=g, device="cuda")
+        V = torch.randn((L, H, n, 64), generator=g, device="cuda")
+        P = torch.arange(n, dtype=torch.int32, device="cuda").repeat(L, H, 1)
+        hl = synth.head_lengths("ragged", L, H, n, seed=s)
+        hls.append(hl)
+        scs.append(synth.make_scores("dups", L * H, n, seed=s).reshape(L, H, n))
+        pristine.append((K.cpu(), V.cpu(), P.cpu()))
+        seqs.append(tri.Seq(K, V, P, n, n - 1, torch.from_numpy(hl).cuda()))
+    scores = torch.from_numpy(np.concatenate([x.reshape(-1) for x in scs])).cuda()
+    kept = torch.full((len(lens) * L * H * total,), -7, dtype=torch.int32, device="cuda")
+    counts = torch.full((len(lens) * L * H,), -9, dtype=torch.int32, device="cuda")
+    ws = torch.empty(tri.select_shared_workspace_bytes(ctx, len(lens)), dtype=torch.uint8,
+                     device="cuda")
+    cws = torch.empty(tri.compact_counts_workspace_bytes(ctx), dtype=torch.uint8, device="cuda")
+    tri.tri_select_shared(ctx, seqs, scores, B, F, W, kept, counts, ws)
+    kept_h = kept.cpu().numpy().reshape(len(lens), L, H, total)
+    cnt_h = counts.cpu().numpy().reshape(len(lens), L, H)
+    tri.tri_compact_kv_counts(ctx, seqs, kept, total, counts, cws)
+    torch.cuda.synchronize()
+    for s, n in enumerate(lens):
+        K0, V0, P0 = pristine[s]
+        hl_after = seqs[s].head_len.cpu().numpy()
+        for l in range(L):
+            pos = np.broadcast_to(np.arange(n), (H, n))
+            ref = orc.select_shared(scs[s][l].astype(np.float64), pos, hls[s][l], total, F, W)
+            if ref is None:
+                assert np.all(cnt_h[s, l] == -1)
+                assert np.array_equal(hl_after[l], hls[s][l])
+                continue
+            for h in range(H):
+                c = len(ref[h])
+                assert cnt_h[s, l, h] == c and hl_after[l, h] == c
+                np.testing.assert_array_equal(kept_h[s, l, h, :c], ref[h])
+                kk = torch.from_numpy(ref[h]).long()
+                assert torch.equal(seqs[s].k[l, h, :c].cpu(), K0[l, h, kk])
+                assert torch.equal(seqs[s].v[l, h, :c].cpu(), V0[l, h, kk])
+                assert torch.equal(seqs[s].pos[l, h, :c].cpu(), P0[l, h, kk])
+    assert cnt_h[2].max() == -1        # 8 heads of <= 200 keys never exceed 8 x 300 + 8 x 16
+
+
+def test_shared_calls_reject_bad_arguments():
+    L, H, n = 1, 4, 500
+    ctx = dummy_ctx(L, H)
+    k = torch.zeros((L, H, n, 64), device="cuda")
+    hl = torch.full((L, H), n, dtype=torch.int32, device="cuda")
+    seq = tri.Seq(k, torch.zeros_like(k), torch.zeros((L, H, n), dtype=torch.int32, device="cuda"),
+                  n, n - 1, hl)
+    sc = torch.zeros(L * H * n, device="cuda")
+    kept = torch.zeros(L * H * 100 * H, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(L * H, dtype=torch.int32, device="cuda")
+    ws = torch.empty(tri.select_shared_workspace_bytes(ctx, 1), dtype=torch.uint8, device="cuda")
+    lib = tri.library()
+    arr = (tri._Seq * 1)(tri._Seq(k.data_ptr(), seq.v.data_ptr(), seq.pos.data_ptr(), n, n, n - 1,
+                                  hl.data_ptr()))
+    call = lambda budget, floor, window, wsb, kc=counts.data_ptr(): lib.tri_select_shared(
+        ctx.handle, arr, 1, sc.data_ptr(), budget, floor, window, kept.data_ptr(), kc,
+        ws.data_ptr(), wsb, None)
+    nb = ws.numel()
+    assert call(100, 101, 0, nb) == tri.TRI_E_INVAL          # floor above the budget
+    assert call(100, -1, 0, nb) == tri.TRI_E_INVAL           # negative floor
+    assert call(0, 0, 0, nb) == tri.TRI_E_INVAL              # no budget
+    assert call(100, 10, -1, nb) == tri.TRI_E_INVAL          # negative window
+    assert call(100, 10, 0, nb - 1) == tri.TRI_E_INVAL       # short workspace
+    assert call(100, 10, 0, nb, kc=None) == tri.TRI_E_INVAL  # no counts
+    assert call(100, 10, 0, nb) == tri.TRI_OK
+    big = dummy_ctx(1, 129)
+    assert lib.tri_select_shared(big.handle, arr, 0, None, 1, 0, 0, None, None, None, 0,
+                                 None) == tri.TRI_E_UNSUPPORTED
+    torch.cuda.synchronize()
