@@ -466,7 +466,7 @@ def main():
                    "budgets": ("shared per layer (budget x %d KV heads), floor %d per head"
                                % (spec.n_kv_heads, F)) if shared else "uniform per head"},
         "roofline": {"bound": "hbm", "kernel": SCORE_KERNEL if spec.group == 1 else
-                     "GQA score phase (gqa_score_kernel, gqa_stats_kernel, gqa_norm_kernel)",
+                     "GQA score phase (gqa_prep_kernel, gqa_mfma_kernel, gqa_stats_kernel, gqa_norm_kernel; f32 K: gqa_score_kernel)",
                      "achieved": score_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": score_gbs / HBM_PEAK_GBS,
                      "traffic": load_traffic(spec), "alg_bytes_per_launch": bytes_score,

@@ -219,7 +219,8 @@ tri_status tri_score(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs, i
 
 /* Device workspace bytes tri_score_ws needs for these sequences: 0 for a
  * context with one query table per KV head; for GQA contexts 4 * G bytes per
- * cached key plus per-tile statistics.  Returns -1 on bad arguments. */
+ * cached key plus per-tile statistics and 8 KB per (layer, KV head) of
+ * prepared constants.  Returns -1 on bad arguments. */
 int64_t tri_score_workspace_bytes(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq);
 
 /*

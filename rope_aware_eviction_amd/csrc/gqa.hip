@@ -31,7 +31,14 @@ constexpr int kBlock = 256;
 constexpr int kTileRows = 512;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource word 3, gfx9 family
 constexpr int kSC1 = 16;                   // cache-policy bits: sc1
+constexpr int kNT = 2;                     // cache-policy bits: non-temporal
+constexpr uint32_t kDrop = 0xFFFFFFC0u;    // buffer offset that is always out of range
+// matrix-core B operands of one head: at most 8 k-blocks x 64 lanes x 16 bytes
+constexpr int64_t kBopBytesPerHead = 8 * 64 * 16;
 constexpr double kFlat = 1e-9;             // deviation at or below kFlat * max|s| counts as zero
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
@@ -146,6 +153,64 @@ struct Chunk {
         }
     }
 };
+
+// The end of a score tile: its raw scores (rows [tile_start, row_end) x G,
+// staged in s_raw) leave in one contiguous sweep, and per query head the
+// fp64 partial statistics of the tile (sum, sum of squares, count of finite
+// scores, largest |score|) are reduced in a fixed order.
+template <int G>
+__device__ __forceinline__ void tile_epilogue(const float* s_raw, double (*s_red)[4],
+                                              float* __restrict__ raw,
+                                              double* __restrict__ partial, int head, int tile,
+                                              int tiles_per_head, int len, int tile_start,
+                                              int row_end, int tid, int lane, int wave)
+{
+    const int n_out = (row_end - tile_start) * G;
+    float* out = raw + ((size_t)head * (size_t)len + tile_start) * G;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, n_out * 4, kBufferWord3);
+    for (int i = tid; i < n_out; i += kBlock)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_raw[i]), ro, i * 4, 0, kSC1);
+
+    double* pt = partial + (((size_t)head * tiles_per_head + tile) * G) * 4;
+    const int n_rows = row_end - tile_start;
+    for (int g = 0; g < G; ++g) {
+        double s1 = 0.0, s2 = 0.0, cnt = 0.0, big = 0.0;
+        for (int r = tid; r < n_rows; r += kBlock) {
+            const double x = (double)s_raw[r * G + g];
+            if (isfinite(x)) {
+                s1 += x;
+                s2 += x * x;
+                cnt += 1.0;
+                big = fmax(big, fabs(x));
+            }
+        }
+        s1 = wave_sum_d(s1);
+        s2 = wave_sum_d(s2);
+        cnt = wave_sum_d(cnt);
+        big = wave_max_d(big);
+        if (lane == 0) {
+            s_red[wave][0] = s1;
+            s_red[wave][1] = s2;
+            s_red[wave][2] = cnt;
+            s_red[wave][3] = big;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double a1 = 0.0, a2 = 0.0, ac = 0.0, ab = 0.0;
+            for (int x = 0; x < kBlock / 64; ++x) {
+                a1 += s_red[x][0];
+                a2 += s_red[x][1];
+                ac += s_red[x][2];
+                ab = fmax(ab, s_red[x][3]);
+            }
+            pt[g * 4 + 0] = a1;
+            pt[g * 4 + 1] = a2;
+            pt[g * 4 + 2] = ac;
+            pt[g * 4 + 3] = ab;
+        }
+        __syncthreads();
+    }
+}
 
 template <int D, bool BF16, int G>
 struct GqaShape {
@@ -269,53 +334,253 @@ __global__ __launch_bounds__(kBlock) void gqa_score_kernel(
     }
     __syncthreads();
 
-    // raw scores of the tile: rows [tile_start, row_end) x G, contiguous
-    const int n_out = (row_end - tile_start) * G;
-    float* out = raw + ((size_t)head * (size_t)len + tile_start) * G;
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, n_out * 4, kBufferWord3);
-    for (int i = tid; i < n_out; i += kBlock)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_raw[i]), ro, i * 4, 0, kSC1);
+    tile_epilogue<G>(s_raw, s_red, raw, partial, head, tile, tiles_per_head, len, tile_start,
+                     row_end, tid, lane, wave);
+}
 
-    // fp64 partial statistics of the tile per query head, in a fixed order
-    double* pt = partial + (((size_t)head * tiles_per_head + tile) * G) * 4;
-    const int n_rows = row_end - tile_start;
-    for (int g = 0; g < G; ++g) {
-        double s1 = 0.0, s2 = 0.0, cnt = 0.0, big = 0.0;
-        for (int r = tid; r < n_rows; r += kBlock) {
-            const double x = (double)s_raw[r * G + g];
-            if (isfinite(x)) {
-                s1 += x;
-                s2 += x * x;
-                cnt += 1.0;
-                big = fmax(big, fabs(x));
-            }
-        }
-        s1 = wave_sum_d(s1);
-        s2 = wave_sum_d(s2);
-        cnt = wave_sum_d(cnt);
-        big = wave_max_d(big);
-        if (lane == 0) {
-            s_red[wave][0] = s1;
-            s_red[wave][1] = s2;
-            s_red[wave][2] = cnt;
-            s_red[wave][3] = big;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            double a1 = 0.0, a2 = 0.0, ac = 0.0, ab = 0.0;
-            for (int x = 0; x < kBlock / 64; ++x) {
-                a1 += s_red[x][0];
-                a2 += s_red[x][1];
-                ac += s_red[x][2];
-                ab = fmax(ab, s_red[x][3]);
-            }
-            pt[g * 4 + 0] = a1;
-            pt[g * 4 + 1] = a2;
-            pt[g * 4 + 2] = ac;
-            pt[g * 4 + 3] = ab;
-        }
-        __syncthreads();
+// MFMA variant for bf16 K (D = 64 or 128): the G dot products and the G
+// norm sums of 16 rows are one small contraction,
+//   raw[row][g] = sum_k K[row][k] u_g[k] + sum_f |K_f|[row] w_g[f],
+// which v_mfma_f32_16x16x32_bf16 evaluates with the rows as M, the query
+// heads as N and [K | |K|] as the contraction.  Its operands are bf16: K is
+// stored in bf16 (exact); the folded constants u_g, the weights w_g and the
+// magnitudes |K_f| are fp32 and enter as a sum of two bf16 numbers,
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), which leaves an error
+// of at most 2^-16 |x|.  Columns g < G carry the hi parts of the constants,
+// columns G + g their lo parts, and raw[row][g] is the sum of columns g and
+// G + g:
+//   column g:     K . u_hi  +  |K|_hi . w_hi  +  |K|_lo . w_hi
+//   column G + g: K . u_lo  +  |K|_hi . w_lo
+// (the dropped |K|_lo . w_lo is below 2^-16 of the norm term).  Products of
+// bf16 numbers are exact and the MFMA accumulates in fp32.
+//
+// Lane layout of the 16x16x32 operands (checked on the device): lane l holds
+// A[l % 16][8 (l / 16) + i] and B[8 (l / 16) + i][l % 16], i < 8, and result
+// rows 4 (l / 16) + i of column l % 16, i < 4.  So lane l loads 16 bytes of
+// row l % 16 at byte 16 (l / 16) of each 64-byte k-block: a row's real half
+// and imaginary half land in the same lane (k-blocks m and m + KB / 2), which
+// gives the band magnitudes with no data exchange.
+//
+// gqa_prep_kernel folds the constants once per head (fp64) and writes every
+// lane's B operands, [head][k-block][lane] x 16 bytes, to the workspace;
+// gqa_mfma_kernel reads them at the start of each tile.
+template <int D>
+struct MfmaShape {
+    static constexpr int kHalf = D / 2;
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int KB = kRowBytes / 64;   // k-blocks of a K row
+    static constexpr int KM = KB / 2;           // k-blocks of the band magnitudes
+    static constexpr int NT = KB + 2 * KM;      // k-blocks of the contraction
+    static_assert(KB >= 2 && KB % 2 == 0, "row of whole k-block pairs");
+};
+
+// B operands of one head: one wave; lane l's entries of column l % 16.
+template <int D, int G>
+__global__ __launch_bounds__(64) void gqa_prep_kernel(double p_now, const double* __restrict__ omega,
+                                                      const double2* __restrict__ qa,
+                                                      const float* __restrict__ w,
+                                                      u32x4* __restrict__ bops)
+{
+    using S = MfmaShape<D>;
+    constexpr int kHalf = S::kHalf, KB = S::KB, KM = S::KM, NT = S::NT;
+    static_assert(2 * G <= 16, "hi and lo columns of every query head fit in 16");
+    __shared__ float s_u[G][D];
+    __shared__ float s_w[G][kHalf];
+    const int head = blockIdx.x;
+    const int lane = threadIdx.x;
+    for (int t = lane; t < G * kHalf; t += 64) {
+        const int g = t / kHalf, f = t - g * kHalf;
+        double sn, cs;
+        sincos(omega[f] * p_now, &sn, &cs);
+        const double2 a = qa[((size_t)head * G + g) * kHalf + f];
+        s_u[g][f] = (float)(a.x * cs - a.y * sn);
+        s_u[g][f + kHalf] = (float)(a.x * sn + a.y * cs);
+        s_w[g][f] = w[((size_t)head * G + g) * kHalf + f];
     }
+    __syncthreads();
+    const int q = lane >> 4, rl = lane & 15;
+    const bool col_hi = rl < G, col_lo = rl >= G && rl < 2 * G;
+    const int g = col_hi ? rl : (col_lo ? rl - G : 0);
+    for (int t = 0; t < NT; ++t) {
+        bf16x8 v;
+        for (int i = 0; i < 8; ++i) {
+            float x;
+            bool take_lo = col_lo;
+            bool use = col_hi || col_lo;
+            if (t < KB) {
+                x = s_u[g][t * 32 + 8 * q + i];
+            } else if (t < KB + KM) {
+                x = s_w[g][(t - KB) * 32 + 8 * q + i];
+            } else {
+                x = s_w[g][(t - KB - KM) * 32 + 8 * q + i];
+                use = col_hi;               // |K|_lo meets w_hi only
+                take_lo = false;
+            }
+            const __bf16 h = (__bf16)x;
+            v[i] = !use ? (__bf16)0.0f : (take_lo ? (__bf16)(x - (float)h) : h);
+        }
+        bops[((size_t)head * NT + t) * 64 + lane] = __builtin_bit_cast(u32x4, v);
+    }
+}
+
+// Squares of the two bands held in the low and the high halves of a bf16
+// pair register: the real and imaginary parts are paired by a byte permute
+// and squared and summed by one dot instruction (exact products).
+__device__ __forceinline__ void band_energy(uint32_t re2, uint32_t im2, float& e0, float& e1)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t p0 = __builtin_amdgcn_perm(im2, re2, 0x05040100u);   // (re lo, im lo)
+    const uint32_t p1 = __builtin_amdgcn_perm(im2, re2, 0x07060302u);   // (re hi, im hi)
+    const bf16x2 a0 = __builtin_bit_cast(bf16x2, p0), a1 = __builtin_bit_cast(bf16x2, p1);
+    e0 = __builtin_amdgcn_fdot2_f32_bf16(a0, a0, 0.0f, false);
+    e1 = __builtin_amdgcn_fdot2_f32_bf16(a1, a1, 0.0f, false);
+}
+
+// Each wave takes 16-row groups w, w + 4, ... of the tile, R of them in flight.
+template <int D, int G>
+__global__ __launch_bounds__(kBlock) void gqa_mfma_kernel(
+    const unsigned char* __restrict__ k, int64_t cap, int len, int tiles_per_head,
+    const u32x4* __restrict__ bops, float* __restrict__ raw, double* __restrict__ partial,
+    const int32_t* __restrict__ head_len)
+{
+    using S = MfmaShape<D>;
+    constexpr int kRowBytes = S::kRowBytes, KB = S::KB, KM = S::KM, NT = S::NT;
+    constexpr int R = 2;                      // 16-row groups in registers per wave
+    constexpr int P = 1;                      // groups computed together
+    static_assert(R % P == 0, "whole steps");
+    constexpr int kWaves = kBlock / 64;
+    constexpr int kGroupsPerWave = kTileRows / 16 / kWaves;
+    static_assert(kGroupsPerWave % R == 0, "whole rounds of groups per wave");
+
+    __shared__ float s_raw[kTileRows * G];
+    __shared__ double s_red[kBlock / 64][4];
+    __shared__ __attribute__((aligned(16))) unsigned char s_stage[kWaves * 16 * (kRowBytes + 16)];
+
+    const int head = blockIdx.x / tiles_per_head;
+    const int tile = blockIdx.x - head * tiles_per_head;
+    const int n_h = head_len ? max(0, min(head_len[head], len)) : len;
+    if (tile * kTileRows >= n_h) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int q = lane >> 4;                  // 16-byte chunk within a k-block
+    const int rl = lane & 15;                 // row within a group; result column
+    const int tile_start = tile * kTileRows;
+    const int row_end = min(n_h, tile_start + kTileRows);
+
+    bf16x8 bop[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        bop[t] = __builtin_bit_cast(bf16x8, bops[((size_t)head * NT + t) * 64 + lane]);
+
+    // K rows through a bounds-checked buffer resource: groups past the
+    // tile's end get an offset the hardware drops (zeros, no traffic), so
+    // every wave issues the same loads in the same order and the waits can
+    // count them
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(k + (size_t)head * (size_t)cap * kRowBytes), 0, row_end * kRowBytes, kBufferWord3);
+    // A wave instruction reads whole rows (RPI rows of CPR 16-byte chunks,
+    // every 128-byte line complete); the rows then pass through LDS, where
+    // each lane picks up the chunks the MFMA layout gives it.
+    constexpr int CPR = kRowBytes / 16;       // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;             // rows per wave instruction
+    constexpr int NI = 16 / RPI;              // instructions per 16-row group
+    static_assert(NI == KB, "a group is one load per k-block");
+    u32x4 buf[R][KB];
+    auto load_group = [&](u32x4* b, int gi) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int row = tile_start + gi * 16 + j * RPI + lane / CPR;
+            const uint32_t off = row < row_end ? (uint32_t)row * kRowBytes + (lane % CPR) * 16 : kDrop;
+            b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kNT));
+        }
+    };
+    // staging rows padded by 16 bytes: the MFMA-layout reads (16 rows at
+    // one chunk offset) fall into 16 different 4-bank groups
+    constexpr int kStageRow = kRowBytes + 16;
+    unsigned char* stage = s_stage + wave * (16 * kStageRow);
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_group(buf[r], wave + r * kWaves);
+
+    // P groups at a time: their magnitude work and their MFMA chains are
+    // independent, which gives the scheduler work to overlap with each
+    // chain's latency
+    auto compute = [&](const u32x4 (*bl)[KB], const int* gi) {
+        u32x4 b[P][KB];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                *reinterpret_cast<u32x4*>(stage + (j * RPI + lane / CPR) * kStageRow + (lane % CPR) * 16) =
+                    bl[p][j];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                b[p][kb] = *reinterpret_cast<const u32x4*>(stage + rl * kStageRow + (kb * 4 + q) * 16);
+        }
+        bf16x8 mh[P][KM], ml[P][KM];
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int m = 0; m < KM; ++m)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    float e0, e1;
+                    band_energy(b[p][m][c], b[p][m + KM][c], e0, e1);
+                    const float m0 = __builtin_amdgcn_sqrtf(e0), m1 = __builtin_amdgcn_sqrtf(e1);
+                    const __bf16 h0 = (__bf16)m0, h1 = (__bf16)m1;
+                    mh[p][m][2 * c] = h0;
+                    mh[p][m][2 * c + 1] = h1;
+                    ml[p][m][2 * c] = (__bf16)(m0 - (float)h0);
+                    ml[p][m][2 * c + 1] = (__bf16)(m1 - (float)h1);
+                }
+        f32x4 acc[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KB; ++t)
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b[p][t]),
+                                                                 bop[t], acc[p], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < KM; ++m)
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh[p][m], bop[KB + m], acc[p], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < KM; ++m)
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml[p][m], bop[KB + KM + m], acc[p], 0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo_part = __shfl_down(acc[p][i], G);   // column G + rl, same rows
+                const int row = tile_start + gi[p] * 16 + 4 * q + i;
+                if (rl < G && row < row_end) s_raw[(row - tile_start) * G + rl] = acc[p][i] + lo_part;
+            }
+    };
+
+    // scheduling barriers pin every step's loads right after the compute
+    // that frees their registers, so R - P groups stay in flight
+#pragma unroll
+    for (int o = 0; o < kGroupsPerWave; o += R) {
+#pragma unroll
+        for (int r = 0; r < R; r += P) {
+            int gi[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) gi[p] = wave + (o + r + p) * kWaves;
+            __builtin_amdgcn_sched_barrier(0);
+            compute(&buf[r], gi);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < P; ++p) load_group(buf[r + p], gi[p] + R * kWaves);
+        }
+    }
+    __syncthreads();
+    tile_epilogue<G>(s_raw, s_red, raw, partial, head, tile, tiles_per_head, len, tile_start,
+                     row_end, tid, lane, wave);
 }
 
 // mean and deviation per (head, query head): one wave per head; lane t sums
@@ -396,14 +661,26 @@ template <int D, bool BF16, int G>
 hipError_t launch_g(const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
                     const double* omega, const double2* qa, const float* w, float* raw,
                     double* partial, double2* stats, float* scores, const int32_t* head_len,
-                    hipStream_t stream)
+                    u32x4* bops, hipStream_t stream)
 {
     const int tiles = (len + kTileRows - 1) / kTileRows;
     const int64_t grid = (int64_t)tiles * n_heads;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gqa_score_kernel<D, BF16, G>), dim3((unsigned)grid), dim3(kBlock), 0,
-                       stream, static_cast<const unsigned char*>(k), cap, len, tiles,
-                       (double)p_now, omega, qa, w, raw, partial, head_len);
+    if constexpr (BF16) {
+        // bf16 K: the G dot products and norm sums on the matrix cores, their
+        // operands prepared once per head
+        hipLaunchKernelGGL((gqa_prep_kernel<D, G>), dim3((unsigned)n_heads), dim3(64), 0, stream,
+                           (double)p_now, omega, qa, w, bops);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                           static_cast<const unsigned char*>(k), cap, len, tiles,
+                           static_cast<const u32x4*>(bops), raw, partial, head_len);
+    } else {
+        hipLaunchKernelGGL((gqa_score_kernel<D, BF16, G>), dim3((unsigned)grid), dim3(kBlock), 0,
+                           stream, static_cast<const unsigned char*>(k), cap, len, tiles,
+                           (double)p_now, omega, qa, w, raw, partial, head_len);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gqa_stats_kernel, dim3(n_heads), dim3(64), 0, stream, partial, tiles, G,
@@ -419,12 +696,12 @@ template <int D, bool BF16>
 hipError_t launch_d(int group, const void* k, int64_t cap, int len, int n_heads, int64_t p_now,
                     const double* omega, const double2* qa, const float* w, float* raw,
                     double* partial, double2* stats, float* scores, const int32_t* head_len,
-                    hipStream_t stream)
+                    u32x4* bops, hipStream_t stream)
 {
 #define TRI_GQA_CASE(G)                                                                           \
     case G:                                                                                       \
         return launch_g<D, BF16, G>(k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,      \
-                                    stats, scores, head_len, stream);
+                                    stats, scores, head_len, bops, stream);
     switch (group) {
         TRI_GQA_CASE(2)
         TRI_GQA_CASE(3)
@@ -445,7 +722,7 @@ int64_t gqa_workspace_bytes(int64_t n_heads, int64_t len, int group)
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t tiles = (len + kTileRows - 1) / kTileRows;
     return up(n_heads * len * group * 4) + up(n_heads * tiles * group * 4 * 8) +
-           up(n_heads * group * 16);
+           up(n_heads * group * 16) + up(n_heads * kBopBytesPerHead);
 }
 
 hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void* k, int64_t cap,
@@ -454,6 +731,9 @@ hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void
                             const int32_t* head_len, hipStream_t stream)
 {
     if (len <= 0 || n_heads <= 0) return hipSuccess;
+    // the matrix-core kernel addresses a head's rows with 32-bit buffer offsets
+    if (dtype == TRI_BF16 && (int64_t)len * head_dim * 2 >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t tiles = (len + kTileRows - 1) / kTileRows;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -461,18 +741,21 @@ hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void
     double* partial = reinterpret_cast<double*>(ws + up((int64_t)n_heads * len * group * 4));
     double2* stats = reinterpret_cast<double2*>(ws + up((int64_t)n_heads * len * group * 4) +
                                                 up((int64_t)n_heads * tiles * group * 4 * 8));
+    u32x4* bops = reinterpret_cast<u32x4*>(ws + up((int64_t)n_heads * len * group * 4) +
+                                           up((int64_t)n_heads * tiles * group * 4 * 8) +
+                                           up((int64_t)n_heads * group * 16));
     if (dtype == TRI_BF16 && head_dim == 128)
         return launch_d<128, true>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                   stats, scores, head_len, stream);
+                                   stats, scores, head_len, bops, stream);
     if (dtype == TRI_F32 && head_dim == 64)
         return launch_d<64, false>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                   stats, scores, head_len, stream);
+                                   stats, scores, head_len, bops, stream);
     if (dtype == TRI_BF16 && head_dim == 64)
         return launch_d<64, true>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                  stats, scores, head_len, stream);
+                                  stats, scores, head_len, bops, stream);
     if (dtype == TRI_F32 && head_dim == 128)
         return launch_d<128, false>(group, k, cap, len, n_heads, p_now, omega, qa, w, raw, partial,
-                                    stats, scores, head_len, stream);
+                                    stats, scores, head_len, bops, stream);
     return hipErrorInvalidValue;
 }
 
