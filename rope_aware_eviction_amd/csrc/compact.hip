@@ -239,14 +239,13 @@ hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_he
     // at once is slower still.  On the 32 x 8 x 8192 cache (512 streams of
     // 2048 rows) 256 workgroups of two streams take 98 us (one per stream:
     // 97.5 us).
-    static const int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        return n;
-    }();
-    if (cus <= 0) return hipErrorInvalidDevice;
+    // compute units of the current device (a cheap query, done per call so
+    // that every device gets its own count)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return hipErrorInvalidDevice;
     const int streams = 2 * n_heads;
     if (queue) {
         // counted lists: 128-byte column parts, one workgroup per compute

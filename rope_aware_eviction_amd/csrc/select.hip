@@ -1104,14 +1104,11 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
                            scores, n, budget, kept, kept_stride, head_len);
     } else if (n <= kLdsKeysMax) {
         const size_t lds = (size_t)(kHistBins + n) * sizeof(uint32_t);
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void*)select_kernel<true>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)((kHistBins + kLdsKeysMax) * sizeof(uint32_t)));
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        // the attribute belongs to the current device: set it on every call
+        hipError_t e = hipFuncSetAttribute((const void*)select_kernel<true>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)((kHistBins + kLdsKeysMax) * sizeof(uint32_t)));
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(select_kernel<true>, dim3(n_heads), dim3(kBlock), lds, stream, scores, n,
                            budget, kept, kept_stride, head_len);
     } else {
