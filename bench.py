@@ -5,8 +5,9 @@ Default workload: the Qwen3-8B-shaped 32K reasoning cache (36 layers x 8 KV
 heads x head_dim 128, 32768 cached keys per head, budget 4096, bf16), synthetic
 and seeded.  A step is one whole prune pass over every head, with inputs
 resident in HBM.  Between steps the cache is restored from a pristine device
-copy and a 512 MiB buffer is read to flush the 256 MB last-level cache; both
-are outside the timed events.  The flush reads rather than writes: a written
+copy (for caches above 64 GB, such as the 64-sequence batch, a copy of the
+rows a step can overwrite) and a 512 MiB buffer is read to flush the 256 MB
+last-level cache; both are outside the timed events.  The flush reads rather than writes: a written
 flush buffer leaves up to 256 MB of dirty lines whose write-back then lands
 inside the timed step (measured: ~12 us per step), while a read evicts the
 restore's dirty lines before the first event.  Times come from HIP events
@@ -384,14 +385,27 @@ def main():
         print("pmc steps done", file=sys.stderr, flush=True)
         return
 
-    pristine = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
+    # Restores: a full pristine copy of K, V and positions, or, when that
+    # would not fit beside the cache (the 64-sequence batch holds ~155 GB),
+    # a copy of the rows a step can overwrite: compaction writes only rows
+    # below the kept count (budget, or budget x KV heads when the heads of a
+    # layer share it), so restoring those rows restores the cache.
+    kv_bytes = sum(2 * k.numel() * k.element_size() for k in cache.k)
+    partial = kv_bytes > (64 << 30)
+    rows = B * spec.n_kv_heads if shared else B
+    if partial:
+        pristine = [(k[:, :, :rows].clone(), v[:, :, :rows].clone(), p[:, :, :rows].clone())
+                    for k, v, p in zip(cache.k, cache.v, cache.pos)]
+    else:
+        pristine = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
 
     def restore():
         for (k0, v0, p0), k, v, p in zip(pristine, cache.k, cache.v, cache.pos):
-            k.copy_(k0)
-            v.copy_(v0)
-            p.copy_(p0)
+            r = k0.shape[2]
+            k[:, :, :r].copy_(k0)
+            v[:, :, :r].copy_(v0)
+            p[:, :, :r].copy_(p0)
         if shared:
             for hl, n in zip(head_len, cache.lens):
                 hl.fill_(n)
