@@ -103,11 +103,18 @@ def check_kept(orc, s_ref, tol, P, kept_gpu, B, window, what):
     say("  %s: kept-set disagreements with the oracle: %d of %d" % (what, len(dis), B))
 
 
-@pytest.mark.parametrize("name,heads", [("gqa_toy", None), ("gqa_small", None), ("gqa_g7", 2),
-                                        ("gqa_g8_d64", 2)])
-def test_gqa_scores_match_oracle(orc, name, heads):
+@pytest.mark.parametrize("name,heads,over", [
+    ("gqa_toy", None, None), ("gqa_small", None, None), ("gqa_g7", 2, None), ("gqa_g8_d64", 2, None),
+    # fp32 K at head_dim 128 (the vector-unit kernel), and a length that ends
+    # inside a 16-row group and a 512-row tile (the matrix-core kernel's tails)
+    ("gqa_small", 2, {"dtype": "f32", "name": "gqa_small_f32"}),
+    ("gqa_small", None, {"lengths": (4001,), "name": "gqa_small_4001"}),
+    ("gqa_g8_d64", None, {"lengths": (530,), "name": "gqa_g8_d64_530"})])
+def test_gqa_scores_match_oracle(orc, name, heads, over):
     spec = synth.workload(name)
-    say("gqa scores", name, "G =", spec.group)
+    if over:
+        spec = spec.replace(**over)
+    say("gqa scores", spec.name, "G =", spec.group)
     cache = synth.make_cache(spec, "cuda", seed=3)
     ctx = ctx_gqa(cache)
     seqs = seqs_for(cache)
@@ -123,7 +130,7 @@ def test_gqa_scores_match_oracle(orc, name, heads):
     for l, h in pairs:
         K, _, P = head_inputs(cache, 0, l, h)
         s_ref, tol = oracle_gqa(orc, cache, 0, l, h, K, P)
-        check_agg(sg[l, h], s_ref, tol, "%s l%d h%d" % (name, l, h))
+        check_agg(sg[l, h], s_ref, tol, "%s l%d h%d" % (spec.name, l, h))
 
 
 def test_gqa_needs_its_workspace():
