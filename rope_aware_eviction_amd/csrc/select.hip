@@ -336,14 +336,17 @@ __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane)
 // RESERVE (head-specific budgets, budget = the per-head floor): instead of
 // the kept list, writes rec[head] = {Th, Sh, min, max}: the kept set as the
 // pointwise test "key > Th, or key == Th and slot <= Sh", and the range of
-// the keys outside it (min > max when there are none).
+// the keys outside it (min > max when there are none); and hist_out[head],
+// the histogram of the keys outside it by their top 12 bits (the first
+// radix digit of the layer-wide selection, whose binning needs no range).
 template <int KPT, int NT, bool RESERVE = false>
 __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict__ scores,
                                                         int stride, int budget,
                                                         int32_t* __restrict__ kept,
                                                         int kept_stride,
                                                         const int32_t* __restrict__ head_len,
-                                                        uint4* __restrict__ rec = nullptr)
+                                                        uint4* __restrict__ rec = nullptr,
+                                                        uint32_t* __restrict__ hist_out = nullptr)
 {
     constexpr int kW = NT / 64;
     __shared__ uint32_t hist[1 << kRegDigitBits];
@@ -357,7 +360,11 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
     const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
     if (n <= budget) {
         // RESERVE: every key is reserved (Th = 0 lies below every real key)
-        if (RESERVE && threadIdx.x == 0) rec[blockIdx.x] = make_uint4(0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0u);
+        if constexpr (RESERVE) {
+            for (int b = threadIdx.x; b < (1 << kRegDigitBits); b += NT)
+                hist_out[(size_t)blockIdx.x * (1 << kRegDigitBits) + b] = 0u;
+            if (threadIdx.x == 0) rec[blockIdx.x] = make_uint4(0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0u);
+        }
         return;
     }
     const int tid = threadIdx.x;
@@ -406,9 +413,43 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
         }
     }
 
+    // RESERVE: the range and the top-12-bit histogram of the keys outside
+    // the reserved set "key > th, or key == th and slot <= sh"
+    auto reserve_tail = [&](uint32_t th, int sh) {
+        __syncthreads();                                // earlier readers of hist / s_*
+        for (uint32_t b = tid; b < (1u << kRegDigitBits); b += NT) hist[b] = 0u;
+        __syncthreads();
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) {
+            const uint32_t k = key[c];
+            const bool res = k > th || (k == th && seg0 + 64 * c <= sh);
+            if (k != 0u && !res) {
+                lo = min(lo, k);
+                hi = max(hi, k);
+                atomicAdd(&hist[k >> (32 - kRegDigitBits)], 1u);
+            }
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) {
+            s_wa[wave] = lo;
+            s_wb[wave] = hi;
+        }
+        __syncthreads();
+        uint32_t* ho = hist_out + (size_t)blockIdx.x * (1 << kRegDigitBits);
+        for (uint32_t b = tid; b < (1u << kRegDigitBits); b += NT) ho[b] = hist[b];
+        if (tid == 0) {
+            for (int x = 0; x < kW; ++x) {
+                lo = min(lo, s_wa[x]);
+                hi = max(hi, s_wb[x]);
+            }
+            rec[blockIdx.x] = make_uint4(th, (uint32_t)sh, lo, hi);
+        }
+    };
+
     if (RESERVE && budget == 0) {
-        // nothing reserved (no key lies above kTopKey); the range of all keys
-        if (tid == 0) rec[blockIdx.x] = make_uint4(kTopKey, 0xFFFFFFFFu, kmin, kmax);
+        reserve_tail(kTopKey, -1);                      // nothing reserved
         return;
     }
 
@@ -524,33 +565,7 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             __syncthreads();
             sh = need_eq == 0u ? -1 : (int)s_T;
         }
-        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-        for (int c = 0; c < KPT; ++c) {
-            const uint32_t k = key[c];
-            const bool res = k > th || (k == th && seg0 + 64 * c <= sh);
-            if (k != 0u && !res) {
-                lo = min(lo, k);
-                hi = max(hi, k);
-            }
-        }
-        lo = wave_min(lo);
-        hi = wave_max(hi);
-        __syncthreads();
-        if (lane == 0) {
-            s_wa[wave] = lo;
-            s_wb[wave] = hi;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            for (int x = 1; x < kW; ++x) {
-                lo = min(lo, s_wa[x]);
-                hi = max(hi, s_wb[x]);
-            }
-            lo = min(lo, s_wa[0]);
-            hi = max(hi, s_wb[0]);
-            rec[blockIdx.x] = make_uint4(th, (uint32_t)sh, lo, hi);
-        }
+        reserve_tail(th, sh);
         return;
     }
 
@@ -628,19 +643,21 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
 // and the lowest slots among the keys equal to it.  So the reserved set is
 // a pointwise test and needs no flag array.
 //
-// The layer-wide threshold is an offset radix select (12-bit digits, as in
-// the register-resident kernel) over the layer's unreserved keys, spread
-// over one workgroup per head so that every compute unit works: each pass
-// is one launch in which every head histograms its own unreserved keys into
-// a histogram of its own in the workspace; the next launch sums the layer's
-// histograms (every workgroup of the layer does the same sum and takes the
-// same decision) and picks the digit.  Three passes cover any key range
-// (12 + 12 + 8 bits).  When equal keys straddle the threshold, the bin
-// counts of the deciding pass give each head's equal keys, handed out in
-// head order.
-//   shared_reserve_kernel  (Th, Sh) and the range of the unreserved keys
-//   shared_pass_kernel     decide the previous pass, histogram the next
-//   shared_write_kernel    decide the last pass, write each head's list
+// The layer-wide threshold is a radix select (12-bit digits) over the
+// layer's unreserved keys, spread over one workgroup per head so that every
+// compute unit works: in each pass every head histograms its own unreserved
+// keys into a histogram of its own in the workspace, and the next launch
+// sums the layer's histograms (every workgroup of the layer does the same
+// sum and takes the same decision) and picks the digit.  The digits are the
+// key's bits 31..20, 19..8 and 7..0, so the first needs no key range and is
+// histogrammed by the reserve step itself.  When equal keys straddle the
+// threshold, the bin counts of the deciding pass give each head's equal
+// keys, handed out in head order.
+//   select_reg_kernel<.., true> / shared_reserve_kernel
+//                          (Th, Sh), the range and the first-digit histogram
+//                          of the unreserved keys
+//   shared_pass_kernel     (twice) decide the previous digit, histogram the next
+//   shared_write_kernel    decide the last digit, write each head's list
 
 constexpr int kMaxSharedHeads = 128;
 constexpr int kSharedBins = 1 << kRegDigitBits;
@@ -726,9 +743,11 @@ __device__ __forceinline__ void for_head_keys(const float* sc, int n, int tid, F
 // (min > max when nothing is unreserved).
 __global__ __launch_bounds__(kBlock) void shared_reserve_kernel(
     const float* __restrict__ scores, int stride, const int32_t* __restrict__ head_len,
-    int total, int floor_, const int32_t* __restrict__ kept, uint4* __restrict__ rec)
+    int total, int floor_, const int32_t* __restrict__ kept, uint4* __restrict__ rec,
+    uint32_t* __restrict__ hist_out)
 {
     __shared__ uint32_t s_w[kWaves];
+    __shared__ uint32_t lhist[1 << kRegDigitBits];
     const int head = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -755,15 +774,20 @@ __global__ __launch_bounds__(kBlock) void shared_reserve_kernel(
         }
         sh = (int)block_max((uint32_t)(mx + 1), s_w, lane, wave) - 1;
     }
+    for (int b = tid; b < (1 << kRegDigitBits); b += kBlock) lhist[b] = 0u;
+    __syncthreads();
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for_head_keys(sc, n, tid, [&](int i, uint32_t key) {
         if (!is_reserved(key, i, th, sh)) {
             lo = min(lo, key);
             hi = max(hi, key);
+            atomicAdd(&lhist[key >> (32 - kRegDigitBits)], 1u);
         }
     });
     lo = block_min(lo, s_w, lane, wave);
     hi = block_max(hi, s_w, lane, wave);
+    for (int b = tid; b < (1 << kRegDigitBits); b += kBlock)
+        hist_out[(size_t)head * (1 << kRegDigitBits) + b] = lhist[b];
     if (tid == 0) rec[head] = make_uint4(th, (uint32_t)sh, lo, hi);
 }
 
@@ -800,8 +824,10 @@ __device__ __forceinline__ LayerState layer_init(const uint4* __restrict__ rec_l
         S.need_eq = S.rem;
         S.res_pass = 0u;
     } else {
-        S.base = lo;
-        S.wb = (uint32_t)(32 - __clz((int)(hi - lo)));
+        // the first digit is the top 12 bits of the key: the reserve step
+        // has already histogrammed it, with no range needed
+        S.base = 0u;
+        S.wb = 32u;
     }
     return S;
 }
@@ -819,6 +845,10 @@ __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
     // thread t sums bins t + j*kBlock over the heads, eight heads' loads in
     // flight at a time (the sums are latency-bound, not bandwidth-bound)
     constexpr int kBinsPerThread = kSharedBins / kBlock;
+    // a buffer resource over the layer's histograms: the head offset goes in
+    // the scalar offset, so every load shares one per-lane offset register
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)hist_l, 0, n_kv * kSharedBins * 4, kBufferWord3);
     uint32_t acc[kBinsPerThread];
 #pragma unroll
     for (int j = 0; j < kBinsPerThread; ++j) acc[j] = 0u;
@@ -830,7 +860,9 @@ __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
 #pragma unroll
             for (int j = 0; j < kBinsPerThread; ++j) {
                 const uint32_t b = (uint32_t)(tid + j * kBlock);
-                v[u][j] = b < nbins ? hist_l[(size_t)(h + u) * kSharedBins + b] : 0u;
+                v[u][j] = b < nbins ? __builtin_amdgcn_raw_buffer_load_b32(
+                                          rh, (int)(b * 4), (h + u) * kSharedBins * 4, 0)
+                                    : 0u;
             }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -841,7 +873,9 @@ __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
 #pragma unroll
         for (int j = 0; j < kBinsPerThread; ++j) {
             const uint32_t b = (uint32_t)(tid + j * kBlock);
-            acc[j] += b < nbins ? hist_l[(size_t)h * kSharedBins + b] : 0u;
+            acc[j] += b < nbins ? __builtin_amdgcn_raw_buffer_load_b32(rh, (int)(b * 4),
+                                                                        h * kSharedBins * 4, 0)
+                                : 0u;
         }
 #pragma unroll
     for (int j = 0; j < kBinsPerThread; ++j) {
@@ -870,8 +904,8 @@ __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
     __syncthreads();                     // lhist and s_dig are reused
 }
 
-// Launch `pass` (1..3): decide pass-1 (or set up the layer when pass == 1),
-// then histogram this head's unreserved keys for pass `pass`.
+// Launch `pass` (2 or 3): decide pass - 1 (pass 1's histograms come from the
+// reserve step), then histogram this head's unreserved keys for pass `pass`.
 __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
     int pass, const float* __restrict__ scores, int stride, int n_layers, int n_kv,
     const int32_t* __restrict__ head_len, int total, int floor_, int window,
@@ -886,18 +920,17 @@ __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const size_t heads = (size_t)n_layers * (size_t)n_kv;
-    LayerState S;
-    if (pass == 1) {
-        S = layer_init(rec + (size_t)layer * n_kv, head_len ? head_len + (size_t)layer * n_kv : nullptr,
-                       stride, n_kv, total, floor_, window);
-    } else {
-        S = state[(size_t)(pass - 2) * n_layers + layer];
-        if (!S.done)
-            layer_resolve(S, (uint32_t)(pass - 1),
-                          hist + (size_t)((pass - 2) & 1) * heads * kSharedBins +
-                              (size_t)layer * n_kv * kSharedBins,
-                          n_kv, lhist, s_run, s_dig, tid, lane, wave);
-    }
+    // the state before pass - 1: set up from the reserve step (pass 2) or
+    // stored by the previous launch
+    LayerState S = pass == 2
+        ? layer_init(rec + (size_t)layer * n_kv, head_len ? head_len + (size_t)layer * n_kv : nullptr,
+                     stride, n_kv, total, floor_, window)
+        : state[(size_t)(pass - 2) * n_layers + layer];
+    if (!S.done)
+        layer_resolve(S, (uint32_t)(pass - 1),
+                      hist + (size_t)((pass - 2) & 1) * heads * kSharedBins +
+                          (size_t)layer * n_kv * kSharedBins,
+                      n_kv, lhist, s_run, s_dig, tid, lane, wave);
     if (h == 0 && tid == 0) state[(size_t)(pass - 1) * n_layers + layer] = S;
     if (S.done) return;
 
@@ -1030,7 +1063,9 @@ __global__ __launch_bounds__(kBlock) void shared_write_kernel(
             gt_all += s_wgt[x];
             eq_all += s_weq[x];
         }
-#pragma unroll
+        // a partly unrolled sweep: a full unroll keeps every ballot mask of
+        // the 32 rounds live at once and spills scalar registers
+#pragma unroll 4
         for (int c = 0; c < KPT; ++c) {
             const bool gt = (gtb >> c) & 1u;
             const bool eq = (eqb >> c) & 1u;
@@ -1152,7 +1187,7 @@ hipError_t launch_select_shared(const float* scores, int stride, int n_layers, i
         // register-resident: the floor selection writes the reserved sets directly
 #define TRI_RESERVE(KPT)                                                                          \
         hipLaunchKernelGGL((select_reg_kernel<KPT, kBlock, true>), grid, block, 0, stream, scores, \
-                           stride, floor_, nullptr, 0, head_len, rec)
+                           stride, floor_, nullptr, 0, head_len, rec, hist)
         if (stride <= kBlock * 8) TRI_RESERVE(8);
         else if (stride <= kBlock * 16) TRI_RESERVE(16);
         else TRI_RESERVE(32);
@@ -1165,11 +1200,11 @@ hipError_t launch_select_shared(const float* scores, int stride, int n_layers, i
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(shared_reserve_kernel, grid, block, 0, stream, scores, stride,
-                           head_len, (int)total, floor_, kept, rec);
+                           head_len, (int)total, floor_, kept, rec, hist);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    for (int pass = 1; pass <= 3; ++pass) {
+    for (int pass = 2; pass <= 3; ++pass) {
         hipLaunchKernelGGL(shared_pass_kernel, grid, block, 0, stream, pass, scores, stride,
                            n_layers, n_kv, head_len, (int)total, floor_, window,
                            static_cast<const uint4*>(rec), hist, state);
