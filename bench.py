@@ -298,8 +298,9 @@ def main():
         summarize_pmc(args.summarize_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the pass is independent per "
-              "(sequence, layer, KV head) and needs no collectives); run with --gpus 1",
+        print("bench.py measures one GPU: the pass is independent per (sequence, layer, "
+              "KV head) and needs no collectives, so N GPUs each run this on their own share; "
+              "run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
