@@ -690,13 +690,6 @@ __device__ __forceinline__ bool is_reserved(uint32_t key, int i, uint32_t th, in
     return key > th || (key == th && i <= sh);
 }
 
-__device__ __forceinline__ int wave_max_i(int v)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
-}
-
 // Block-wide min / max over uint32 (every thread gets the result).
 __device__ __forceinline__ uint32_t block_min(uint32_t v, uint32_t* s_w, int lane, int wave)
 {
@@ -738,9 +731,11 @@ __device__ __forceinline__ void for_head_keys(const float* sc, int n, int tid, F
     }
 }
 
-// One workgroup per head: (Th, Sh) from the head's reserved list and the
-// key range of its unreserved keys -> rec[head] = {Th, Sh, min, max}
-// (min > max when nothing is unreserved).
+// Heads of more than 32768 keys: one workgroup per head takes (Th, Sh) from
+// the head's reserved list (written by the list-making selection) and writes
+// rec[head] = {Th, Sh, min, max} of its unreserved keys (min > max when there
+// are none) and their first-digit histogram, as the register-resident
+// reserve step does.
 __global__ __launch_bounds__(kBlock) void shared_reserve_kernel(
     const float* __restrict__ scores, int stride, const int32_t* __restrict__ head_len,
     int total, int floor_, const int32_t* __restrict__ kept, uint4* __restrict__ rec,
