@@ -173,6 +173,7 @@ def summarize_pmc(directory: str):
         return out
 
     res = {}
+    others = {}          # the step's other kernels, by name: counter -> values
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         score, copy = [], []
         for r in rows(counter):
@@ -181,6 +182,10 @@ def summarize_pmc(directory: str):
                 score.append(float(r["Counter_Value"]))
             elif "copyBuffer" in name:
                 copy.append(float(r["Counter_Value"]))
+            else:
+                for k in ("select_reg_kernel", "compact_kernel"):
+                    if k in name:
+                        others.setdefault(k, {}).setdefault(counter, []).append(float(r["Counter_Value"]))
         # the 1 GiB copy is the run's only large copy: its counter is the largest
         res[counter] = {"score": float(np.median(score)), "copy": max(copy)}
     copy_bytes = float(1 << 30)
@@ -192,7 +197,10 @@ def summarize_pmc(directory: str):
            "fetch_kib_raw": res["FETCH_SIZE"]["score"], "write_kib_raw": res["WRITE_SIZE"]["score"],
            "copy_fetch_kib_raw": res["FETCH_SIZE"]["copy"], "copy_write_kib_raw": res["WRITE_SIZE"]["copy"],
            "fetch_scale": f_scale, "write_scale": w_scale,
-           "traffic_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write}
+           "traffic_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+           "other_kernels": {k: {"fetch_bytes": float(np.median(v["FETCH_SIZE"])) * 1024.0 * f_scale,
+                                 "write_bytes": float(np.median(v["WRITE_SIZE"])) * 1024.0 * w_scale}
+                             for k, v in others.items() if "FETCH_SIZE" in v and "WRITE_SIZE" in v}}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
