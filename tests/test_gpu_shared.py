@@ -567,3 +567,89 @@ def test_shared_calls_reject_bad_arguments():
     assert lib.tri_select_shared(big.handle, arr, 0, None, 1, 0, 0, None, None, None, 0,
                                  None) == tri.TRI_E_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+def test_shared_prune_then_append_then_prune(orc):
+    """Two prune cycles with head-specific budgets and a decode window between
+    them: after the first prune the heads hold different lengths; 128 new
+    keys are appended to every head at its own length; the second prune runs
+    on that ragged cache.  Every step is replayed by the oracle from the same
+    inputs (its own scores, selection and gather), and the final K, V,
+    positions and lengths are compared bit for bit."""
+    L, H1, n, W, B, F = 2, 8, 3000, 128, 256, 32
+    total = B * H1
+    spec = synth.workload("llama8b").replace(name="append", n_layers=L, lengths=(n, W))
+    pos_new = np.arange(n, n + W)
+    cache = synth.make_cache(spec, "cuda", seed=8, positions=[np.arange(n), pos_new],
+                             p_now=[n - 1, n + W - 1], caps=[n + W, W])
+    cal = cache.calib
+    om = orc.omega(spec.head_dim, spec.rope_theta)
+    K, V, P = cache.k[0], cache.v[0], cache.pos[0]
+    Kn, Vn = cache.k[1][:, :, :W].clone(), cache.v[1][:, :, :W].clone()
+    host = {"K": K[:, :, :n].float().cpu().numpy(), "Kb": K[:, :, :n].cpu(),
+            "V": V[:, :, :n].cpu(), "P": P[:, :, :n].cpu().numpy()}
+    Kn_f, Kn_b, Vn_h = Kn.float().cpu().numpy(), Kn.cpu(), Vn.cpu()
+    ctx = ctx_for(cache)
+    head_len = torch.full((L, H1), n, dtype=torch.int32, device="cuda")
+    kept = torch.empty(L * H1 * total, dtype=torch.int32, device="cuda")
+    counts = torch.empty(L * H1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(tri.select_shared_workspace_bytes(ctx, 1), dtype=torch.uint8, device="cuda")
+    cws = torch.empty(tri.compact_counts_workspace_bytes(ctx), dtype=torch.uint8, device="cuda")
+
+    def gpu_prune(length, p_now):
+        seq = tri.Seq(K, V, P, length, p_now, head_len)
+        scores = torch.empty(L * H1 * length, device="cuda")
+        tri.prune_step_shared(ctx, [seq], B, F, 0, scores, kept, counts, ws, cws)
+        torch.cuda.synchronize()
+
+    def oracle_prune(rows_f, rows_k, rows_v, rows_p, p_now, l):
+        """rows_*[h]: the head's rows (fp32 view, stored dtype, V, positions)."""
+        lens = [len(r) for r in rows_p]
+        stride = max(lens)
+        S = np.full((H1, stride), -np.inf)
+        Pm = np.zeros((H1, stride), dtype=np.int64)
+        for h in range(H1):
+            args = (cal.qc_re[l, h], cal.qc_im[l, h], cal.q_mean_norm[l, h], cal.q_mrl[l, h])
+            _, _, S[h, :lens[h]] = orc.score_head(rows_f[h], rows_p[h], p_now, om, cal.offsets, *args)
+            Pm[h, :lens[h]] = rows_p[h]
+        sel = orc.select_shared(S, Pm, lens, total, F, 0)
+        assert sel is not None
+        take = lambda x, k: x[torch.from_numpy(k).long()] if torch.is_tensor(x) else x[k]
+        return ([take(rows_f[h], sel[h]) for h in range(H1)], [take(rows_k[h], sel[h]) for h in range(H1)],
+                [take(rows_v[h], sel[h]) for h in range(H1)], [take(rows_p[h], sel[h]) for h in range(H1)])
+
+    # first prune
+    gpu_prune(n, n - 1)
+    hl1 = head_len.cpu().numpy().copy()
+    # decode window: 128 new keys per head at the head's own length
+    for l in range(L):
+        for h in range(H1):
+            c = int(hl1[l, h])
+            K[l, h, c:c + W] = Kn[l, h]
+            V[l, h, c:c + W] = Vn[l, h]
+            P[l, h, c:c + W] = torch.from_numpy(pos_new).to(torch.int32).cuda()
+    head_len += W
+    assert int(head_len.max()) <= n + W
+    # second prune on the ragged cache
+    gpu_prune(n + W, n + W - 1)
+    hl2 = head_len.cpu().numpy()
+
+    for l in range(L):
+        f1, k1, v1, p1 = oracle_prune([host["K"][l, h] for h in range(H1)],
+                                      [host["Kb"][l, h] for h in range(H1)],
+                                      [host["V"][l, h] for h in range(H1)],
+                                      [host["P"][l, h] for h in range(H1)], n - 1, l)
+        assert [len(x) for x in p1] == list(hl1[l]), "layer %d: first-prune counts" % l
+        f2in = [np.concatenate([f1[h], Kn_f[l, h]]) for h in range(H1)]
+        k2in = [torch.cat([k1[h], Kn_b[l, h]]) for h in range(H1)]
+        v2in = [torch.cat([v1[h], Vn_h[l, h]]) for h in range(H1)]
+        p2in = [np.concatenate([p1[h], pos_new]) for h in range(H1)]
+        _, k2, v2, p2 = oracle_prune(f2in, k2in, v2in, p2in, n + W - 1, l)
+        for h in range(H1):
+            c = len(p2[h])
+            assert hl2[l, h] == c, "layer %d head %d: final count" % (l, h)
+            np.testing.assert_array_equal(P[l, h, :c].cpu().numpy(), p2[h])
+            assert torch.equal(K[l, h, :c].cpu().view(torch.int16), k2[h].view(torch.int16))
+            assert torch.equal(V[l, h, :c].cpu().view(torch.int16), v2[h].view(torch.int16))
+    say("  two prune cycles agree with the oracle on every head; lengths after the first prune %s"
+        % sorted(set(hl1.reshape(-1).tolist()))[:6])
