@@ -434,3 +434,52 @@ def test_exact_duplicate_rows_keep_the_lower_slot(orc):
         lo, hi = kk[kk < 2000], kk[kk >= 2000] - 2000
         # a kept copy at i + 2000 implies the kept copy at i; B odd splits a pair
         assert set(hi.tolist()) <= set(lo.tolist()) and len(lo) > len(hi)
+
+
+def test_prune_then_append_then_prune(orc):
+    """The decode-time cycle with uniform budgets: prune to B, append a window
+    of 128 new keys (positions past p_now) to every head, prune again.  The
+    oracle replays both prunes from the same inputs; the final K, V and
+    positions are compared bit for bit."""
+    L, H1, n, W, B = 2, 8, 3000, 128, 700
+    spec = synth.workload("llama8b").replace(name="cycle", n_layers=L, lengths=(n, W), budget=B,
+                                             window=W)
+    pos_new = np.arange(n + 5, n + 5 + W)          # a gap, as if a few tokens were dropped
+    cache = synth.make_cache(spec, "cuda", seed=12, positions=[np.arange(n), pos_new],
+                             p_now=[n - 1, int(pos_new[-1])], caps=[n, W])
+    cal = cache.calib
+    om = orc.omega(spec.head_dim, spec.rope_theta)
+    K, V, P = cache.k[0], cache.v[0], cache.pos[0]
+    K0f, K0b, V0, P0 = K.float().cpu().numpy(), K.cpu(), V.cpu(), P.cpu().numpy()
+    Kn, Vn = cache.k[1], cache.v[1]
+    Knf, Knb, Vnh = Kn.float().cpu().numpy(), Kn.cpu(), Vn.cpu()
+    ctx = ctx_for(cache)
+    kept = torch.empty(L * H1 * B, dtype=torch.int32, device="cuda")
+    seq = tri.Seq(K, V, P, n, n - 1)
+    tri.prune_step(ctx, [seq], B, W, torch.empty(L * H1 * n, device="cuda"), kept)
+    torch.cuda.synchronize()
+    assert seq.len == B
+    K[:, :, B:B + W] = Kn
+    V[:, :, B:B + W] = Vn
+    P[:, :, B:B + W] = torch.from_numpy(pos_new).to(torch.int32).cuda()
+    seq = tri.Seq(K, V, P, B + W, int(pos_new[-1]))
+    tri.prune_step(ctx, [seq], B, W - 1, torch.empty(L * H1 * (B + W), device="cuda"), kept)
+    torch.cuda.synchronize()
+    assert seq.len == B
+    for l in range(L):
+        for h in range(H1):
+            args = (cal.qc_re[l, h], cal.qc_im[l, h], cal.q_mean_norm[l, h], cal.q_mrl[l, h])
+            r1 = orc.prune_head(K0f[l, h], bits(V0[l, h]).numpy(), P0[l, h], n - 1, om, cal.offsets,
+                                *args, B, W)
+            k1 = orc.gather_rows(r1["kept"], bits(K0b[l, h]).numpy())
+            f1 = K0f[l, h][r1["kept"]]
+            Kin = np.concatenate([f1, Knf[l, h]])
+            Kin_b = np.concatenate([k1, bits(Knb[l, h]).numpy()])
+            Vin = np.concatenate([r1["V"], bits(Vnh[l, h]).numpy()])
+            Pin = np.concatenate([r1["pos"], pos_new]).astype(np.int32)
+            r2 = orc.prune_head(Kin, Vin, Pin, int(pos_new[-1]), om, cal.offsets, *args, B, W - 1)
+            np.testing.assert_array_equal(P[l, h, :B].cpu().numpy(), r2["pos"])
+            np.testing.assert_array_equal(bits(K[l, h, :B]).cpu().numpy(),
+                                          orc.gather_rows(r2["kept"], Kin_b))
+            np.testing.assert_array_equal(bits(V[l, h, :B]).cpu().numpy(), r2["V"])
+    say("  two uniform prune cycles agree with the oracle on all %d heads" % (L * H1))
