@@ -301,22 +301,6 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nbins,
     }
 }
 
-// Sorts one value per lane of a wave in descending order (bitonic network).
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane)
-{
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint32_t p = (uint32_t)__shfl_xor((int)v, j);
-            const bool first = (lane & k) == 0;        // block sorted descending
-            const bool lower = (lane & j) == 0;        // lower lane of the pair
-            v = (first == lower) ? max(v, p) : min(v, p);
-        }
-    }
-    return v;
-}
-
 // Register-resident variant for heads of at most NT * KPT keys (NT threads):
 // lane l of wave w holds the keys of slots w*64*KPT + c*64 + l, c < KPT,
 // which is the order the output sweep consumes them in.  LDS holds only the
@@ -327,8 +311,10 @@ __device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane)
 // always span the populated key range (the keys of concentrated scores sit
 // in a narrow range, often straddling a power of two, and a bit-aligned
 // digit would pile them into a few bins).  Keys above the chosen bin are
-// kept, keys below it evicted.  Once at most 64 candidates are left, one
-// wave sorts them in registers and reads off the threshold.  The result is
+// kept, keys below it evicted.  The adds of a pass take no branch: keys
+// outside the live range go to a spill bin of their lane.  Once at most 64
+// candidates are left, one wave ranks them (each counts the candidates
+// above it and equal to it) and reads off the threshold.  The result is
 // either "keep every key >= Tlo" (exactly B keys) or, when equal keys
 // straddle the threshold, "keep keys > T and the first need_eq keys == T in
 // slot order".
@@ -349,7 +335,8 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
                                                         uint32_t* __restrict__ hist_out = nullptr)
 {
     constexpr int kW = NT / 64;
-    __shared__ uint32_t hist[1 << kRegDigitBits];
+    // the histogram, then one spill bin per lane (keys outside the live range)
+    __shared__ uint32_t hist[(1 << kRegDigitBits) + 64];
     __shared__ uint32_t s_cand[64];
     __shared__ uint32_t s_wa[kW], s_wb[kW], s_run[kW];
     __shared__ uint32_t s_digit, s_above, s_inbin, s_ncand;
@@ -390,6 +377,8 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             key[c] = seg0 + 64 * c < n ? ordered_key(__uint_as_float(x[c])) : 0u;
     }
 
+    // slots past the head's end (key 0)
+    const uint32_t npad = (uint32_t)(NT * KPT - n);
     uint32_t kmin, kmax;
     {
         uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -474,15 +463,21 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             for (uint32_t b = tid; b < nbins; b += NT) hist[b] = 0u;
             if (tid == 0) s_ncand = 0u;
             __syncthreads();
-            // padding keys (0) are skipped; the comparison value is opaque so
-            // the compiler recomputes the KPT masks per pass instead of
-            // keeping them live in scalar registers across passes
-            uint32_t pad = 0u;
-            asm volatile("" : "+v"(pad));
+            // Every key is added somewhere, with no branch: a key outside the
+            // live range goes to its lane's own spill bin past the histogram
+            // (distinct addresses, so those adds never collide).  Padding
+            // keys (0) lie outside the range unless the range wraps past
+            // 2^32 - 1 to reach 0; then they land in the bin of key 0 and
+            // are taken out again below.
+            const uint32_t spill = (1u << kRegDigitBits) + (uint32_t)lane;
 #pragma unroll
             for (int c = 0; c < KPT; ++c) {
                 const uint32_t off = key[c] - base;
-                if (off <= span && key[c] != pad) atomicAdd(&hist[off >> sh], 1u);
+                atomicAdd(&hist[off <= span ? off >> sh : spill], 1u);
+            }
+            if (npad != 0u && 0u - base <= span) {      // block-uniform
+                __syncthreads();
+                if (tid == 0) hist[(0u - base) >> sh] -= npad;
             }
             __syncthreads();
             find_digit<NT>(hist, nbins, rem, tid, lane, wave, s_run, &s_digit, &s_above, &s_inbin);
@@ -505,8 +500,12 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
                 break;
             }
             if (in_bin <= 64u) {
-                // stage the few candidates and let one wave sort them
+                // stage the few candidates and let one wave rank them
                 const uint32_t cspan = (1u << wb) - 1u;
+                // an opaque zero, so the padding test is made here and not
+                // kept live in scalar registers from elsewhere
+                uint32_t pad = 0u;
+                asm volatile("" : "+v"(pad));
 #pragma unroll
                 for (int c = 0; c < KPT; ++c) {
                     const uint32_t off = key[c] - base;
@@ -517,10 +516,20 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
                 }
                 __syncthreads();
                 if (wave == 0) {
-                    const uint32_t v = wave_sort_desc((uint32_t)lane < in_bin ? s_cand[lane] : 0u, lane);
-                    const uint32_t t = (uint32_t)__shfl((int)v, (int)rem - 1);
-                    const uint32_t g = (uint32_t)__popcll(__ballot(v > t));
-                    const uint32_t e = (uint32_t)__popcll(__ballot(v == t));
+                    // each candidate counts the candidates above it and equal
+                    // to it; the rem-th largest is one with gt < rem <= gt + eq
+                    const uint32_t v = (uint32_t)lane < in_bin ? s_cand[lane] : 0u;
+                    uint32_t gt = 0u, eq = 0u;
+                    for (uint32_t j = 0; j < in_bin; ++j) {
+                        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)j);
+                        gt += o > v ? 1u : 0u;
+                        eq += o == v ? 1u : 0u;
+                    }
+                    const bool hit = (uint32_t)lane < in_bin && gt < rem && rem <= gt + eq;
+                    const int src = __ffsll((unsigned long long)__ballot(hit)) - 1;   // one exists
+                    const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+                    const uint32_t g = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+                    const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)eq, src);
                     if (lane == 0) {
                         s_T = t;
                         s_need = rem - g;
