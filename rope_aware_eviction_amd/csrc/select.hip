@@ -61,25 +61,58 @@ __device__ __forceinline__ uint32_t key_at(const uint32_t* lds_keys, const float
     else return ordered_key(sc[i]);
 }
 
+// Wave-wide reductions and scan (every lane active).  DPP moves inside each
+// 16-lane row (quad permutations, then the half-row and row mirrors pair
+// every lane with one of the other half), then the four row results are
+// combined from scalar registers: no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ uint32_t lane_u(uint32_t x, int l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op)
+{
+    v = op(v, dpp_u<0xB1>(v));                  // quad_perm [1,0,3,2]
+    v = op(v, dpp_u<0x4E>(v));                  // quad_perm [2,3,0,1]
+    v = op(v, dpp_u<0x141>(v));                 // row_half_mirror
+    v = op(v, dpp_u<0x140>(v));                 // row_mirror: the row's result in every lane
+    return op(op(lane_u(v, 0), lane_u(v, 16)), op(lane_u(v, 32), lane_u(v, 48)));
+}
+
 __device__ __forceinline__ uint32_t wave_min(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-    return v;
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
-    return v;
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-    return v;
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+
+// Inclusive prefix sum over the lanes of a wave: shift-and-add inside each
+// row (row_shr fills the lanes it shifts past with 0), then the totals of
+// the rows below.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane)
+{
+    x += dpp_u<0x111>(x);                       // row_shr:1
+    x += dpp_u<0x112>(x);                       // row_shr:2
+    x += dpp_u<0x114>(x);                       // row_shr:4
+    x += dpp_u<0x118>(x);                       // row_shr:8
+    const uint32_t r0 = lane_u(x, 15), r1 = lane_u(x, 31), r2 = lane_u(x, 47);
+    const int row = lane >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
 template <bool kInLds>
@@ -175,12 +208,7 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict_
                 uint32_t sum = 0u;
                 if (hi < nbins)
                     for (uint32_t t = 0; t < per; ++t) sum += hist[nbins - 1u - hi - t];
-                uint32_t incl = sum;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t v = (uint32_t)__shfl_up((int)incl, o);
-                    if (lane >= o) incl += v;
-                }
+                const uint32_t incl = wave_incl_scan(sum, lane);
                 const unsigned long long hit = __ballot(incl >= rem);
                 const int L = __ffsll((long long)hit) - 1;
                 if (lane == L) {
@@ -275,12 +303,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nbins,
     uint32_t sum = 0u;
     if (active)
         for (uint32_t t = 0; t < per; ++t) sum += hist[nbins - 1u - first - t];
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = (uint32_t)__shfl_up((int)incl, o);
-        if (lane >= o) incl += v;
-    }
+    uint32_t incl = wave_incl_scan(sum, lane);
     if (lane == 63) s_run[wave] = incl;
     __syncthreads();
     for (int x = 0; x < wave; ++x) incl += s_run[x];
