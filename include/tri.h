@@ -287,8 +287,9 @@ tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, in
                           const int32_t* kept, int32_t budget, int32_t window, void* stream);
 
 /* Device workspace bytes tri_select_shared needs: per sequence, 16 bytes
- * and two 16 KB histograms per (layer, KV head) plus 192 bytes per layer,
- * rounded up (9.4 MB for 36 layers x 8 KV heads).  -1 on bad arguments. */
+ * and two histogram rows of 16,640 bytes per (layer, KV head) plus 192 bytes
+ * per layer, rounded up (9.6 MB for 36 layers x 8 KV heads).  -1 on bad
+ * arguments. */
 int64_t tri_select_shared_workspace_bytes(const tri_ctx* ctx, int32_t n_seq);
 
 /*

@@ -34,6 +34,9 @@ constexpr uint32_t kTopKey = 0xFFFFFFFFu;
 constexpr int kHistBins = 1 << kMaxDigitBits;
 // digit width of the register-resident selection's histogram passes
 constexpr int kRegDigitBits = 12;
+// a per-head histogram row in the shared-budget workspace: the 4096 bins,
+// then the sums of their 64 groups of 64 consecutive bins
+constexpr int kHistRow = (1 << kRegDigitBits) + 64;
 // keys of a head staged in LDS up to this many (4 bytes each, plus the
 // 8 KB histogram, within the 160 KB LDS of a gfx950 workgroup)
 constexpr int kLdsKeysMax = 36864;
@@ -99,6 +102,26 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 __device__ __forceinline__ uint32_t wave_max(uint32_t v)
 {
     return wave_reduce(v, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+
+// The 64 group sums of an LDS histogram of nbins <= 4096 bins, out[g] =
+// bins [64g, 64g + 64) below nbins.  Every thread of a 1024-thread workgroup
+// calls it once the histogram is complete: thread t adds bins 4t..4t+3, and
+// the 16 threads of a DPP row add their sums.
+__device__ __forceinline__ void write_group_sums(const uint32_t* h, uint32_t nbins, uint32_t* out,
+                                                 int tid)
+{
+    uint32_t p = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t b = 4u * (uint32_t)tid + (uint32_t)j;
+        p += b < nbins ? h[b] : 0u;
+    }
+    p += dpp_u<0xB1>(p);
+    p += dpp_u<0x4E>(p);
+    p += dpp_u<0x141>(p);
+    p += dpp_u<0x140>(p);
+    if ((tid & 15) == 0) out[tid >> 4] = p;
 }
 
 // Inclusive prefix sum over the lanes of a wave: shift-and-add inside each
@@ -371,8 +394,8 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
     if (n <= budget) {
         // RESERVE: every key is reserved (Th = 0 lies below every real key)
         if constexpr (RESERVE) {
-            for (int b = threadIdx.x; b < (1 << kRegDigitBits); b += NT)
-                hist_out[(size_t)blockIdx.x * (1 << kRegDigitBits) + b] = 0u;
+            for (int b = threadIdx.x; b < kHistRow; b += NT)
+                hist_out[(size_t)blockIdx.x * kHistRow + b] = 0u;
             if (threadIdx.x == 0) rec[blockIdx.x] = make_uint4(0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0u);
         }
         return;
@@ -449,8 +472,10 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             s_wb[wave] = hi;
         }
         __syncthreads();
-        uint32_t* ho = hist_out + (size_t)blockIdx.x * (1 << kRegDigitBits);
+        uint32_t* ho = hist_out + (size_t)blockIdx.x * kHistRow;
         for (uint32_t b = tid; b < (1u << kRegDigitBits); b += NT) ho[b] = hist[b];
+        static_assert(!RESERVE || NT == 1024, "group sums assume 1024 threads");
+        write_group_sums(hist, 1u << kRegDigitBits, ho + (1 << kRegDigitBits), tid);
         if (tid == 0) {
             for (int x = 0; x < kW; ++x) {
                 lo = min(lo, s_wa[x]);
@@ -678,9 +703,11 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
 // The layer-wide threshold is a radix select (12-bit digits) over the
 // layer's unreserved keys, spread over one workgroup per head so that every
 // compute unit works: in each pass every head histograms its own unreserved
-// keys into a histogram of its own in the workspace, and the next launch
-// sums the layer's histograms (every workgroup of the layer does the same
-// sum and takes the same decision) and picks the digit.  The digits are the
+// keys into a histogram of its own in the workspace, with the sums of its
+// 64-bin groups, and the next launch adds up the layer's histograms (every
+// workgroup of the layer does the same sums and takes the same decision):
+// first the group sums, to find the group of the deciding digit, then the
+// 64 bins of that group.  The digits are the
 // key's bits 31..20, 19..8 and 7..0, so the first needs no key range and is
 // histogrammed by the reserve step itself.  When equal keys straddle the
 // threshold, the bin counts of the deciding pass give each head's equal
@@ -813,8 +840,9 @@ __global__ __launch_bounds__(kBlock) void shared_reserve_kernel(
     });
     lo = block_min(lo, s_w, lane, wave);
     hi = block_max(hi, s_w, lane, wave);
-    for (int b = tid; b < (1 << kRegDigitBits); b += kBlock)
-        hist_out[(size_t)head * (1 << kRegDigitBits) + b] = lhist[b];
+    uint32_t* ho = hist_out + (size_t)head * kHistRow;
+    for (int b = tid; b < (1 << kRegDigitBits); b += kBlock) ho[b] = lhist[b];
+    write_group_sums(lhist, 1u << kRegDigitBits, ho + (1 << kRegDigitBits), tid);
     if (tid == 0) rec[head] = make_uint4(th, (uint32_t)sh, lo, hi);
 }
 
@@ -859,59 +887,56 @@ __device__ __forceinline__ LayerState layer_init(const uint4* __restrict__ rec_l
     return S;
 }
 
-// Decides pass `pass` from the layer's per-head histograms (hist_l: n_kv
-// rows of kSharedBins).  Every thread of the workgroup calls it.
+// Decides pass `pass` from the layer's per-head histogram rows (hist_l:
+// n_kv rows of kHistRow).  Every thread of the workgroup calls it; wave 0
+// finds the digit in two steps, each a 64-lane scan counted from the top:
+// the group of 64 bins that holds the rem-th key (from the rows' group
+// sums), then the bin inside it, so a workgroup reads 2 x 64 x n_kv words
+// of the rows instead of all 4096 x n_kv.
 __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
                                               const uint32_t* __restrict__ hist_l, int n_kv,
-                                              uint32_t* lhist, uint32_t* s_run, uint32_t* s_dig,
-                                              int tid, int lane, int wave)
+                                              uint32_t* s_dig, int lane, int wave)
 {
     const int nb = min(kRegDigitBits, (int)S.wb);
     const int shift = (int)S.wb - nb;
     const uint32_t nbins = 1u << nb;
-    // thread t sums bins t + j*kBlock over the heads, eight heads' loads in
-    // flight at a time (the sums are latency-bound, not bandwidth-bound)
-    constexpr int kBinsPerThread = kSharedBins / kBlock;
-    // a buffer resource over the layer's histograms: the head offset goes in
-    // the scalar offset, so every load shares one per-lane offset register
-    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)hist_l, 0, n_kv * kSharedBins * 4, kBufferWord3);
-    uint32_t acc[kBinsPerThread];
+    if (wave == 0) {
+        // the n_kv rows' words at one column, summed (loads in flight 8 at a time)
+        auto column = [&](uint32_t col, bool live) {
+            uint32_t acc = 0u;
+            int h = 0;
+            for (; h + 8 <= n_kv; h += 8) {
+                uint32_t v[8];
 #pragma unroll
-    for (int j = 0; j < kBinsPerThread; ++j) acc[j] = 0u;
-    int h = 0;
-    for (; h + 8 <= n_kv; h += 8) {
-        uint32_t v[8][kBinsPerThread];
+                for (int u = 0; u < 8; ++u) v[u] = live ? hist_l[(size_t)(h + u) * kHistRow + col] : 0u;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int j = 0; j < kBinsPerThread; ++j) {
-                const uint32_t b = (uint32_t)(tid + j * kBlock);
-                v[u][j] = b < nbins ? __builtin_amdgcn_raw_buffer_load_b32(
-                                          rh, (int)(b * 4), (h + u) * kSharedBins * 4, 0)
-                                    : 0u;
+                for (int u = 0; u < 8; ++u) acc += v[u];
             }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int j = 0; j < kBinsPerThread; ++j) acc[j] += v[u][j];
-    }
-    for (; h < n_kv; ++h)
-#pragma unroll
-        for (int j = 0; j < kBinsPerThread; ++j) {
-            const uint32_t b = (uint32_t)(tid + j * kBlock);
-            acc[j] += b < nbins ? __builtin_amdgcn_raw_buffer_load_b32(rh, (int)(b * 4),
-                                                                        h * kSharedBins * 4, 0)
-                                : 0u;
+            for (; h < n_kv; ++h) acc += live ? hist_l[(size_t)h * kHistRow + col] : 0u;
+            return acc;
+        };
+        // lane j: group 63 - j (groups past nbins sum to 0)
+        const uint32_t g = 63u - (uint32_t)lane;
+        const uint32_t cg_sum = column((uint32_t)kSharedBins + g, true);
+        const uint32_t cg_incl = wave_incl_scan(cg_sum, lane);
+        const int lg = __ffsll((unsigned long long)__ballot(cg_incl >= S.rem)) - 1;
+        const uint32_t grp = 63u - (uint32_t)lg;
+        const uint32_t above_g = lane_u(cg_incl - cg_sum, lg);
+        // lane j: bin 64 * grp + 63 - j
+        const uint32_t bin = 64u * grp + 63u - (uint32_t)lane;
+        const uint32_t b_sum = column(bin, bin < nbins);
+        const uint32_t b_incl = wave_incl_scan(b_sum, lane);
+        const int lb = __ffsll((unsigned long long)__ballot(above_g + b_incl >= S.rem)) - 1;
+        // lane reads with every lane active (a value computed under a
+        // one-lane mask would hold garbage in the other lanes)
+        const uint32_t above_b = lane_u(b_incl - b_sum, lb);
+        const uint32_t in_b = lane_u(b_sum, lb);
+        if (lane == 0) {
+            s_dig[0] = 64u * grp + 63u - (uint32_t)lb;
+            s_dig[1] = above_g + above_b;
+            s_dig[2] = in_b;
         }
-#pragma unroll
-    for (int j = 0; j < kBinsPerThread; ++j) {
-        const uint32_t b = (uint32_t)(tid + j * kBlock);
-        if (b < nbins) lhist[b] = acc[j];
     }
-    __syncthreads();
-    find_digit<kBlock>(lhist, nbins, S.rem, tid, lane, wave, s_run, &s_dig[0], &s_dig[1],
-                       &s_dig[2]);
     __syncthreads();
     const uint32_t d = s_dig[0] & (nbins - 1u);
     const uint32_t in_bin = s_dig[2];
@@ -928,7 +953,7 @@ __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
     S.need_eq = straddle ? S.rem : S.need_eq;
     S.res_pass = straddle ? pass : S.res_pass;
     S.eq_bin = straddle ? d : S.eq_bin;
-    __syncthreads();                     // lhist and s_dig are reused
+    __syncthreads();                     // s_dig is reused
 }
 
 // Launch `pass` (2 or 3): decide pass - 1 (pass 1's histograms come from the
@@ -939,7 +964,7 @@ __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
     const uint4* __restrict__ rec, uint32_t* __restrict__ hist, LayerState* __restrict__ state)
 {
     __shared__ uint32_t lhist[kSharedBins];
-    __shared__ uint32_t s_run[kWaves], s_dig[3];
+    __shared__ uint32_t s_dig[3];
     const int head = blockIdx.x;
     const int layer = head / n_kv;
     const int h = head - layer * n_kv;
@@ -955,9 +980,9 @@ __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
         : state[(size_t)(pass - 2) * n_layers + layer];
     if (!S.done)
         layer_resolve(S, (uint32_t)(pass - 1),
-                      hist + (size_t)((pass - 2) & 1) * heads * kSharedBins +
-                          (size_t)layer * n_kv * kSharedBins,
-                      n_kv, lhist, s_run, s_dig, tid, lane, wave);
+                      hist + (size_t)((pass - 2) & 1) * heads * kHistRow +
+                          (size_t)layer * n_kv * kHistRow,
+                      n_kv, s_dig, lane, wave);
     if (h == 0 && tid == 0) state[(size_t)(pass - 1) * n_layers + layer] = S;
     if (S.done) return;
 
@@ -977,8 +1002,9 @@ __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
         if (off <= span && !is_reserved(key, i, th, sh)) atomicAdd(&lhist[off >> shift], 1u);
     });
     __syncthreads();
-    uint32_t* out = hist + (size_t)((pass - 1) & 1) * heads * kSharedBins + (size_t)head * kSharedBins;
+    uint32_t* out = hist + (size_t)((pass - 1) & 1) * heads * kHistRow + (size_t)head * kHistRow;
     for (uint32_t b = tid; b < nbins; b += kBlock) out[b] = lhist[b];
+    write_group_sums(lhist, nbins, out + kSharedBins, tid);
 }
 
 // One workgroup per head: decide the last pass if needed, then the kept list
@@ -994,8 +1020,7 @@ __global__ __launch_bounds__(kBlock) void shared_write_kernel(
     const uint32_t* __restrict__ hist, const LayerState* __restrict__ state,
     int32_t* __restrict__ kept, int32_t* __restrict__ kept_count)
 {
-    __shared__ uint32_t lhist[kSharedBins];
-    __shared__ uint32_t s_run[kWaves], s_dig[3];
+    __shared__ uint32_t s_dig[3];
     __shared__ uint32_t s_wgt[kWaves], s_weq[kWaves];
     const int lh = blockIdx.x;
     const int layer = lh / n_kv;
@@ -1006,8 +1031,7 @@ __global__ __launch_bounds__(kBlock) void shared_write_kernel(
     const size_t heads = (size_t)n_layers * (size_t)n_kv;
     LayerState S = state[(size_t)2 * n_layers + layer];
     if (!S.done)
-        layer_resolve(S, 3u, hist + (size_t)layer * n_kv * kSharedBins, n_kv, lhist, s_run, s_dig,
-                      tid, lane, wave);
+        layer_resolve(S, 3u, hist + (size_t)layer * n_kv * kHistRow, n_kv, s_dig, lane, wave);
     if (!S.fired) {
         if (tid == 0) kept_count[lh] = -1;
         return;
@@ -1016,8 +1040,8 @@ __global__ __launch_bounds__(kBlock) void shared_write_kernel(
     uint32_t take = 0u;
     if (S.tie) {
         const int32_t* hl_l = head_len ? head_len + (size_t)layer * n_kv : nullptr;
-        const uint32_t* bins = hist + (size_t)((S.res_pass - 1u) & 1u) * heads * kSharedBins +
-                               (size_t)layer * n_kv * kSharedBins + S.eq_bin;
+        const uint32_t* bins = hist + (size_t)((S.res_pass - 1u) & 1u) * heads * kHistRow +
+                               (size_t)layer * n_kv * kHistRow + S.eq_bin;
         uint32_t left = S.need_eq;
         for (int h = 0; h <= hh; ++h) {
             uint32_t eq;
@@ -1025,7 +1049,7 @@ __global__ __launch_bounds__(kBlock) void shared_write_kernel(
                 const int n = head_rows(hl_l, h, stride);
                 eq = (uint32_t)(n - min(n, floor_));
             } else {
-                eq = bins[(size_t)h * kSharedBins];
+                eq = bins[(size_t)h * kHistRow];
             }
             const uint32_t t = min(eq, left);
             if (h == hh) take = t;
@@ -1188,7 +1212,7 @@ int64_t shared_workspace_bytes(int64_t n_seq, int64_t n_layers, int64_t n_kv)
 {
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t heads = n_layers * n_kv;
-    return n_seq * (up(heads * 16) + up(2 * heads * kSharedBins * 4) +
+    return n_seq * (up(heads * 16) + up(2 * heads * kHistRow * 4) +
                     up(3 * n_layers * (int64_t)sizeof(LayerState)));
 }
 
@@ -1207,7 +1231,7 @@ hipError_t launch_select_shared(const float* scores, int stride, int n_layers, i
     uint4* rec = reinterpret_cast<uint4*>(ws);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + up(heads * 16));
     LayerState* state = reinterpret_cast<LayerState*>(ws + up(heads * 16) +
-                                                      up(2 * heads * kSharedBins * 4));
+                                                      up(2 * heads * kHistRow * 4));
     const dim3 grid((unsigned)heads), block(kBlock);
     hipError_t e = hipSuccess;
     if (stride <= kBlock * 32) {
