@@ -455,15 +455,15 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
         for (uint32_t b = tid; b < (1u << kRegDigitBits); b += NT) hist[b] = 0u;
         __syncthreads();
         uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        const uint32_t spill = (1u << kRegDigitBits) + (uint32_t)lane;
 #pragma unroll
         for (int c = 0; c < KPT; ++c) {
             const uint32_t k = key[c];
             const bool res = k > th || (k == th && seg0 + 64 * c <= sh);
-            if (k != 0u && !res) {
-                lo = min(lo, k);
-                hi = max(hi, k);
-                atomicAdd(&hist[k >> (32 - kRegDigitBits)], 1u);
-            }
+            const bool live = k != 0u && !res;
+            lo = min(lo, live ? k : 0xFFFFFFFFu);
+            hi = max(hi, live ? k : 0u);
+            atomicAdd(&hist[live ? k >> (32 - kRegDigitBits) : spill], 1u);
         }
         lo = wave_min(lo);
         hi = wave_max(hi);
@@ -958,12 +958,17 @@ __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
 
 // Launch `pass` (2 or 3): decide pass - 1 (pass 1's histograms come from the
 // reserve step), then histogram this head's unreserved keys for pass `pass`.
+// KPT > 0: every thread loads its KPT keys at once (lane l of wave w: slots
+// w*64*KPT + c*64 + l); KPT == 0: batches of kHeadBatch.  Every key is
+// added with no branch: keys outside the live range, reserved keys and
+// slots past the head's end go to the lane's spill bin past the histogram.
+template <int KPT>
 __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
     int pass, const float* __restrict__ scores, int stride, int n_layers, int n_kv,
     const int32_t* __restrict__ head_len, int total, int floor_, int window,
     const uint4* __restrict__ rec, uint32_t* __restrict__ hist, LayerState* __restrict__ state)
 {
-    __shared__ uint32_t lhist[kSharedBins];
+    __shared__ uint32_t lhist[kSharedBins + 64];
     __shared__ uint32_t s_dig[3];
     const int head = blockIdx.x;
     const int layer = head / n_kv;
@@ -997,10 +1002,26 @@ __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
     const int sh = (int)r.y;
     const uint32_t base = S.base;
     const int n = head_rows(head_len, head, stride);
-    for_head_keys(scores + (size_t)head * (size_t)stride, n, tid, [&](int i, uint32_t key) {
+    const float* sc = scores + (size_t)head * (size_t)stride;
+    const uint32_t spill = (uint32_t)kSharedBins + (uint32_t)lane;
+    auto add = [&](int i, uint32_t key) {
         const uint32_t off = key - base;
-        if (off <= span && !is_reserved(key, i, th, sh)) atomicAdd(&lhist[off >> shift], 1u);
-    });
+        const bool live = i < n && off <= span && !is_reserved(key, i, th, sh);
+        atomicAdd(&lhist[live ? off >> shift : spill], 1u);
+    };
+    if constexpr (KPT > 0) {
+        const int seg0 = wave * (64 * KPT) + lane;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)sc, 0, n * 4, kBufferWord3);
+        uint32_t x[KPT];
+#pragma unroll
+        for (int c = 0; c < KPT; ++c)
+            x[c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (seg0 + 64 * c) * 4, 0, 0);
+#pragma unroll
+        for (int c = 0; c < KPT; ++c) add(seg0 + 64 * c, ordered_key(__uint_as_float(x[c])));
+    } else {
+        for_head_keys(sc, n, tid, add);
+    }
     __syncthreads();
     uint32_t* out = hist + (size_t)((pass - 1) & 1) * heads * kHistRow + (size_t)head * kHistRow;
     for (uint32_t b = tid; b < nbins; b += kBlock) out[b] = lhist[b];
@@ -1256,9 +1277,15 @@ hipError_t launch_select_shared(const float* scores, int stride, int n_layers, i
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int pass = 2; pass <= 3; ++pass) {
-        hipLaunchKernelGGL(shared_pass_kernel, grid, block, 0, stream, pass, scores, stride,
-                           n_layers, n_kv, head_len, (int)total, floor_, window,
-                           static_cast<const uint4*>(rec), hist, state);
+#define TRI_PASS(KPT)                                                                             \
+        hipLaunchKernelGGL(shared_pass_kernel<KPT>, grid, block, 0, stream, pass, scores, stride,  \
+                           n_layers, n_kv, head_len, (int)total, floor_, window,                  \
+                           static_cast<const uint4*>(rec), hist, state)
+        if (stride <= kBlock * 8) TRI_PASS(8);
+        else if (stride <= kBlock * 16) TRI_PASS(16);
+        else if (stride <= kBlock * 32) TRI_PASS(32);
+        else TRI_PASS(0);
+#undef TRI_PASS
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
