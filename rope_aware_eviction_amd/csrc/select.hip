@@ -1100,7 +1100,9 @@ __global__ __launch_bounds__(kBlock) void shared_write_kernel(
     if constexpr (KPT > 0) {
         static_assert(KPT <= 32, "one bit per key in a 32-bit mask");
         const int seg0 = wave * (64 * KPT) + lane;
-        // classify every key once; bit c of gtb / eqb is key c's class
+        // classify every key once; bit c of gtb / eqb is key c's class.  The
+        // tests are 0/1 words combined with bit operations, so the sweep is
+        // straight-line code (the same classes as classify below)
         uint32_t gtb = 0u, eqb = 0u;
         {
             const __amdgpu_buffer_rsrc_t rsrc =
@@ -1109,13 +1111,19 @@ __global__ __launch_bounds__(kBlock) void shared_write_kernel(
 #pragma unroll
             for (int c = 0; c < KPT; ++c)
                 x[c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (seg0 + 64 * c) * 4, 0, 0);
+            const uint32_t tie_w = tie ? 1u : 0u;
 #pragma unroll
             for (int c = 0; c < KPT; ++c) {
-                const uint32_t key = seg0 + 64 * c < n ? ordered_key(__uint_as_float(x[c])) : 0u;
-                bool gt, eq;
-                classify(seg0 + 64 * c, key, gt, eq);
-                gtb |= (gt ? 1u : 0u) << c;
-                eqb |= (eq ? 1u : 0u) << c;
+                const int slot = seg0 + 64 * c;
+                const uint32_t key = ordered_key(__uint_as_float(x[c]));
+                const uint32_t real = slot < n ? 1u : 0u;
+                const uint32_t at_th = key == th ? 1u : 0u;
+                const uint32_t low_slot = slot <= sh ? 1u : 0u;
+                const uint32_t res = real & ((key > th ? 1u : 0u) | (at_th & low_slot));
+                const uint32_t at_t = key == T ? 1u : 0u;
+                const uint32_t above = (key > T ? 1u : 0u) | (at_t & (tie_w ^ 1u));
+                gtb |= (res | (real & above)) << c;
+                eqb |= ((res ^ 1u) & real & tie_w & at_t) << c;
             }
         }
         uint32_t cgt = (uint32_t)__popc(gtb), ceq = (uint32_t)__popc(eqb);
