@@ -418,19 +418,22 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
 #pragma unroll
         for (int c = 0; c < KPT; ++c)
             x[c] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (seg0 + 64 * c) * 4, 0, 0);
+        // a mask rather than a select, so the key is computed with no branch
 #pragma unroll
         for (int c = 0; c < KPT; ++c)
-            key[c] = seg0 + 64 * c < n ? ordered_key(__uint_as_float(x[c])) : 0u;
+            key[c] = ordered_key(__uint_as_float(x[c])) & (0u - (seg0 + 64 * c < n ? 1u : 0u));
     }
 
     // slots past the head's end (key 0)
     const uint32_t npad = (uint32_t)(NT * KPT - n);
     uint32_t kmin, kmax;
     {
+        // the minimum of key - 1 skips key 0 (it wraps to the top) with no
+        // comparison; the head has a real key, so adding 1 back is exact
         uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
         for (int c = 0; c < KPT; ++c) {
-            lo = min(lo, key[c] ? key[c] : 0xFFFFFFFFu);
+            lo = min(lo, key[c] - 1u);
             hi = max(hi, key[c]);
         }
         lo = wave_min(lo);
@@ -446,6 +449,7 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             kmin = min(kmin, s_wa[x]);
             kmax = max(kmax, s_wb[x]);
         }
+        kmin += 1u;
     }
 
     // RESERVE: the range and the top-12-bit histogram of the keys outside
