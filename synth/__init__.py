@@ -477,7 +477,10 @@ def make_scores(kind: str, n_heads: int, n: int, seed: int = 0) -> np.ndarray:
     ``dups`` (normal with 30% exact duplicates of other slots),
     ``straddle`` (concentrated around 2.0), ``outlier`` (normal plus one
     +1e30 and one -1e30), ``narrow`` (all within a few ulps of 1.0),
-    ``ulp`` (clusters of values one fp32 ulp apart).
+    ``ulp`` (clusters of values one fp32 ulp apart), ``wide`` (positive
+    values spread over the exponents from 2e-9 to 3e38, with +inf mixed in: the
+    order-preserving keys span more than a quarter of the uint32 range, all in
+    its top half).
     """
     rng = _np_rng(seed, "scores", kind, n_heads, n)
     if kind == "normal":
@@ -516,6 +519,9 @@ def make_scores(kind: str, n_heads: int, n: int, seed: int = 0) -> np.ndarray:
         s = np.take_along_axis(base, idx, axis=1)
         steps = rng.integers(-2, 3, size=(n_heads, n)).astype(np.int32)
         s = (s.view(np.int32) + steps).view(np.float32)
+    elif kind == "wide":
+        s = np.exp(rng.uniform(-20.0, 88.0, size=(n_heads, n))).astype(np.float32)
+        s[rng.random((n_heads, n)) < 0.01] = np.inf
     else:
         raise KeyError(kind)
     return np.ascontiguousarray(s, dtype=np.float32)

@@ -225,6 +225,8 @@ SELECT_CASES = [
     ("normal", 129, 1), ("straddle", 32768, 4096), ("straddle", 20000, 2048),
     ("outlier", 32768, 4096), ("outlier", 7000, 3500), ("narrow", 32768, 4096), ("narrow", 9000, 100),
     ("straddle", 131072, 8192), ("outlier", 36000, 1000),
+    # positive keys whose live range runs past 2^32 - 1, with padding slots
+    ("wide", 5000, 1234), ("wide", 20000, 2048), ("wide", 32768, 4096),
 ]
 
 

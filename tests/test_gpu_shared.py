@@ -109,6 +109,7 @@ SHARED_CASES = [
     ("normal", 1, 1, 3000, 700, 10, 0, "full"),
     ("normal", 2, 5, 129, 1, 1, 0, "ragged"),
     ("normal", 2, 128, 300, 20, 5, 0, "ragged"),
+    ("wide", 2, 8, 20000, 2048, 256, 0, "ragged"),
 ]
 
 
