@@ -357,9 +357,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nbins,
 // always span the populated key range (the keys of concentrated scores sit
 // in a narrow range, often straddling a power of two, and a bit-aligned
 // digit would pile them into a few bins).  Keys above the chosen bin are
-// kept, keys below it evicted.  The adds of a pass take no branch: keys
-// outside the live range go to a spill bin of their lane.  Once at most 64
-// candidates are left, one wave ranks them (each counts the candidates
+// kept, keys below it evicted.  Once at most 64 candidates are left, one wave ranks them (each counts the candidates
 // above it and equal to it) and reads off the threshold.  The result is
 // either "keep every key >= Tlo" (exactly B keys) or, when equal keys
 // straddle the threshold, "keep keys > T and the first need_eq keys == T in
@@ -381,8 +379,7 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
                                                         uint32_t* __restrict__ hist_out = nullptr)
 {
     constexpr int kW = NT / 64;
-    // the histogram, then one spill bin per lane (keys outside the live range)
-    __shared__ uint32_t hist[(1 << kRegDigitBits) + 64];
+    __shared__ uint32_t hist[1 << kRegDigitBits];
     __shared__ uint32_t s_cand[64];
     __shared__ uint32_t s_wa[kW], s_wb[kW], s_run[kW];
     __shared__ uint32_t s_digit, s_above, s_inbin, s_ncand;
@@ -424,8 +421,6 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             key[c] = ordered_key(__uint_as_float(x[c])) & (0u - (seg0 + 64 * c < n ? 1u : 0u));
     }
 
-    // slots past the head's end (key 0)
-    const uint32_t npad = (uint32_t)(NT * KPT - n);
     uint32_t kmin, kmax;
     {
         // the minimum of key - 1 skips key 0 (it wraps to the top) with no
@@ -459,7 +454,6 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
         for (uint32_t b = tid; b < (1u << kRegDigitBits); b += NT) hist[b] = 0u;
         __syncthreads();
         uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-        const uint32_t spill = (1u << kRegDigitBits) + (uint32_t)lane;
 #pragma unroll
         for (int c = 0; c < KPT; ++c) {
             const uint32_t k = key[c];
@@ -467,7 +461,7 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             const bool live = k != 0u && !res;
             lo = min(lo, live ? k : 0xFFFFFFFFu);
             hi = max(hi, live ? k : 0u);
-            atomicAdd(&hist[live ? k >> (32 - kRegDigitBits) : spill], 1u);
+            if (live) atomicAdd(&hist[k >> (32 - kRegDigitBits)], 1u);
         }
         lo = wave_min(lo);
         hi = wave_max(hi);
@@ -515,21 +509,19 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             for (uint32_t b = tid; b < nbins; b += NT) hist[b] = 0u;
             if (tid == 0) s_ncand = 0u;
             __syncthreads();
-            // Every key is added somewhere, with no branch: a key outside the
-            // live range goes to its lane's own spill bin past the histogram
-            // (distinct addresses, so those adds never collide).  Padding
-            // keys (0) lie outside the range unless the range wraps past
-            // 2^32 - 1 to reach 0; then they land in the bin of key 0 and
-            // are taken out again below.
-            const uint32_t spill = (1u << kRegDigitBits) + (uint32_t)lane;
+            // Only keys in the live range are added (padding keys, 0, never
+            // are).  The adds are masked, not redirected: after the first
+            // pass most keys lie outside the range, and sending them to spill
+            // bins made every add a full-wave LDS operation, which was slower
+            // wherever the keys in range pile into a few bins.  The padding
+            // value is opaque so that the compiler recomputes the masks per
+            // pass instead of keeping them live in scalar registers.
+            uint32_t pad = 0u;
+            asm volatile("" : "+v"(pad));
 #pragma unroll
             for (int c = 0; c < KPT; ++c) {
                 const uint32_t off = key[c] - base;
-                atomicAdd(&hist[off <= span ? off >> sh : spill], 1u);
-            }
-            if (npad != 0u && 0u - base <= span) {      // block-uniform
-                __syncthreads();
-                if (tid == 0) hist[(0u - base) >> sh] -= npad;
+                if (off <= span && key[c] != pad) atomicAdd(&hist[off >> sh], 1u);
             }
             __syncthreads();
             find_digit<NT>(hist, nbins, rem, tid, lane, wave, s_run, &s_digit, &s_above, &s_inbin);
@@ -963,16 +955,14 @@ __device__ __forceinline__ void layer_resolve(LayerState& S, uint32_t pass,
 // Launch `pass` (2 or 3): decide pass - 1 (pass 1's histograms come from the
 // reserve step), then histogram this head's unreserved keys for pass `pass`.
 // KPT > 0: every thread loads its KPT keys at once (lane l of wave w: slots
-// w*64*KPT + c*64 + l); KPT == 0: batches of kHeadBatch.  Every key is
-// added with no branch: keys outside the live range, reserved keys and
-// slots past the head's end go to the lane's spill bin past the histogram.
+// w*64*KPT + c*64 + l); KPT == 0: batches of kHeadBatch.
 template <int KPT>
 __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
     int pass, const float* __restrict__ scores, int stride, int n_layers, int n_kv,
     const int32_t* __restrict__ head_len, int total, int floor_, int window,
     const uint4* __restrict__ rec, uint32_t* __restrict__ hist, LayerState* __restrict__ state)
 {
-    __shared__ uint32_t lhist[kSharedBins + 64];
+    __shared__ uint32_t lhist[kSharedBins];
     __shared__ uint32_t s_dig[3];
     const int head = blockIdx.x;
     const int layer = head / n_kv;
@@ -1007,11 +997,9 @@ __global__ __launch_bounds__(kBlock) void shared_pass_kernel(
     const uint32_t base = S.base;
     const int n = head_rows(head_len, head, stride);
     const float* sc = scores + (size_t)head * (size_t)stride;
-    const uint32_t spill = (uint32_t)kSharedBins + (uint32_t)lane;
     auto add = [&](int i, uint32_t key) {
         const uint32_t off = key - base;
-        const bool live = i < n && off <= span && !is_reserved(key, i, th, sh);
-        atomicAdd(&lhist[live ? off >> shift : spill], 1u);
+        if (i < n && off <= span && !is_reserved(key, i, th, sh)) atomicAdd(&lhist[off >> shift], 1u);
     };
     if constexpr (KPT > 0) {
         const int seg0 = wave * (64 * KPT) + lane;
