@@ -357,11 +357,11 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nbins,
 // always span the populated key range (the keys of concentrated scores sit
 // in a narrow range, often straddling a power of two, and a bit-aligned
 // digit would pile them into a few bins).  Keys above the chosen bin are
-// kept, keys below it evicted.  Once at most 64 candidates are left, one wave ranks them (each counts the candidates
-// above it and equal to it) and reads off the threshold.  The result is
-// either "keep every key >= Tlo" (exactly B keys) or, when equal keys
-// straddle the threshold, "keep keys > T and the first need_eq keys == T in
-// slot order".
+// kept, keys below it evicted.  Once at most 64 candidates are left, one
+// wave ranks them (each counts the candidates above it and equal to it)
+// and reads off the threshold.  The result is either "keep every key >= T"
+// (exactly B keys) or, when equal keys straddle the threshold, "keep keys
+// > T and the first need_eq keys == T in slot order".
 //
 // RESERVE (head-specific budgets, budget = the per-head floor): instead of
 // the kept list, writes rec[head] = {Th, Sh, min, max}: the kept set as the
