@@ -185,6 +185,28 @@ def test_score_parity_all_heads(orc, name):
             check_scores(sg[l, h], s_ref, M, "%s l%d h%d" % (name, l, h))
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+@pytest.mark.parametrize("n", [1, 77, 129, 257, 300])
+def test_score_parity_short_and_ragged_heads(orc, dtype, d, n):
+    """Heads shorter than one workgroup's tile and tails one row past a tile
+    (tiles are 128 rows, 256 for bf16 with head_dim 64)."""
+    spec = synth.workload("toy").replace(dtype=dtype, head_dim=d, lengths=(n,), n_kv_heads=2)
+    say("score parity short", dtype, d, n)
+    cache = synth.make_cache(spec, "cuda", seed=n)
+    ctx = ctx_for(cache)
+    seqs = seqs_for(cache)
+    _, total = score_offsets(cache)
+    scores = torch.full((total,), float("nan"), device="cuda")
+    tri.tri_score(ctx, seqs, scores)
+    torch.cuda.synchronize()
+    sg = scores.cpu().numpy().reshape(spec.n_layers, spec.n_kv_heads, -1)
+    for l in range(spec.n_layers):
+        for h in range(spec.n_kv_heads):
+            K, _, P = head_inputs(cache, 0, l, h)
+            s_ref, M = oracle_scores(orc, cache, 0, l, h, K, P)
+            check_scores(sg[l, h], s_ref, M, "%s d%d n%d l%d h%d" % (dtype, d, n, l, h))
+
+
 def test_score_special_tables(orc):
     """q-centre 0 (norm term only), R = 1 (trig term only), explicit
     frequencies, non-identity positions and p_now well past the newest key."""
