@@ -32,6 +32,7 @@
  *   - the norm-term weight of band f is (1 - R_f) * E|q_f|;
  *   - the average over offsets is the plain arithmetic mean;
  *   - the trig and norm terms are added unscaled;
+ *   - a key whose stored row holds an infinite or NaN element scores NaN;
  *   - GQA: query heads [h*G, (h+1)*G) share KV head h; each query head's
  *     score row is z-normalized with the mean and population standard
  *     deviation of its finite scores over the head's cached keys; a
@@ -110,6 +111,20 @@ void tri_oracle_score_head(int d, int n, const double* K, const int64_t* pos,
     double complex* k = (double complex*)malloc(sizeof(double complex) * (size_t)half);
     for (int i = 0; i < n; ++i) {
         const double* row = K + (size_t)i * (size_t)d;
+
+        /* A stored row with an infinite or NaN element has no score: it gets
+           NaN, which the selection ranks below every number (reading; the
+           pages define the score for finite keys only). */
+        int finite_row = 1;
+        for (int j = 0; j < d; ++j)
+            if (!isfinite(row[j])) finite_row = 0;
+        if (!finite_row) {
+            if (trig) trig[i] = NAN;
+            if (norm) norm[i] = NAN;
+            if (score) score[i] = NAN;
+            continue;
+        }
+
         for (int f = 0; f < half; ++f)
             k[f] = unrotate_band(row, d, f, pos[i], omega);
 

@@ -81,6 +81,12 @@ MUTANTS = {
         "if (all <= (int64_t)total) return 0;"),
     "shared budget kept lists unsorted": (
         "qsort(kept + (size_t)h * total, (size_t)count[h], sizeof(int32_t), by_int32);", ";"),
+    "non-finite keys keep their literal score": ("        if (!finite_row) {\n", "        if (0) {\n"),
+    "bound drops |A_f|": ("cabs(qc_re[f] + I * qc_im[f]) * cabs(a)", "cabs(qc_re[f] + I * qc_im[f])"),
+    "bound drops the norm weight": ("                + (1.0 - q_mrl[f]) * q_mean_norm[f];", "                ;"),
+    "bound doubled": ("        bound[i] = m;", "        bound[i] = 2.0 * m;"),
+    "bound takes the mean norm as the trig coefficient": (
+        "cabs(qc_re[f] + I * qc_im[f]) * cabs(a)", "q_mean_norm[f] * cabs(a)"),
     "GQA statistics include non-finite scores": (
         "if (isfinite(s[i])) { sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }",
         "{ sum += s[i]; ++count; if (fabs(s[i]) > big) big = fabs(s[i]); }"),
@@ -103,10 +109,16 @@ def _pin_calls():
         (pins.test_norm_term_is_position_invariant, {}),
         (pins.test_score_is_sum_and_bounded, {}),
         (pins.test_folded_form_agrees, {}),
+        (pins.test_bound_adds_over_bands, {}),
+        (pins.test_nonfinite_keys_score_nan_and_are_evicted, {}),
         (pins.test_select_matches_numpy_lexsort, {}),
         (pins.test_select_invariants_and_fire_rule, {}),
         (pins.test_gather_matches_numpy_take_and_identity, {}),
     ]
+    for i in range(len(pins._bound_golden()["examples"])):
+        calls.append((pins.test_golden_bound_examples, {"i": i}))
+    for seed in range(6):
+        calls.append((pins.test_bound_is_the_largest_score_over_key_phases, {"seed": seed}))
     for ex in pins._golden()["score_examples"]:
         calls.append((pins.test_golden_score_examples, {"ex": ex}))
     for i in range(len(pins._golden()["select_examples"])):

@@ -259,6 +259,106 @@ def test_folded_form_agrees(oracle_lib):
     assert np.all(np.abs(score - folded) <= 1e-11 * M)
 
 
+# ------------------------------------------- the tolerance scale M, two-sided
+
+def _bound_golden():
+    with open(os.path.join(GOLDEN, "bound_examples.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("i", range(len(_bound_golden()["examples"])))
+def test_golden_bound_examples(oracle_lib, i):
+    """Hand-derived values of M (tests/golden/bound_examples.json)."""
+    ex = _bound_golden()["examples"][i]
+    d = ex["head_dim"]
+    qc = np.array(ex["qc"])
+    M = oracle_lib.bound_head(np.array([ex["key_stored"]]), ex["omega"], ex["offsets"],
+                              qc[: d // 2], qc[d // 2:], ex["q_mean_norm"], ex["q_mrl"])
+    assert abs(M[0] - ex["bound"]) <= 1e-12 * max(1.0, abs(ex["bound"]))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bound_is_the_largest_score_over_key_phases(oracle_lib, seed):
+    """M is attained: with one band, the score of a key of fixed magnitude r
+    is a + b cos(phi) + c sin(phi) in the stored phase phi (the trig term is
+    linear in the stored row, the norm term does not see the phase), so its
+    largest value over phi is a + sqrt(b^2 + c^2).  Four phases give a, b, c
+    from the oracle's own scores, a fifth checks the form; M must equal that
+    maximum, and the smallest score must be 2a - M."""
+    rng = np.random.default_rng(100 + seed)
+    om = rng.uniform(0.01, 3.0, 1)
+    offs = np.sort(rng.choice(1 << 12, size=int(rng.integers(1, 6)), replace=False)) + 1
+    qr, qi = rng.standard_normal(1), rng.standard_normal(1)
+    m = np.hypot(qr, qi) * rng.uniform(1.0, 2.0, 1)
+    R = rng.uniform(0.0, 1.0, 1)
+    r = rng.uniform(0.5, 3.0)
+    p, p_now = int(rng.integers(0, 4000)), 4000 + int(rng.integers(0, 100))
+
+    def s_at(phi):
+        K = np.array([[r * math.cos(phi), r * math.sin(phi)]])
+        return oracle_lib.score_head(K, [p], p_now, om, offs, qr, qi, m, R)[2][0]
+
+    s0, s1, s2, s3 = (s_at(k * math.pi / 2) for k in range(4))
+    a, b, c = (s0 + s1 + s2 + s3) / 4, (s0 - s2) / 2, (s1 - s3) / 2
+    phi = 0.7
+    assert abs(s_at(phi) - (a + b * math.cos(phi) + c * math.sin(phi))) <= 1e-12 * (abs(a) + abs(b) + abs(c))
+    top = a + math.hypot(b, c)
+    M = oracle_lib.bound_head(np.array([[r, 0.0]]), om, offs, qr, qi, m, R)[0]
+    assert abs(M - top) <= 1e-12 * M
+    assert abs((2 * a - M) - (a - math.hypot(b, c))) <= 1e-12 * M
+    assert abs(a - (1 - R[0]) * m[0] * r) <= 1e-12 * M      # the phase-free part is the norm term
+
+
+def test_bound_adds_over_bands(oracle_lib):
+    """M of a key is the sum of M over its bands taken one at a time (every
+    other band zero), and it scales with the key: M(cK) = |c| M(K)."""
+    rng = np.random.default_rng(11)
+    d = 8
+    qc_re, qc_im, m, R, pos, K = random_head(rng, d, 5)
+    om = omega_np(d, 1e4)
+    offs = synth.pow2_offsets(10)
+    M = oracle_lib.bound_head(K, om, offs, qc_re, qc_im, m, R)
+    h = d // 2
+    parts = np.zeros(len(K))
+    for f in range(h):
+        Kf = np.zeros_like(K)
+        Kf[:, f], Kf[:, f + h] = K[:, f], K[:, f + h]
+        parts += oracle_lib.bound_head(Kf, om, offs, qc_re, qc_im, m, R)
+    np.testing.assert_allclose(M, parts, rtol=1e-13)
+    np.testing.assert_allclose(oracle_lib.bound_head(-2.5 * K, om, offs, qc_re, qc_im, m, R), 2.5 * M,
+                               rtol=1e-13)
+
+
+# ------------------------------------------------------- non-finite keys
+
+def test_nonfinite_keys_score_nan_and_are_evicted(oracle_lib):
+    """A key whose stored row holds +inf, -inf or NaN scores NaN (trig, norm
+    and score), so it ranks below every number; the other keys score as they
+    would alone.  The one-band case K = (inf, inf), centre 1, R = 0 is one
+    where plain complex arithmetic reaches +inf, which would rank first."""
+    t, nm, s = oracle_lib.score_head(np.array([[np.inf, np.inf]]), [0], 0, [1.0], [1],
+                                     [1.0], [0.0], [1.0], [0.0])
+    assert np.isnan(t[0]) and np.isnan(nm[0]) and np.isnan(s[0])
+    rng = np.random.default_rng(12)
+    d, n = 128, 40
+    qc_re, qc_im, m, R, pos, K = random_head(rng, d, n)
+    om = omega_np(d, 1e6)
+    offs = synth.pow2_offsets(16)
+    bad = {3: np.inf, 7: -np.inf, 11: np.nan, 20: np.inf, 33: np.nan}
+    Kb = K.copy()
+    for i, v in bad.items():
+        Kb[i, int(rng.integers(0, d))] = v
+    Kb[20, 5], Kb[20, 5 + d // 2] = np.inf, -np.inf
+    trig, norm, score = oracle_lib.score_head(Kb, pos, 6000, om, offs, qc_re, qc_im, m, R)
+    good = np.array([i not in bad for i in range(n)])
+    for x in (trig, norm, score):
+        assert np.all(np.isnan(x[~good])) and np.all(np.isfinite(x[good]))
+    _, _, alone = oracle_lib.score_head(K[good], pos[good], 6000, om, offs, qc_re, qc_im, m, R)
+    np.testing.assert_array_equal(score[good], alone)
+    kept = oracle_lib.select_head(score, pos, n - len(bad), 0)
+    assert sorted(kept.tolist()) == np.nonzero(good)[0].tolist()
+
+
 # --------------------------------------------------------- golden examples
 
 def _golden():
