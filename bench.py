@@ -19,8 +19,9 @@ between the launches.
 Prints one JSON line.  Extra modes:
   --pmc-steps N      a plain 1 GiB device copy, then N steps with no restores
                      (for rocprofv3 counter runs; see --summarize-pmc)
-  --summarize-pmc D  turn rocprofv3 counter CSVs under D into the traffic
-                     summary that later runs report as roofline.traffic
+  --summarize-pmc D  turn rocprofv3 counter CSVs under D (runs of --pmc-steps N
+                     on --workload W) into profiles/score_kernel_W_traffic.json,
+                     which later runs report as roofline.traffic
   --shared-floor F   head-specific budgets: the KV heads of a layer share
                      budget * n_kv_heads slots, each keeping at least its F
                      best keys (shared select and counted compaction)
@@ -43,8 +44,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "cached keys scored+pruned/sec (G keys/s) and achieved HBM GB/s vs peak"
 SCORE_KERNEL = "score_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_qwen3_32k_traffic.json")
-KERNEL_SOURCES = ["rope_aware_eviction_amd/csrc/score.hip", "rope_aware_eviction_amd/csrc/tri_internal.h"]
+# the score kernel's source (tri_internal.h holds only declarations shared by
+# every kernel file, so it is not part of the hash)
+KERNEL_SOURCES = ["rope_aware_eviction_amd/csrc/score.hip"]
+
+
+def traffic_file(workload: str) -> str:
+    """Committed byte-counter summary of the score kernel on one workload."""
+    return os.path.join(ROOT, "profiles", "score_kernel_%s_traffic.json" % workload)
 
 
 def kernel_hash() -> str:
@@ -58,16 +65,20 @@ def kernel_hash() -> str:
 def workload_bytes(spec):
     """Algorithmic bytes of one prune step and of its score kernel.
 
-    pass:  per head N*row (read K) + 4*B*row (read and write kept K and V rows)
-           + 8*B (read and write kept positions)
-    score: per head N*row (read K) + 4*N (write fp32 scores); with G > 1 query
-           heads per KV head the score phase also writes and reads back the G
-           raw scores per key: + 8*G*N
+    pass:   per firing head N*row (read K) + 4*B*row (read and write the kept K
+            and V rows) + 8*B (read and write the kept positions); the scores
+            are an intermediate and are not counted
+    k_read: per head N*row, the K rows the score kernel must read once (its
+            algorithmic bytes)
+    score_io: what the score phase writes besides: 4*N of fp32 scores; with
+            G > 1 query heads per KV head instead the G raw scores per key,
+            4*G*N (the selection reads them back and forms the score)
     """
     H, row, B, G = spec.heads, spec.row_bytes, spec.budget, spec.group
     p = sum(H * (n * row + 4 * B * row + 8 * B) for n in spec.lengths if n > B + spec.window)
-    s = sum(H * (n * row + 4 * n + (8 * G * n if G > 1 else 0)) for n in spec.lengths)
-    return p, s
+    k = sum(H * n * row for n in spec.lengths)
+    io = sum(H * (4 * G * n if G > 1 else 4 * n) for n in spec.lengths)
+    return p, k, io
 
 
 def describe(spec) -> str:
@@ -78,35 +89,63 @@ def describe(spec) -> str:
         spec.name, spec.n_layers, spec.n_kv_heads, spec.head_dim, gqa, lens, spec.budget, spec.dtype)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cache, n_heads_sample: int):
     """The fp64 oracle, as it stands, on a bounded sample of the same cache:
-    full prune of the first n_heads_sample heads, one head per host thread."""
-    import numpy as np
+    full prune (score, select, gather) of n_heads_sample heads, one head per
+    host thread on every core the process may use, then one head on one
+    thread.  Heads are the first ones of a one-sequence cache, or spread over
+    the sequences (and their lengths) of a batch."""
+    import torch
     import oracle
 
     orc = oracle.load()
     sp, cal = cache.spec, cache.calib
     threads = min(len(os.sched_getaffinity(0)), 64)
     om = orc.omega(sp.head_dim, sp.rope_theta)
-    jobs = []
-    n = cache.lens[0]
     G = sp.group
-    for hi in range(n_heads_sample):
-        l, h = divmod(hi, sp.n_kv_heads)
+    if sp.n_seq == 1:
+        picks = [(0,) + divmod(hi, sp.n_kv_heads) for hi in range(n_heads_sample)]
+    else:
+        step = max(1, sp.n_seq // n_heads_sample)
+        picks = [(s, (7 * s) % sp.n_layers, s % sp.n_kv_heads)
+                 for s in range(0, sp.n_seq, step)][:n_heads_sample]
+
+    def job(s, l, h):
+        n = cache.lens[s]
         q = slice(h * G, (h + 1) * G) if G > 1 else h
-        jobs.append(dict(
-            K=cache.k[0][l, h, :n].float().cpu().numpy(), V=cache.v[0][l, h, :n].cpu().view(
-                __import__("torch").int16).numpy(), pos=cache.pos[0][l, h, :n].cpu().numpy(),
-            p_now=cache.p_now[0], om=om, offsets=cal.offsets, qc_re=cal.qc_re[l, q],
-            qc_im=cal.qc_im[l, q], q_mean_norm=cal.q_mean_norm[l, q], q_mrl=cal.q_mrl[l, q],
-            budget=sp.budget, window=sp.window))
+        return dict(K=cache.k[s][l, h, :n].float().cpu().numpy(),
+                    V=cache.v[s][l, h, :n].cpu().view(torch.int16).numpy(),
+                    pos=cache.pos[s][l, h, :n].cpu().numpy(), p_now=cache.p_now[s], om=om,
+                    offsets=cal.offsets, qc_re=cal.qc_re[l, q], qc_im=cal.qc_im[l, q],
+                    q_mean_norm=cal.q_mean_norm[l, q], q_mrl=cal.q_mrl[l, q],
+                    budget=sp.budget, window=sp.window)
+
+    jobs = [job(*x) for x in picks]
     t0 = time.perf_counter()
     orc.prune_heads_parallel(jobs, threads)
     dt = time.perf_counter() - t0
-    keys = n_heads_sample * n
+    keys = sum(cache.lens[s] for s, _, _ in picks)
+    t1 = time.perf_counter()
+    orc.prune_heads_parallel(jobs[:1], 1)
+    dt1 = time.perf_counter() - t1
+    keys1 = cache.lens[picks[0][0]]
     return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d heads x %d keys (full score+select+gather per head), %.1f s wall"
-                      % (n_heads_sample, sp.heads, n, dt)}
+            "cpu_model": cpu_model(),
+            "sample": "%d of %d heads, %d keys (full score+select+gather per head), one head per "
+                      "thread, %.1f s wall" % (len(picks), sp.heads * sp.n_seq, keys, dt),
+            "single_thread": {"value": keys1 / dt1 / 1e9, "unit": "G keys/s", "cores": 1,
+                              "sample": "1 head, %d keys, %.2f s" % (keys1, dt1)}}
 
 
 def cpu_baseline_shared(cache, n_layers_sample: int, floor: int):
@@ -145,10 +184,10 @@ def cpu_baseline_shared(cache, n_layers_sample: int, floor: int):
 
 
 def load_traffic(spec):
-    """roofline.traffic from the committed counter summary, or None when absent
-    or taken on a different score kernel source or workload."""
+    """roofline.traffic from the committed counter summary of this workload, or
+    None when absent or taken on a different score kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(spec.name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -157,52 +196,105 @@ def load_traffic(spec):
     return t.get("traffic_bytes_per_launch")
 
 
-def summarize_pmc(directory: str):
-    """Reads rocprofv3 --pmc counter_collection CSVs (one FETCH_SIZE run, one
-    WRITE_SIZE run) and writes the traffic summary.  The byte counters are
-    scaled by what they read for the plain 1 GiB device copy in the same run."""
+# kernel classes the counter summaries report (the first name a kernel's
+# full name contains decides its class)
+PMC_KERNELS = ("gqa_score_kernel", "gqa_mfma_kernel", "gqa_norm_kernel", SCORE_KERNEL,
+               "select_batch_kernel", "select_reg_kernel", "select_kernel", "compact_batch_kernel",
+               "compact_kernel", "copyBuffer")
+REQ_COUNTERS = ("TCC_EA0_RDREQ", "TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B",
+                "TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B")
+
+
+def summarize_pmc(directory: str, workload: str, steps: int):
+    """Reads rocprofv3 --pmc counter_collection CSVs of `bench.py --pmc-steps
+    steps` runs and writes the traffic summary of the score phase (and of the
+    step's other kernels) on one workload, per prune step.
+
+    Two sets of runs are read.  The memory-side request counters of the L2
+    by request size (TCC_EA0_RDREQ_32B / _64B / _128B; TCC_EA0_WRREQ with
+    TCC_EA0_WRREQ_64B, the rest of the write requests being 32 bytes) give
+    bytes directly; FETCH_SIZE and WRITE_SIZE (derived KiB) are kept beside
+    them.  Each is checked against the plain 1 GiB device copy of the same
+    run and scaled by it.  traffic_bytes_per_launch (per step: the score
+    phase is one launch per sequence) is the request-counter figure."""
     import numpy as np
 
-    def rows(counter):
-        out = []
+    def values(counter):
+        """counter -> {kernel class: [per-dispatch values]}"""
+        out = {}
         for p in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
             with open(p) as f:
                 for r in csv.DictReader(f):
-                    if r.get("Counter_Name") == counter:
-                        out.append(r)
+                    name = r.get("Counter_Name", "")
+                    if name.endswith("_sum"):
+                        name = name[:-4]
+                    if name != counter:
+                        continue
+                    kname = r.get("Kernel_Name", "")
+                    for k in PMC_KERNELS:
+                        if k in kname:
+                            out.setdefault(k, []).append(float(r["Counter_Value"]))
+                            break
         return out
 
-    res = {}
-    others = {}          # the step's other kernels, by name: counter -> values
-    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        score, copy = [], []
-        for r in rows(counter):
-            name = r.get("Kernel_Name", "")
-            if SCORE_KERNEL in name:
-                score.append(float(r["Counter_Value"]))
-            elif "copyBuffer" in name:
-                copy.append(float(r["Counter_Value"]))
-            else:
-                for k in ("select_reg_kernel", "compact_kernel"):
-                    if k in name:
-                        others.setdefault(k, {}).setdefault(counter, []).append(float(r["Counter_Value"]))
-        # the 1 GiB copy is the run's only large copy: its counter is the largest
-        res[counter] = {"score": float(np.median(score)), "copy": max(copy)}
+    vals = {c: values(c) for c in ("FETCH_SIZE", "WRITE_SIZE") + REQ_COUNTERS}
+
+    def per_step(counter, k):
+        v = vals[counter].get(k)
+        return sum(v) / steps if v else None
+
+    def copy_val(counter):
+        v = vals[counter].get("copyBuffer")
+        return max(v) if v else None     # the 1 GiB copy is the run's largest copy
+
+    def req_bytes(get):
+        r32, r64, r128 = (get("TCC_EA0_RDREQ_%s" % x) for x in ("32B", "64B", "128B"))
+        wr, w64 = get("TCC_EA0_WRREQ"), get("TCC_EA0_WRREQ_64B")
+        if None in (r32, r64, r128, wr, w64):
+            return None
+        return {"rdreq": get("TCC_EA0_RDREQ"), "rdreq_32b": r32, "rdreq_64b": r64, "rdreq_128b": r128,
+                "wrreq": wr, "wrreq_64b": w64, "read_bytes": 32 * r32 + 64 * r64 + 128 * r128,
+                "write_bytes": 64 * w64 + 32 * (wr - w64)}
+
     copy_bytes = float(1 << 30)
-    f_scale = copy_bytes / (res["FETCH_SIZE"]["copy"] * 1024.0)
-    w_scale = copy_bytes / (res["WRITE_SIZE"]["copy"] * 1024.0)
-    fetch = res["FETCH_SIZE"]["score"] * 1024.0 * f_scale
-    write = res["WRITE_SIZE"]["score"] * 1024.0 * w_scale
-    out = {"workload": "qwen3_32k", "kernel": SCORE_KERNEL, "kernel_hash": kernel_hash(),
-           "fetch_kib_raw": res["FETCH_SIZE"]["score"], "write_kib_raw": res["WRITE_SIZE"]["score"],
-           "copy_fetch_kib_raw": res["FETCH_SIZE"]["copy"], "copy_write_kib_raw": res["WRITE_SIZE"]["copy"],
-           "fetch_scale": f_scale, "write_scale": w_scale,
-           "traffic_bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
-           "other_kernels": {k: {"fetch_bytes": float(np.median(v["FETCH_SIZE"])) * 1024.0 * f_scale,
-                                 "write_bytes": float(np.median(v["WRITE_SIZE"])) * 1024.0 * w_scale}
-                             for k, v in others.items() if "FETCH_SIZE" in v and "WRITE_SIZE" in v}}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    out = {"workload": workload, "kernel": SCORE_KERNEL, "kernel_hash": kernel_hash(),
+           "steps": steps, "unit": "bytes per prune step (all launches of the kernel class)"}
+    cr = req_bytes(copy_val)
+    if cr:
+        out["copy_requests"] = dict(cr, read_scale=copy_bytes / cr["read_bytes"],
+                                    write_scale=copy_bytes / cr["write_bytes"])
+    cf, cw = copy_val("FETCH_SIZE"), copy_val("WRITE_SIZE")
+    if cf and cw:
+        out["copy_derived"] = {"fetch_kib": cf, "write_kib": cw, "fetch_scale": copy_bytes / (cf * 1024.0),
+                               "write_scale": copy_bytes / (cw * 1024.0)}
+    per = {}
+    for k in PMC_KERNELS[:-1]:
+        entry = {}
+        b = req_bytes(lambda c: per_step(c, k))
+        if b and cr:
+            b["read_bytes_scaled"] = b["read_bytes"] * out["copy_requests"]["read_scale"]
+            b["write_bytes_scaled"] = b["write_bytes"] * out["copy_requests"]["write_scale"]
+            entry["requests"] = b
+        f, w = per_step("FETCH_SIZE", k), per_step("WRITE_SIZE", k)
+        if f is not None and w is not None and "copy_derived" in out:
+            entry["derived"] = {"fetch_kib": f, "write_kib": w,
+                                "fetch_bytes_scaled": f * 1024.0 * out["copy_derived"]["fetch_scale"],
+                                "write_bytes_scaled": w * 1024.0 * out["copy_derived"]["write_scale"]}
+        if entry:
+            entry["dispatches_per_step"] = len(vals["TCC_EA0_RDREQ_128B"].get(k) or
+                                               vals["FETCH_SIZE"].get(k) or []) / steps
+            per[k] = entry
+    out["kernels"] = per
+    sk = per.get(SCORE_KERNEL, {})
+    if "requests" in sk:
+        out["traffic_bytes_per_launch"] = sk["requests"]["read_bytes_scaled"] + sk["requests"]["write_bytes_scaled"]
+        out["traffic_from"] = "TCC_EA0 read and write requests by size, scaled by the 1 GiB copy"
+    elif "derived" in sk:
+        out["traffic_bytes_per_launch"] = sk["derived"]["fetch_bytes_scaled"] + sk["derived"]["write_bytes_scaled"]
+        out["traffic_from"] = "FETCH_SIZE + WRITE_SIZE, scaled by the 1 GiB copy"
+    path = traffic_file(workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -291,7 +383,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the cache the oracle baseline prunes (0 = skip)")
     ap.add_argument("--pmc-steps", type=int, default=0)
-    ap.add_argument("--summarize-pmc", default=None)
+    ap.add_argument("--summarize-pmc", default=None, metavar="DIR",
+                    help="write profiles/score_kernel_<workload>_traffic.json from the counter CSVs "
+                         "under DIR (with --workload)")
     ap.add_argument("--calib-stats", type=int, default=0, metavar="N_SAMPLES",
                     help="measure tri_calibrate_stats instead: N_SAMPLES pre-RoPE query samples of "
                          "the Qwen3-8B query heads (36 layers x 32 heads x head_dim 128, bf16)")
@@ -303,7 +397,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc)
+        summarize_pmc(args.summarize_pmc, args.workload, max(1, args.pmc_steps))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the pass is independent per (sequence, layer, "
@@ -362,9 +456,19 @@ def main():
     ws_bytes = tri.score_workspace_bytes(ctx, seqs())
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
+    # GQA with uniform budgets: the selection forms the aggregated score from
+    # the raw per-query-head scores in the workspace (no score array written)
+    gqa_ws = spec.group > 1 and not shared
+    long_heads = max(cache.lens) > 32768
+
+    def score(s):
+        tri.tri_score(ctx, s, None if gqa_ws else scores, stream, ws)
+
     def select(s):
         if shared:
             tri.tri_select_shared(ctx, s, scores, B, F, W, kept, counts, sel_ws, stream)
+        elif gqa_ws:
+            tri.tri_select_topb_ws(ctx, s, ws, B, W, kept, stream, scores if long_heads else None)
         else:
             tri.tri_select_topb(ctx, s, scores, B, W, kept, stream)
 
@@ -375,7 +479,7 @@ def main():
             tri.tri_compact_kv(ctx, s, kept, B, W, stream)
 
     def step(s):
-        tri.tri_score(ctx, s, scores, stream, ws)
+        score(s)
         select(s)
         compact(s)
 
@@ -448,7 +552,7 @@ def main():
         s = seqs()
         e = pev[i]
         e[0].record(stream)
-        tri.tri_score(ctx, s, scores, stream, ws)
+        score(s)
         e[1].record(stream)
         select(s)
         e[2].record(stream)
@@ -461,8 +565,8 @@ def main():
     mean = lambda x: sum(x) / len(x)
     ms = mean(t_step)
     keys = spec.keys
-    bytes_pass, bytes_score = workload_bytes(spec)
-    score_gbs = bytes_score / (mean(t_score) * 1e-3) / 1e9
+    bytes_pass, bytes_k, bytes_score_io = workload_bytes(spec)
+    score_gbs = bytes_k / (mean(t_score) * 1e-3) / 1e9
     pass_gbs = bytes_pass / (ms * 1e-3) / 1e9
 
     if shared:
@@ -489,11 +593,16 @@ def main():
                    "budgets": ("shared per layer (budget x %d KV heads), floor %d per head"
                                % (spec.n_kv_heads, F)) if shared else "uniform per head"},
         "roofline": {"bound": "hbm", "kernel": SCORE_KERNEL if spec.group == 1 else
-                     "GQA score phase (gqa_prep_kernel, gqa_mfma_kernel, gqa_stats_kernel, gqa_norm_kernel; f32 K: gqa_score_kernel)",
+                     "GQA score phase (gqa_prep_kernel, gqa_mfma_kernel, gqa_stats_kernel; f32 K: "
+                     "gqa_score_kernel); the selection forms the aggregated score",
                      "achieved": score_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": score_gbs / HBM_PEAK_GBS,
-                     "traffic": load_traffic(spec), "alg_bytes_per_launch": bytes_score,
-                     "launch_ms": mean(t_score)},
+                     "traffic": load_traffic(spec),
+                     # K rows read once: the score phase's algorithmic bytes
+                     "alg_bytes_per_launch": bytes_k,
+                     # not algorithmic: fp32 scores written (and GQA raw scores written and read)
+                     "intermediate_bytes_per_launch": bytes_score_io,
+                     "launches": spec.n_seq, "launch_ms": mean(t_score)},
         "pass": {"alg_bytes": bytes_pass, "achieved_gbs": pass_gbs, "frac": pass_gbs / HBM_PEAK_GBS,
                  "phase_ms": {"score": mean(t_score), "select": mean(t_select),
                               "compact": mean(t_compact)},
@@ -501,7 +610,7 @@ def main():
         "wall_s_timed_loop_incl_restores": wall,
         "cpu_baseline": None,
     }
-    if args.cpu_heads > 0 and spec.n_seq == 1:
+    if args.cpu_heads > 0 and (spec.n_seq == 1 or not shared):
         restore()
         torch.cuda.synchronize()
         print("bench: oracle baseline on %d heads" % args.cpu_heads, file=sys.stderr, flush=True)

@@ -9,8 +9,8 @@
  *     norms and mean resultant lengths R_f; online, each cached key gets a
  *     trigonometric distance-preference term plus a norm term weighted by
  *     (1 - R_f), averaged over geometric future offsets; every 128 decoded
- *     tokens the cache is pruned back to the budget.  Figure 4 caption: only
- *     the top-scoring keys survive the prune.
+ *     tokens the cache is pruned back to the budget; figure 4 caption: the
+ *     pruning step retains the highest-scoring keys.
  *   - "TriAttention ... Review", dimensionstp.github.io, section 2-2 (the
  *     RoPE logit as a per-band cosine series in query-key distance) and
  *     section 3-2 items 2)-5) (the cached key's position and pre-RoPE form
@@ -202,7 +202,10 @@ int64_t tri_scores_count(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq)
  * The un-rotation and the distance share p_i and cancel, so the kernel folds
  * C_f = E[q_f] * A_f * exp(i*w_f*p_now) once per head in fp64 and takes
  * score = sum_f (Re C_f * K[f] + Im C_f * K[f + d/2]) + sum_f w_f * |K_f|
- * from the stored row, accumulating in fp32.
+ * from the stored row, accumulating in fp32.  A key whose stored row holds
+ * an infinite or NaN element scores NaN (so every selection ranks it last);
+ * so does a finite row whose fp32 evaluation overflows (elements of magnitude
+ * above ~1e18).
  * GQA contexts (n_q_heads > n_kv_heads) need tri_score_ws; tri_score
  * returns TRI_E_INVAL for them.
  *   dtype   element type of every seq's K (TRI_F32 or TRI_BF16)
@@ -235,7 +238,10 @@ int64_t tri_score_workspace_bytes(const tri_ctx* ctx, const tri_seq* seqs, int32
  * head of its KV head, each the score above with that query head's table;
  * each query head's scores are z-normalized over the head's cached keys,
  *   z_g = (s_g - mean_g) / sd_g   (mean and population deviation of the finite s_g),
- * and the key's score is the largest z_g.  K is read once.  Readings: a
+ * and the key's score is the largest z_g.  K is read once.  With GQA
+ * contexts `scores` may be NULL: then only the raw scores and their
+ * statistics are computed, into the workspace, for tri_select_topb_ws.
+ * Readings: a
  * deviation at most 1e-9 of the largest |s_g| counts as zero and gives
  * z_g = 0; a non-finite s_g gives NaN, which loses to every number; mean_g
  * and sd_g are accumulated in fp64 in a fixed order (the result does not
@@ -268,6 +274,31 @@ tri_status tri_score_ws(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs
 tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
                            const float* scores, int32_t budget, int32_t window,
                            int32_t* kept, void* stream);
+
+/*
+ * tri_select_topb for GQA contexts without the normalized score array: the
+ * keys are ranked by the GQA score of tri_score_ws (the largest z-normalized
+ * per-query-head score), formed on the fly from the raw per-query-head
+ * scores and statistics that a tri_score_ws call on the same sequences, with
+ * scores == NULL, left in `workspace`.  The kept lists are those
+ * tri_select_topb gives on the scores tri_score_ws would have written (the
+ * same fp64 operations, rounded once to fp32).  Saves writing and reading
+ * back the normalized scores.
+ *   scores     NULL, unless a firing sequence holds more than 32768 keys per
+ *              head: then device fp32 in the layout of tri_score, where the
+ *              normalized scores of those sequences are written first
+ *   workspace  the workspace of that tri_score_ws call, unchanged since
+ *              (16-byte aligned, at least tri_score_workspace_bytes())
+ *   budget, window, kept, the fire rule: as tri_select_topb (head_len NULL)
+ * Errors: TRI_E_INVAL (also: a context with one query table per KV head, a
+ * missing or short workspace), TRI_E_HIP.
+ * Source: dimensionstp.github.io review, section 3-2 items 5 and 6 (top-budget
+ * keys; per query head z-score, then the max over the query heads of a KV
+ * head); romaanj.github.io review, section "Method".
+ */
+tri_status tri_select_topb_ws(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
+                              float* scores, const void* workspace, int64_t workspace_bytes,
+                              int32_t budget, int32_t window, int32_t* kept, void* stream);
 
 /*
  * Evicts in place (head_len must be NULL): for every head of every firing
@@ -319,7 +350,7 @@ int64_t tri_select_shared_workspace_bytes(const tri_ctx* ctx, int32_t n_seq);
  * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED (n_kv_heads > 128), TRI_E_HIP.
  * Source: romaanj.github.io review, section "Future work" (refined
  * compression with head-specific budgets); section "Method" and figure 4
- * caption for the top-scoring keys surviving.
+ * caption (the highest-scoring keys are retained).
  */
 tri_status tri_select_shared(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
                              const float* scores, int32_t budget, int32_t floor, int32_t window,

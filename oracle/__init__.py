@@ -30,25 +30,37 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "tri_oracle.c")
 LIBRARY = os.path.join(_HERE, "libtri_oracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source, used
+# when TRI_ORACLE_SANITIZE=1 (the process must preload the ASan runtime)
+SAN_LIBRARY = os.path.join(_HERE, "libtri_oracle_san.so")
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
 
-def compile_c(src: str, out: str) -> str:
-    """gcc, plain C99, -O2, no fast-math."""
+def compile_c(src: str, out: str, sanitize: bool = False) -> str:
+    """gcc, plain C99, -O2, no fast-math; with sanitize, AddressSanitizer and
+    UndefinedBehaviorSanitizer (host code only: the oracle has no GPU part)."""
     tmp = out + ".tmp%d" % os.getpid()
-    subprocess.check_call(["gcc", "-std=c99", "-O2", "-fPIC", "-shared",
-                           "-Wall", "-Wextra", "-o", tmp, src, "-lm"])
+    flags = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra"]
+    if sanitize:
+        flags += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
+    subprocess.check_call(flags + ["-o", tmp, src, "-lm"])
     os.replace(tmp, out)
     return out
 
 
+def sanitized() -> bool:
+    return os.environ.get("TRI_ORACLE_SANITIZE") == "1"
+
+
 def build(force: bool = False) -> str:
-    if force or not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
-        compile_c(SOURCE, LIBRARY)
-    return LIBRARY
+    lib = SAN_LIBRARY if sanitized() else LIBRARY
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(SOURCE):
+        compile_c(SOURCE, lib, sanitize=sanitized())
+    return lib
 
 
 def _f64(a):
@@ -334,6 +346,5 @@ def load() -> Oracle:
     """The oracle built from ``tri_oracle.c`` (compiled on first use)."""
     global _default
     if _default is None:
-        build()
-        _default = Oracle(LIBRARY)
+        _default = Oracle(build())
     return _default

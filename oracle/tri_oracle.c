@@ -13,8 +13,8 @@
  *        the per-band trigonometric term ||E[q_f]||*||k_f||*cos(w_f*D + phi_f),
  *        the norm term weighted by (1 - R_f), averaging over geometrically
  *        spaced future offsets {1,2,4,...,2^16}, pruning to the budget every
- *        128 decoded tokens; figure 4 caption ("only top-scoring keys survive
- *        the prune").
+ *        128 decoded tokens; figure 4 caption (the prune retains the
+ *        highest-scoring keys).
  *   [R2] "TriAttention ... Review", dimensionstp.github.io, section 2-2
  *        (RoPE logit as a sum over bands of r_q*r_k*cos((i-j)*theta_f+phi_f)),
  *        section 3-2 items 2)-5) (cached key has a known position and

@@ -32,7 +32,8 @@ TRI_F32, TRI_BF16 = 0, 1
 
 EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last_hip_error",
             "tri_scores_count", "tri_score", "tri_score_workspace_bytes", "tri_score_ws",
-            "tri_select_topb", "tri_compact_kv", "tri_calibrate_stats", "tri_distance_curve",
+            "tri_select_topb", "tri_select_topb_ws", "tri_compact_kv", "tri_calibrate_stats",
+            "tri_distance_curve",
             "tri_offset_set", "tri_select_shared_workspace_bytes", "tri_select_shared",
             "tri_compact_kv_counts", "tri_compact_kv_counts_workspace_bytes")
 
@@ -104,6 +105,9 @@ def library() -> ctypes.CDLL:
         lib.tri_select_topb.restype = ctypes.c_int
         lib.tri_select_topb.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
                                         ctypes.c_int32, ctypes.c_int32, vp, vp]
+        lib.tri_select_topb_ws.restype = ctypes.c_int
+        lib.tri_select_topb_ws.argtypes = [vp, ctypes.POINTER(_Seq), ctypes.c_int32, vp, vp,
+                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp]
         lib.tri_compact_kv.restype = ctypes.c_int
         lib.tri_compact_kv.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq), ctypes.c_int32, vp,
                                        ctypes.c_int32, ctypes.c_int32, vp]
@@ -327,7 +331,12 @@ def tri_score(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, stream=No
     GQA contexts also need ``workspace``: a contiguous GPU tensor of at least
     score_workspace_bytes(ctx, seqs) bytes (tri_score_ws)."""
     arr, dtype = _seq_array(ctx, seqs, need_kv=False)
-    if scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous() \
+    if scores is None:
+        # GQA contexts: raw per-query-head scores and statistics only, into
+        # the workspace (for tri_select_topb_ws)
+        if workspace is None:
+            raise ValueError("scores=None needs the GQA workspace")
+    elif scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous() \
             or scores.numel() < scores_count(ctx, seqs):
         raise ValueError("scores must be a contiguous fp32 GPU tensor of %d elements"
                          % scores_count(ctx, seqs))
@@ -338,9 +347,36 @@ def tri_score(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, stream=No
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(library().tri_score_ws(ctx.handle, dtype, arr, len(seqs), scores.data_ptr(),
+    _check(library().tri_score_ws(ctx.handle, dtype, arr, len(seqs),
+                                  None if scores is None else scores.data_ptr(),
                                   workspace.data_ptr(), nbytes, _stream_ptr(stream)),
            "tri_score_ws")
+
+
+def tri_select_topb_ws(ctx: Context, seqs: Sequence[Seq], workspace: torch.Tensor, budget: int,
+                       window: int, kept: torch.Tensor, stream=None,
+                       scores: Optional[torch.Tensor] = None):
+    """GQA contexts: top-``budget`` kept slots per head ranked by the GQA score
+    formed on the fly from the raw scores and statistics a
+    tri_score(..., scores=None, workspace=workspace) call left in
+    ``workspace``.  ``scores`` (fp32, the layout of tri_score) is needed only
+    when a firing sequence has more than 32768 keys per head."""
+    arr, _ = _seq_array(ctx, seqs, need_kv=False)
+    if kept.dtype != torch.int32 or not kept.is_cuda or not kept.is_contiguous() \
+            or kept.numel() < len(seqs) * ctx.n_heads * budget:
+        raise ValueError("kept must be a contiguous int32 GPU tensor of n_seq*n_heads*budget")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if scores is not None and (scores.dtype != torch.float32 or not scores.is_cuda
+                               or not scores.is_contiguous()
+                               or scores.numel() < scores_count(ctx, seqs)):
+        raise ValueError("scores must be a contiguous fp32 GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(library().tri_select_topb_ws(ctx.handle, arr, len(seqs),
+                                        None if scores is None else scores.data_ptr(),
+                                        workspace.data_ptr(), nbytes, int(budget), int(window),
+                                        kept.data_ptr(), _stream_ptr(stream)),
+           "tri_select_topb_ws")
 
 
 def tri_select_topb(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, budget: int,
@@ -372,6 +408,15 @@ def tri_compact_kv(ctx: Context, seqs: Sequence[Seq], kept: torch.Tensor, budget
            "tri_compact_kv")
     for i, s in enumerate(seqs):
         s.len = int(arr[i].len)
+
+
+def prune_step_gqa(ctx: Context, seqs: List[Seq], budget: int, window: int, kept: torch.Tensor,
+                   workspace: torch.Tensor, stream=None, scores: Optional[torch.Tensor] = None):
+    """One GQA prune step without the normalized score array (score into the
+    workspace, select from it, compact) on one stream, no host sync."""
+    tri_score(ctx, seqs, None, stream, workspace)
+    tri_select_topb_ws(ctx, seqs, workspace, budget, window, kept, stream, scores)
+    tri_compact_kv(ctx, seqs, kept, budget, window, stream)
 
 
 def fires(seq: Seq, budget: int, window: int) -> bool:

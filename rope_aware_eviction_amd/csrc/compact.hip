@@ -47,6 +47,9 @@ constexpr int kIdxChunk = 8192;                 // kept entries staged in LDS at
 constexpr uint32_t kDrop = 0xFFFFFFC0u;          // buffer offset that is always out of range
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer resource word 3, gfx9 family
 constexpr int kNT = 2;                           // cache-policy bits: non-temporal
+// sequences per launch of the batched compaction (the table travels in the
+// kernel arguments: 40 bytes per sequence)
+constexpr int kCompactBatch = 32;
 
 // s_waitcnt with only the vector-memory count bounded (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima)
@@ -55,6 +58,110 @@ __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Moves one column part (PARTS = 1: the whole rows) of one K or V stream in
+// place: rows r < n_keep become the rows at idx[r] (strictly ascending, in
+// [0, len)); with moves_pos the positions move with them.  Every thread of
+// the workgroup calls it; s_idx is the workgroup's LDS index buffer.
+template <int ROWB, int PARTS>
+__device__ __forceinline__ void move_stream(unsigned char* __restrict__ rows,
+                                            int32_t* __restrict__ hpos,
+                                            const int32_t* __restrict__ idx, int n_keep, int len,
+                                            int part, bool moves_pos, int32_t* s_idx)
+{
+    constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
+    constexpr int kCpp = kChunks / PARTS;               // chunks per column part
+    static_assert(kCpp * PARTS == kChunks, "parts split the row evenly");
+    constexpr int kRowsPerStep = kBlock / kCpp;
+    constexpr int kTile = kRowsPerStep * kUnroll;
+    constexpr int kPosPerThread = (kTile + kBlock - 1) / kBlock;
+    constexpr int kStores = kUnroll + kPosPerThread;    // memory stores per thread per tile
+    static_assert(kIdxChunk % kTile == 0, "tiles never straddle an index chunk");
+
+    const __amdgpu_buffer_rsrc_t rrows =
+        __builtin_amdgcn_make_buffer_rsrc(rows, 0, len * ROWB, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rpos =
+        __builtin_amdgcn_make_buffer_rsrc(hpos, 0, len * 4, kBufferWord3);
+
+    const int tid = threadIdx.x;
+    const int c = part * kCpp + tid % kCpp;
+    const int rs = tid / kCpp;
+
+    // one tile's data in flight: rows, their destinations, positions
+    struct Tile {
+        u32x4 buf[kUnroll];
+        uint32_t dst[kUnroll];
+        uint32_t pval[kPosPerThread];
+        uint32_t pdst[kPosPerThread];
+    };
+    Tile ta, tb;
+
+    auto load = [&](Tile& t, int t0, int c0) {
+        // all of the tile's indices first, so the LDS reads overlap
+        int srcs[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int r = t0 + u * kRowsPerStep + rs;
+            srcs[u] = s_idx[min(r, c0 + kIdxChunk - 1) - c0];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int r = t0 + u * kRowsPerStep + rs;
+            const int src = r < n_keep ? srcs[u] : r;
+            const bool mv = r < n_keep && src != r && (unsigned)src < (unsigned)len;
+            const uint32_t from = mv ? (uint32_t)src * ROWB + 16u * c : kDrop;
+            t.dst[u] = mv ? (uint32_t)r * ROWB + 16u * c : kDrop;
+            t.buf[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrows, from, 0, kNT));
+        }
+#pragma unroll
+        for (int q = 0; q < kPosPerThread; ++q) {
+            const int i = q * kBlock + tid;
+            const int r = t0 + i;
+            const int src = (i < kTile && r < n_keep) ? s_idx[r - c0] : r;
+            const bool mv = moves_pos && i < kTile && r < n_keep && src != r && (unsigned)src < (unsigned)len;
+            t.pdst[q] = mv ? (uint32_t)r * 4u : kDrop;
+            t.pval[q] = __builtin_amdgcn_raw_buffer_load_b32(rpos, mv ? (uint32_t)src * 4u : kDrop, 0, 0);
+        }
+    };
+    auto store = [&](const Tile& t) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(t.buf[u], rrows, t.dst[u], 0, kNT);
+#pragma unroll
+        for (int q = 0; q < kPosPerThread; ++q)
+            __builtin_amdgcn_raw_buffer_store_b32(t.pval[q], rpos, t.pdst[q], 0, 0);
+    };
+
+    for (int c0 = 0; c0 < n_keep; c0 += kIdxChunk) {
+        const int c1 = min(n_keep, c0 + kIdxChunk);
+        __syncthreads();                               // previous chunk's index reads done
+        for (int i = c0 + tid; i < c1; i += kBlock) s_idx[i - c0] = idx[i];
+        __syncthreads();
+        const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
+        load(ta, c0, c0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        // tiles alternate between the two register sets
+        // (the scheduling barriers keep every load of the next tile ahead of
+        // the stores, which the exact wait count relies on)
+        for (int t = 0; t < n_tiles; t += 2) {
+            const int t0 = c0 + t * kTile;
+            if (t + 1 < n_tiles) load(tb, t0 + kTile, c0);
+            __builtin_amdgcn_sched_barrier(0);
+            store(ta);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<kStores>();                     // tile t+1's reads have landed
+            __syncthreads();
+            if (t + 1 >= n_tiles) break;
+            if (t + 2 < n_tiles) load(ta, t0 + 2 * kTile, c0);
+            __builtin_amdgcn_sched_barrier(0);
+            store(tb);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<kStores>();
+            __syncthreads();
+        }
+    }
 }
 
 template <int ROWB, int PARTS>
@@ -68,15 +175,6 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
                                                          int32_t* __restrict__ head_len,
                                                          uint32_t* __restrict__ queue)
 {
-    constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
-    constexpr int kCpp = kChunks / PARTS;               // chunks per column part
-    static_assert(kCpp * PARTS == kChunks, "parts split the row evenly");
-    constexpr int kRowsPerStep = kBlock / kCpp;
-    constexpr int kTile = kRowsPerStep * kUnroll;
-    constexpr int kPosPerThread = (kTile + kBlock - 1) / kBlock;
-    constexpr int kStores = kUnroll + kPosPerThread;    // memory stores per thread per tile
-    static_assert(kIdxChunk % kTile == 0, "tiles never straddle an index chunk");
-
     __shared__ int32_t s_idx[kIdxChunk];
     __shared__ int s_item;
 
@@ -101,92 +199,45 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(unsigned char* __restri
         const int n_keep = counts ? min(counts[head], kept_stride) : budget;
         if (n_keep < 0) continue;
         if (counts && moves_pos && threadIdx.x == 0) head_len[head] = n_keep;
-        unsigned char* rows = (is_v ? v : k) + (size_t)head * (size_t)cap * ROWB;
-        int32_t* hpos = pos + (size_t)head * (size_t)cap;
-        const int32_t* idx = kept + (size_t)head * (size_t)kept_stride;
-        const __amdgpu_buffer_rsrc_t rrows =
-            __builtin_amdgcn_make_buffer_rsrc(rows, 0, len * ROWB, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rpos =
-            __builtin_amdgcn_make_buffer_rsrc(hpos, 0, len * 4, kBufferWord3);
+        move_stream<ROWB, PARTS>((is_v ? v : k) + (size_t)head * (size_t)cap * ROWB,
+                                 pos + (size_t)head * (size_t)cap,
+                                 kept + (size_t)head * (size_t)kept_stride, n_keep, len, part,
+                                 moves_pos, s_idx);
+    }
+}
 
-        const int tid = threadIdx.x;
-        const int c = part * kCpp + tid % kCpp;
-        const int rs = tid / kCpp;
+// A ragged batch of sequences with uniform budgets in one launch: the K and
+// V streams of every head of every sequence in the table, all `budget` rows
+// long, taken by the workgroups in turn (stream i by workgroup i mod grid).
+struct CompactSeq {
+    unsigned char* k;
+    unsigned char* v;
+    int32_t* pos;
+    const int32_t* kept;   // the sequence's kept lists, [heads][budget]
+    int32_t cap;
+    int32_t len;
+};
+struct CompactBatch {
+    CompactSeq seq[kCompactBatch];
+};
 
-        // one tile's data in flight: rows, their destinations, positions
-        struct Tile {
-            u32x4 buf[kUnroll];
-            uint32_t dst[kUnroll];
-            uint32_t pval[kPosPerThread];
-            uint32_t pdst[kPosPerThread];
-        };
-        Tile ta, tb;
-
-        auto load = [&](Tile& t, int t0, int c0) {
-            // all of the tile's indices first, so the LDS reads overlap
-            int srcs[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int r = t0 + u * kRowsPerStep + rs;
-                srcs[u] = s_idx[min(r, c0 + kIdxChunk - 1) - c0];
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int r = t0 + u * kRowsPerStep + rs;
-                const int src = r < n_keep ? srcs[u] : r;
-                const bool mv = r < n_keep && src != r && (unsigned)src < (unsigned)len;
-                const uint32_t from = mv ? (uint32_t)src * ROWB + 16u * c : kDrop;
-                t.dst[u] = mv ? (uint32_t)r * ROWB + 16u * c : kDrop;
-                t.buf[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrows, from, 0, kNT));
-            }
-#pragma unroll
-            for (int q = 0; q < kPosPerThread; ++q) {
-                const int i = q * kBlock + tid;
-                const int r = t0 + i;
-                const int src = (i < kTile && r < n_keep) ? s_idx[r - c0] : r;
-                const bool mv = moves_pos && i < kTile && r < n_keep && src != r && (unsigned)src < (unsigned)len;
-                t.pdst[q] = mv ? (uint32_t)r * 4u : kDrop;
-                t.pval[q] = __builtin_amdgcn_raw_buffer_load_b32(rpos, mv ? (uint32_t)src * 4u : kDrop, 0, 0);
-            }
-        };
-        auto store = [&](const Tile& t) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                __builtin_amdgcn_raw_buffer_store_b128(t.buf[u], rrows, t.dst[u], 0, kNT);
-#pragma unroll
-            for (int q = 0; q < kPosPerThread; ++q)
-                __builtin_amdgcn_raw_buffer_store_b32(t.pval[q], rpos, t.pdst[q], 0, 0);
-        };
-
-        for (int c0 = 0; c0 < n_keep; c0 += kIdxChunk) {
-            const int c1 = min(n_keep, c0 + kIdxChunk);
-            __syncthreads();                               // previous chunk's index reads done
-            for (int i = c0 + tid; i < c1; i += kBlock) s_idx[i - c0] = idx[i];
-            __syncthreads();
-            const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
-            load(ta, c0, c0);
-            wait_vmcnt<0>();
-            __syncthreads();
-            // tiles alternate between the two register sets
-            // (the scheduling barriers keep every load of the next tile ahead of
-            // the stores, which the exact wait count relies on)
-            for (int t = 0; t < n_tiles; t += 2) {
-                const int t0 = c0 + t * kTile;
-                if (t + 1 < n_tiles) load(tb, t0 + kTile, c0);
-                __builtin_amdgcn_sched_barrier(0);
-                store(ta);
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<kStores>();                     // tile t+1's reads have landed
-                __syncthreads();
-                if (t + 1 >= n_tiles) break;
-                if (t + 2 < n_tiles) load(ta, t0 + 2 * kTile, c0);
-                __builtin_amdgcn_sched_barrier(0);
-                store(tb);
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<kStores>();
-                __syncthreads();
-            }
-        }
+template <int ROWB>
+__global__ __launch_bounds__(kBlock) void compact_batch_kernel(const CompactBatch b, int n_seq,
+                                                               int n_heads, int budget)
+{
+    __shared__ int32_t s_idx[kIdxChunk];
+    const int per_seq = 2 * n_heads;
+    const int items = n_seq * per_seq;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int s = item / per_seq;
+        const int stream_id = item - s * per_seq;
+        const int head = stream_id >> 1;
+        const bool is_v = (stream_id & 1) != 0;
+        const int64_t cap = b.seq[s].cap;
+        move_stream<ROWB, 1>((is_v ? b.seq[s].v : b.seq[s].k) + (size_t)head * (size_t)cap * ROWB,
+                             b.seq[s].pos + (size_t)head * (size_t)cap,
+                             b.seq[s].kept + (size_t)head * (size_t)budget, budget, b.seq[s].len, 0,
+                             !is_v, s_idx);
     }
 }
 
@@ -275,6 +326,45 @@ hipError_t launch(void* k, void* v, int32_t* pos, int64_t cap, int len, int n_he
 }
 
 }  // namespace
+
+hipError_t launch_compact_batch(int row_bytes, int n_seq, void* const* k, void* const* v,
+                                int32_t* const* pos, const int* cap, const int* len,
+                                const int32_t* const* kept, int n_heads, int budget,
+                                hipStream_t stream)
+{
+    if (n_heads <= 0 || budget <= 0 || n_seq <= 0) return hipSuccess;
+    for (int s = 0; s < n_seq; ++s)
+        if ((int64_t)len[s] * row_bytes >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return hipErrorInvalidDevice;
+    for (int s0 = 0; s0 < n_seq; s0 += kCompactBatch) {
+        const int cnt = std::min(kCompactBatch, n_seq - s0);
+        const int64_t streams = (int64_t)cnt * 2 * n_heads;
+        if (streams > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        CompactBatch b{};
+        for (int j = 0; j < cnt; ++j) {
+            const int s = s0 + j;
+            b.seq[j] = CompactSeq{static_cast<unsigned char*>(k[s]), static_cast<unsigned char*>(v[s]),
+                                  pos[s], kept[s], cap[s], len[s]};
+        }
+        // streams of equal length taken in turn by workgroups on three
+        // quarters of the compute units (as for one sequence, fewer copy
+        // streams in flight move the rows faster)
+        const int grid = (int)std::min<int64_t>(streams, std::max(1, cus * 3 / 4));
+        switch (row_bytes) {
+        case 128: hipLaunchKernelGGL(compact_batch_kernel<128>, dim3(grid), dim3(kBlock), 0, stream, b, cnt, n_heads, budget); break;
+        case 256: hipLaunchKernelGGL(compact_batch_kernel<256>, dim3(grid), dim3(kBlock), 0, stream, b, cnt, n_heads, budget); break;
+        case 512: hipLaunchKernelGGL(compact_batch_kernel<512>, dim3(grid), dim3(kBlock), 0, stream, b, cnt, n_heads, budget); break;
+        default: return hipErrorInvalidValue;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 // counter, item count and one entry per column part (at most 512 / 128 per stream)
 int64_t compact_queue_bytes(int64_t n_heads) { return 8 + 4 * 2 * 4 * n_heads; }

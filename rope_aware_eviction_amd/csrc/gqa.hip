@@ -686,7 +686,7 @@ hipError_t launch_g(const void* k, int64_t cap, int len, int n_heads, int64_t p_
     hipLaunchKernelGGL(gqa_stats_kernel, dim3(n_heads), dim3(64), 0, stream, partial, tiles, G,
                        len, head_len, stats);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !scores) return e;   // no score array: raw scores and statistics only
     hipLaunchKernelGGL((gqa_norm_kernel<G>), dim3((unsigned)grid), dim3(kBlock), 0, stream, raw,
                        stats, len, tiles, scores, head_len);
     return hipGetLastError();
@@ -723,6 +723,43 @@ int64_t gqa_workspace_bytes(int64_t n_heads, int64_t len, int group)
     const int64_t tiles = (len + kTileRows - 1) / kTileRows;
     return up(n_heads * len * group * 4) + up(n_heads * tiles * group * 4 * 8) +
            up(n_heads * group * 16) + up(n_heads * kBopBytesPerHead);
+}
+
+void gqa_workspace_views(void* workspace, int64_t n_heads, int64_t len, int group, float** raw,
+                         double2** stats)
+{
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    const int64_t tiles = (len + kTileRows - 1) / kTileRows;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    *raw = reinterpret_cast<float*>(ws);
+    *stats = reinterpret_cast<double2*>(ws + up(n_heads * len * group * 4) +
+                                        up(n_heads * tiles * group * 4 * 8));
+}
+
+hipError_t launch_gqa_normalize(int group, const float* raw, const double2* stats, int len,
+                                int n_heads, float* scores, hipStream_t stream)
+{
+    if (len <= 0 || n_heads <= 0) return hipSuccess;
+    const int tiles = (len + kTileRows - 1) / kTileRows;
+    const int64_t grid = (int64_t)tiles * n_heads;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+#define TRI_NORM_CASE(G)                                                                          \
+    case G:                                                                                       \
+        hipLaunchKernelGGL((gqa_norm_kernel<G>), dim3((unsigned)grid), dim3(kBlock), 0, stream,   \
+                           raw, stats, len, tiles, scores, nullptr);                              \
+        break;
+    switch (group) {
+        TRI_NORM_CASE(2)
+        TRI_NORM_CASE(3)
+        TRI_NORM_CASE(4)
+        TRI_NORM_CASE(5)
+        TRI_NORM_CASE(6)
+        TRI_NORM_CASE(7)
+        TRI_NORM_CASE(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef TRI_NORM_CASE
+    return hipGetLastError();
 }
 
 hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void* k, int64_t cap,

@@ -202,8 +202,14 @@ __global__ __launch_bounds__(kBlock) void score_kernel(
     // sc1 stores: measured to cost the read stream far less than default
     // write-back stores, while the scores stay cached for the selection
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(out, 0, len * 4, kBufferWord3);
-    for (int i = tid; i < row_end - tile_start; i += kBlock)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_out[i]), ro, (tile_start + i) * 4, 0, kSC1);
+    // A row with an infinite or NaN element has no score: any non-finite
+    // total (an infinite element alone gives +inf or -inf) is stored as NaN,
+    // which every selection ranks below all numbers.
+    for (int i = tid; i < row_end - tile_start; i += kBlock) {
+        uint32_t x = __float_as_uint(s_out[i]);
+        if ((x & 0x7F800000u) == 0x7F800000u) x = 0x7FC00000u;
+        __builtin_amdgcn_raw_buffer_store_b32(x, ro, (tile_start + i) * 4, 0, kSC1);
+    }
 }
 
 template <int D, bool BF16>

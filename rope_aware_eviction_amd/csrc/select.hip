@@ -1,8 +1,8 @@
 // Per-head top-B selection with a deterministic tie-break.
 //
 // Source: romaanj.github.io "TriAttention" review, section "Method" (prune
-// back to the budget) and figure 4 caption (only the top-scoring keys
-// survive); dimensionstp.github.io review, section 3-2 item 5 (keep the
+// back to the budget) and figure 4 caption (the prune retains the
+// highest-scoring keys); dimensionstp.github.io review, section 3-2 item 5 (keep the
 // top-budget keys, evict the rest).  Reading: equal scores go to the lower
 // position, which is the lower slot because positions ascend with slots;
 // NaN ranks below every number; -0 equals +0.
@@ -17,6 +17,9 @@
 // them from there.  The output pass gives each wave a contiguous segment of
 // slots; ballots and popcounts give every kept key its rank among the kept
 // keys in slot order, so the kept list comes out ascending with no sort.
+#include <algorithm>
+#include <vector>
+
 #include "tri_internal.h"
 
 namespace tri {
@@ -40,6 +43,9 @@ constexpr int kHistRow = (1 << kRegDigitBits) + 64;
 // keys of a head staged in LDS up to this many (4 bytes each, plus the
 // 8 KB histogram, within the 160 KB LDS of a gfx950 workgroup)
 constexpr int kLdsKeysMax = 36864;
+// sequences per launch of the batched selection (the table travels in the
+// kernel arguments: 24 bytes per sequence)
+constexpr int kSelectBatch = 64;
 
 // Order-preserving map of fp32 scores to uint32 keys.  Key 0 is never
 // produced (it marks slots past the end of a head, below every real key).
@@ -138,29 +144,22 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane)
     return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
+// The selection of one head of n > budget keys at sc into out, with
+// kHistBins words of LDS at smem for the histogram (kInLds: then n more for
+// the staged keys).  Every thread of the workgroup calls it.
 template <bool kInLds>
-__global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict__ scores,
-                                                        int stride, int budget,
-                                                        int32_t* __restrict__ kept,
-                                                        int kept_stride,
-                                                        const int32_t* __restrict__ head_len)
+__device__ __forceinline__ void select_lds_head(uint32_t* smem, const float* __restrict__ sc, int n,
+                                                int budget, int32_t* __restrict__ out)
 {
-    extern __shared__ uint32_t smem[];
     uint32_t* hist = smem;                             // [kHistBins]
     uint32_t* lds_keys = smem + kHistBins;             // [n] when kInLds
     __shared__ uint32_t s_wmin[kWaves], s_wmax[kWaves];
     __shared__ uint32_t s_wgt[kWaves], s_weq[kWaves];
     __shared__ uint32_t s_digit, s_above;
 
-    // keys of this head: all `stride`, or its own length (ragged heads); a
-    // head with at most `budget` keys keeps them all and gets no list
-    const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
-    if (n <= budget) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const float* sc = scores + (size_t)blockIdx.x * (size_t)stride;
-    int32_t* out = kept + (size_t)blockIdx.x * (size_t)kept_stride;
 
     // stage keys (when they fit) and find the key range of the head
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -307,6 +306,22 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict_
     }
 }
 
+template <bool kInLds>
+__global__ __launch_bounds__(kBlock) void select_kernel(const float* __restrict__ scores,
+                                                        int stride, int budget,
+                                                        int32_t* __restrict__ kept,
+                                                        int kept_stride,
+                                                        const int32_t* __restrict__ head_len)
+{
+    extern __shared__ uint32_t smem[];
+    // keys of this head: all `stride`, or its own length (ragged heads); a
+    // head with at most `budget` keys keeps them all and gets no list
+    const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
+    if (n <= budget) return;
+    select_lds_head<kInLds>(smem, scores + (size_t)blockIdx.x * (size_t)stride, n, budget,
+                            kept + (size_t)blockIdx.x * (size_t)kept_stride);
+}
+
 // Digit holding the rem-th largest counted key, found by the whole
 // workgroup: thread t owns a run of `per` bins counted from the top (thread 0
 // the highest), the run sums are scanned within each wave and across the
@@ -369,44 +384,24 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t nbins,
 // the keys outside it (min > max when there are none); and hist_out[head],
 // the histogram of the keys outside it by their top 12 bits (the first
 // radix digit of the layer-wide selection, whose binning needs no range).
-template <int KPT, int NT, bool RESERVE = false>
-__global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict__ scores,
-                                                        int stride, int budget,
-                                                        int32_t* __restrict__ kept,
-                                                        int kept_stride,
-                                                        const int32_t* __restrict__ head_len,
-                                                        uint4* __restrict__ rec = nullptr,
-                                                        uint32_t* __restrict__ hist_out = nullptr)
-{
-    constexpr int kW = NT / 64;
-    __shared__ uint32_t hist[1 << kRegDigitBits];
-    __shared__ uint32_t s_cand[64];
-    __shared__ uint32_t s_wa[kW], s_wb[kW], s_run[kW];
-    __shared__ uint32_t s_digit, s_above, s_inbin, s_ncand;
-    __shared__ uint32_t s_T, s_need, s_tie;
+// LDS of one register-resident selection.
+template <int NT>
+struct RegLds {
+    uint32_t hist[1 << kRegDigitBits];
+    uint32_t cand[64];
+    uint32_t wa[NT / 64], wb[NT / 64], run[NT / 64];
+    uint32_t digit, above, inbin, ncand, T, need, tie;
+};
 
-    // keys of this head: all `stride`, or its own length (ragged heads); a
-    // head with at most `budget` keys keeps them all and gets no list
-    const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
-    if (n <= budget) {
-        // RESERVE: every key is reserved (Th = 0 lies below every real key)
-        if constexpr (RESERVE) {
-            for (int b = threadIdx.x; b < kHistRow; b += NT)
-                hist_out[(size_t)blockIdx.x * kHistRow + b] = 0u;
-            if (threadIdx.x == 0) rec[blockIdx.x] = make_uint4(0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0u);
-        }
-        return;
-    }
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const float* sc = scores + (size_t)blockIdx.x * (size_t)stride;
-    int32_t* out = RESERVE ? nullptr : kept + (size_t)blockIdx.x * (size_t)kept_stride;
-    const int seg0 = wave * (64 * KPT) + lane;     // slot of key[0]
-
-    // Slots past the head's end hold key 0, below every real key (ordered_key
-    // never returns 0): with budget < n they are never kept.
-    uint32_t key[KPT];
+// The keys a register-resident selection ranks: key[c] of lane l of wave w
+// is the order-preserving key of slot w * 64 * KPT + 64 * c + l, or 0 (below
+// every real key) for slots past the head's n keys.
+//
+// ScoreKeys: the fp32 scores of the head.
+struct ScoreKeys {
+    const float* sc;
+    template <int KPT>
+    __device__ __forceinline__ void load(uint32_t (&key)[KPT], int seg0, int n) const
     {
         // bounds-checked buffer loads: one offset register for all KPT loads
         const __amdgpu_buffer_rsrc_t rsrc =
@@ -420,6 +415,100 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
         for (int c = 0; c < KPT; ++c)
             key[c] = ordered_key(__uint_as_float(x[c])) & (0u - (seg0 + 64 * c < n ? 1u : 0u));
     }
+};
+
+// GqaKeys<G>: the GQA score of the head formed on the fly from its G raw
+// per-query-head scores [n][G] and their statistics (mean, deviation): the
+// largest z_g = (s_g - mean_g) / deviation_g over the finite s_g (z_g = 0
+// for a flat row, deviation 0), in fp64 and rounded once to fp32 in the same
+// operations as the GQA normalize kernel, so the key equals the one of the
+// score that kernel writes; NaN when no s_g is finite.
+template <int G>
+struct GqaKeys {
+    const float* raw;          // the head's raw scores, [n][G]
+    const double2* stats;      // the head's [G] (mean, deviation)
+    template <int KPT>
+    __device__ __forceinline__ void load(uint32_t (&key)[KPT], int seg0, int n) const
+    {
+        double mean[G], inv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const double2 st = stats[g];
+            mean[g] = st.x;
+            inv[g] = st.y > 0.0 ? 1.0 / st.y : 0.0;
+        }
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)raw, 0, n * G * 4, kBufferWord3);
+        constexpr int kRows = G <= 4 ? 8 : 4;     // rows in flight per lane
+        static_assert(KPT % kRows == 0, "whole groups of rows");
+#pragma unroll
+        for (int c0 = 0; c0 < KPT; c0 += kRows) {
+            uint32_t x[kRows][G];
+#pragma unroll
+            for (int c = 0; c < kRows; ++c)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    x[c][g] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rsrc, ((seg0 + 64 * (c0 + c)) * G + g) * 4, 0, 0);
+#pragma unroll
+            for (int c = 0; c < kRows; ++c) {
+                double best = __longlong_as_double(0x7FF8000000000000ll);   // NaN
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const double sg = (double)__uint_as_float(x[c][g]);
+                    if (isfinite(sg)) {
+                        const double z = (sg - mean[g]) * inv[g];
+                        if (isnan(best) || z > best) best = z;
+                    }
+                }
+                key[c0 + c] = ordered_key((float)best) &
+                              (0u - (seg0 + 64 * (c0 + c) < n ? 1u : 0u));
+            }
+        }
+    }
+};
+
+// The selection of one head of n keys (from `keys`): the kept list goes to
+// out (RESERVE: the record to *rec and the histogram row to hist_row).  Every
+// thread of the workgroup calls it.
+template <int KPT, int NT, bool RESERVE, class Keys>
+__device__ __forceinline__ void select_reg_head(RegLds<NT>& L, const Keys& keys, int n,
+                                                int budget, int32_t* __restrict__ out,
+                                                uint4* __restrict__ rec,
+                                                uint32_t* __restrict__ hist_row)
+{
+    constexpr int kW = NT / 64;
+    uint32_t* hist = L.hist;
+    uint32_t* s_cand = L.cand;
+    uint32_t* s_wa = L.wa;
+    uint32_t* s_wb = L.wb;
+    uint32_t* s_run = L.run;
+    uint32_t& s_digit = L.digit;
+    uint32_t& s_above = L.above;
+    uint32_t& s_inbin = L.inbin;
+    uint32_t& s_ncand = L.ncand;
+    uint32_t& s_T = L.T;
+    uint32_t& s_need = L.need;
+    uint32_t& s_tie = L.tie;
+
+    // a head with at most `budget` keys keeps them all and gets no list
+    if (n <= budget) {
+        // RESERVE: every key is reserved (Th = 0 lies below every real key)
+        if constexpr (RESERVE) {
+            for (int b = threadIdx.x; b < kHistRow; b += NT) hist_row[b] = 0u;
+            if (threadIdx.x == 0) *rec = make_uint4(0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0u);
+        }
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int seg0 = wave * (64 * KPT) + lane;     // slot of key[0]
+
+    // Slots past the head's end hold key 0, below every real key (ordered_key
+    // never returns 0): with budget < n they are never kept.
+    uint32_t key[KPT];
+    keys.template load<KPT>(key, seg0, n);
 
     uint32_t kmin, kmax;
     {
@@ -470,16 +559,15 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
             s_wb[wave] = hi;
         }
         __syncthreads();
-        uint32_t* ho = hist_out + (size_t)blockIdx.x * kHistRow;
-        for (uint32_t b = tid; b < (1u << kRegDigitBits); b += NT) ho[b] = hist[b];
+        for (uint32_t b = tid; b < (1u << kRegDigitBits); b += NT) hist_row[b] = hist[b];
         static_assert(!RESERVE || NT == 1024, "group sums assume 1024 threads");
-        write_group_sums(hist, 1u << kRegDigitBits, ho + (1 << kRegDigitBits), tid);
+        write_group_sums(hist, 1u << kRegDigitBits, hist_row + (1 << kRegDigitBits), tid);
         if (tid == 0) {
             for (int x = 0; x < kW; ++x) {
                 lo = min(lo, s_wa[x]);
                 hi = max(hi, s_wb[x]);
             }
-            rec[blockIdx.x] = make_uint4(th, (uint32_t)sh, lo, hi);
+            *rec = make_uint4(th, (uint32_t)sh, lo, hi);
         }
     };
 
@@ -682,6 +770,412 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
     }
 }
 
+
+// One workgroup per head of one sequence: heads of `stride` keys (with
+// head_len, head h has its own length up to stride); kept lists of head h
+// start at kept + h * kept_stride (RESERVE: rec[h] and hist_out row h).
+template <int KPT, int NT, bool RESERVE = false>
+__global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict__ scores,
+                                                        int stride, int budget,
+                                                        int32_t* __restrict__ kept,
+                                                        int kept_stride,
+                                                        const int32_t* __restrict__ head_len,
+                                                        uint4* __restrict__ rec = nullptr,
+                                                        uint32_t* __restrict__ hist_out = nullptr)
+{
+    __shared__ RegLds<NT> L;
+    const int n = head_len ? max(0, min(head_len[blockIdx.x], stride)) : stride;
+    select_reg_head<KPT, NT, RESERVE>(
+        L, ScoreKeys{scores + (size_t)blockIdx.x * (size_t)stride}, n, budget,
+        RESERVE ? nullptr : kept + (size_t)blockIdx.x * (size_t)kept_stride,
+        RESERVE ? rec + blockIdx.x : nullptr,
+        RESERVE ? hist_out + (size_t)blockIdx.x * kHistRow : nullptr);
+}
+
+// GQA without the normalized score array: one workgroup per head of `len`
+// keys selects on the max-z keys formed from the raw per-query-head scores
+// [head][len][G] and the statistics [head][G] (GqaKeys).
+template <int KPT, int G>
+__global__ __launch_bounds__(kBlock) void select_gqa_kernel(const float* __restrict__ raw,
+                                                            const double2* __restrict__ stats,
+                                                            int len, int budget,
+                                                            int32_t* __restrict__ kept,
+                                                            int kept_stride)
+{
+    __shared__ RegLds<kBlock> L;
+    const int h = blockIdx.x;
+    select_reg_head<KPT, kBlock, false>(
+        L, GqaKeys<G>{raw + (size_t)h * (size_t)len * G, stats + (size_t)h * G}, len, budget,
+        kept + (size_t)h * (size_t)kept_stride, nullptr, nullptr);
+}
+
+// A ragged batch in one launch: the heads of up to kSelectBatch sequences of
+// the same length class (at most 64 * KPT * NT / 64 keys each), one
+// workgroup per head.  Workgroup w selects head w % heads of sequence
+// w / heads of the table; the caller orders the table longest first, so the
+// long heads are dispatched first.
+struct SelectSeq {
+    const float* scores;   // the sequence's scores, [heads][n]
+    int32_t* kept;         // its kept lists, [heads][budget]
+    int32_t n;             // keys per head
+    int32_t pad;
+};
+struct SelectBatch {
+    SelectSeq seq[kSelectBatch];
+};
+
+template <int KPT>
+__global__ __launch_bounds__(kBlock) void select_batch_kernel(const SelectBatch b, int heads,
+                                                              int budget)
+{
+    __shared__ RegLds<kBlock> L;
+    const int s = blockIdx.x / heads;
+    const int h = blockIdx.x - s * heads;
+    const float* sc = b.seq[s].scores;
+    int32_t* kept = b.seq[s].kept;
+    const int n = b.seq[s].n;
+    select_reg_head<KPT, kBlock, false>(L, ScoreKeys{sc + (size_t)h * (size_t)n}, n, budget,
+                                        kept + (size_t)h * (size_t)budget, nullptr, nullptr);
+}
+
+
+// ---------------------------------------------------------------------------
+// Heads longer than the register-resident selection takes (more than 32768
+// keys, up to kWideMax), with one read of the scores:
+//
+// 1. A fixed sample of kSample keys: kSampleRuns runs of kSampleRun
+//    consecutive slots, run c at a hashed offset inside the c-th
+//    1/kSampleRuns of the head (stratified, and jittered so that scores that
+//    vary periodically with the position, as the distance preference makes
+//    them, are not sampled at one phase).  With r the number of sample keys
+//    expected among the head's top B (B * kSample / n, rounded up) and
+//    delta = max(32, 6 sqrt(r)), two levels of 4096-bin histograms of the
+//    sample find the bins of its (r - delta)-th and (r + delta)-th largest
+//    keys: hi is the top of the first, lo the bottom of the second.  The
+//    bracket [lo, hi] holds the head's B-th largest key unless the sample
+//    misrepresents the head.
+// 2. One pass over the scores: keys above hi set a bit in the "above"
+//    bitmap; keys in [lo, hi] are candidates: a bit in the candidate bitmap,
+//    and (key, slot) appended to the wave's own segment of an LDS list while
+//    it has room (the count is wave-uniform, so appending needs no atomics).
+// 3. If fewer than B keys lie above hi, at least B at or above lo, and the
+//    candidates fit the list (or lo == hi: then they all equal the
+//    threshold), the threshold T is found among the candidates alone
+//    (offset-radix passes over the LDS list, then one wave ranks the last 64
+//    or fewer); candidates above T (T and above
+//    when equal keys do not straddle it) join the "above" bitmap and those
+//    equal to T make up the candidate bitmap.  Otherwise the head is selected
+//    by the general path (select_lds_head, which reads the scores again), so
+//    the result never depends on the sample.
+// 4. The kept list comes from the two bitmaps in slot order: every "above"
+//    slot and the first need_eq slots equal to T.  Each lane takes a
+//    contiguous run of 64-slot blocks; scans of the per-lane counts give
+//    every lane its place in the list.
+// Dynamic LDS: the two bitmaps (ceil(n / 64) 64-bit words each), a 4096-bin
+// histogram, and the candidate list (cmax keys, then cmax slots, in kWaves
+// equal segments).
+constexpr int kWideMax = 1 << 18;
+constexpr int kSampleRuns = 128;
+constexpr int kSampleRun = 32;
+constexpr int kSample = kSampleRuns * kSampleRun;
+static_assert(kSample == 4 * kBlock, "four sample keys per thread");
+constexpr int kWideBins = 1 << kRegDigitBits;
+constexpr int kWideLdsBytes = 155648;          // dynamic LDS of the wide selection
+constexpr int kPassBatch = 16;                 // score loads per thread in flight in the pass
+static_assert(kWideLdsBytes >= kHistBins * 4, "room for the general path's histogram");
+
+__global__ __launch_bounds__(kBlock) void select_wide_kernel(const float* __restrict__ scores,
+                                                             int n, int budget,
+                                                             int32_t* __restrict__ kept,
+                                                             int kept_stride, int cmax)
+{
+    // 16-byte aligned: the bitmaps are 64-bit words, and LDS atomics on them
+    // (ds_or_b64) need natural alignment
+    extern __shared__ __align__(16) uint32_t smem[];
+    __shared__ uint32_t s_wa[kWaves], s_wb[kWaves], s_run[kWaves], s_cnt[kWaves];
+    __shared__ uint32_t s_cand[64];
+    __shared__ uint32_t s_digit, s_above, s_inbin, s_nc, s_T, s_need, s_tie;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const float* sc = scores + (size_t)blockIdx.x * (size_t)n;
+    int32_t* out = kept + (size_t)blockIdx.x * (size_t)kept_stride;
+    const int W64 = (n + 63) / 64;                       // 64-slot blocks
+    unsigned long long* above_bm = reinterpret_cast<unsigned long long*>(smem);
+    unsigned long long* cand_bm = above_bm + W64;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(cand_bm + W64);
+    uint32_t* ckey = hist + kWideBins;
+    uint32_t* cslot = ckey + cmax;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)sc, 0, n * 4, kBufferWord3);
+    const unsigned long long below = (1ull << lane) - 1ull;
+
+    // ---- 1. the bracket from the sample
+    uint32_t lo, hi;
+    {
+        // run c of kSampleRun keys at a hashed offset inside the c-th
+        // 1/kSampleRuns of the head; thread t reads keys t % 8, +8, +16, +24
+        // of run t / 8
+        const int run = tid / (kSampleRun / 4);
+        const int j = tid % (kSampleRun / 4);
+        const int stride = n / kSampleRuns;
+        uint32_t hsh = (uint32_t)run * 0x9E3779B1u + 0x7F4A7C15u;
+        hsh ^= hsh >> 15;
+        hsh *= 0x2C1B3C6Du;
+        hsh ^= hsh >> 12;
+        const int start = run * stride + (int)(hsh % (uint32_t)(stride - kSampleRun + 1));
+        uint32_t sk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            sk[u] = ordered_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rsrc, (start + j + u * (kSampleRun / 4)) * 4, 0, 0)));
+        uint32_t smn = min(min(sk[0], sk[1]), min(sk[2], sk[3]));
+        uint32_t smx = max(max(sk[0], sk[1]), max(sk[2], sk[3]));
+        smn = wave_min(smn);
+        smx = wave_max(smx);
+        if (lane == 0) {
+            s_wa[wave] = smn;
+            s_wb[wave] = smx;
+        }
+        __syncthreads();
+        smn = s_wa[0];
+        smx = s_wb[0];
+        for (int x = 1; x < kWaves; ++x) {
+            smn = min(smn, s_wa[x]);
+            smx = max(smx, s_wb[x]);
+        }
+        // sample ranks (from the top) of the bracket's ends, then two levels
+        // of histograms narrow [base, top] down to the bins that hold them
+        const int64_t r = ((int64_t)budget * kSample + n - 1) / n;
+        const int64_t delta = max((int64_t)32, (int64_t)ceil(6.0 * sqrt((double)r)));
+        uint32_t r_hi = (uint32_t)max((int64_t)1, r - delta);
+        uint32_t r_lo = (uint32_t)min((int64_t)kSample, r + delta);
+        uint32_t base = smn, top = smx;
+        for (int level = 0; level < 2 && base != top; ++level) {
+            const int wb = 32 - __clz((int)(top - base));
+            const int nb = min(kRegDigitBits, wb);
+            const int sh = wb - nb;
+            const uint32_t nbins = 1u << nb;
+            __syncthreads();                            // previous readers of hist / s_*
+            for (uint32_t b = tid; b < nbins; b += kBlock) hist[b] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (sk[u] >= base && sk[u] <= top) atomicAdd(&hist[(sk[u] - base) >> sh], 1u);
+            __syncthreads();
+            find_digit<kBlock>(hist, nbins, r_hi, tid, lane, wave, s_run, &s_digit, &s_above, &s_inbin);
+            __syncthreads();
+            const uint32_t d_hi = s_digit;
+            const uint32_t a_hi = s_above;
+            __syncthreads();
+            find_digit<kBlock>(hist, nbins, r_lo, tid, lane, wave, s_run, &s_digit, &s_above, &s_inbin);
+            __syncthreads();
+            const uint32_t d_lo = s_digit;
+            top = (uint32_t)min((uint64_t)top, (uint64_t)base + ((uint64_t)(d_hi + 1u) << sh) - 1u);
+            base = base + (d_lo << sh);
+            r_hi -= a_hi;                               // sample keys above top are no longer counted
+            r_lo -= a_hi;
+        }
+        lo = base;
+        hi = top;
+    }
+
+    // ---- 2. one pass: "above" and candidate bitmaps; each wave appends its
+    // candidates to a segment of the list of its own, counted in a register
+    // (no atomics: every lane of the wave holds the same count)
+    const uint32_t segcap = (uint32_t)cmax / kWaves;
+    uint32_t* wkey = ckey + wave * segcap;
+    uint32_t* wslot = cslot + wave * segcap;
+    uint32_t n_above = 0u, n_cw = 0u;                   // this wave's counts
+    for (int i0 = 0; i0 < n; i0 += kBlock * kPassBatch) {
+        uint32_t x[kPassBatch];
+#pragma unroll
+        for (int u = 0; u < kPassBatch; ++u)
+            x[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (i0 + u * kBlock + tid) * 4, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kPassBatch; ++u) {
+            const int blk = i0 + u * kBlock + wave * 64;   // the wave's 64 slots
+            const int i = blk + lane;
+            const uint32_t key = ordered_key(__uint_as_float(x[u]));
+            const bool valid = i < n;
+            const bool ab = valid && key > hi;
+            const bool cd = valid && !ab && key >= lo;
+            const unsigned long long ma = __ballot(ab);
+            const unsigned long long mc = __ballot(cd);
+            if (lane == 0 && blk < n) {
+                above_bm[blk >> 6] = ma;
+                cand_bm[blk >> 6] = mc;
+            }
+            n_above += (uint32_t)__popcll(ma);
+            const uint32_t at = n_cw + (uint32_t)__popcll(mc & below);
+            if (cd && at < segcap) {
+                wkey[at] = key;
+                wslot[at] = (uint32_t)i;
+            }
+            n_cw += (uint32_t)__popcll(mc);
+        }
+    }
+    if (lane == 0) {
+        s_wa[wave] = n_above;
+        s_cnt[wave] = n_cw;
+    }
+    __syncthreads();
+    uint32_t total_above = 0u, n_cand = 0u, max_cw = 0u;
+    for (int x = 0; x < kWaves; ++x) {
+        total_above += s_wa[x];
+        n_cand += s_cnt[x];
+        max_cw = max(max_cw, s_cnt[x]);
+    }
+    const bool bracket = total_above < (uint32_t)budget && total_above + n_cand >= (uint32_t)budget &&
+                         (lo == hi || max_cw <= segcap);
+    if (!bracket) {
+        __syncthreads();                                // every thread is done with the bitmaps
+        select_lds_head<false>(smem, sc, n, budget, out);
+        return;
+    }
+
+    // ---- 3. the threshold among the candidates
+    uint32_t T, need_eq;
+    bool tie;
+    const uint32_t rem0 = (uint32_t)budget - total_above;     // in [1, n_cand]
+    if (lo == hi) {
+        T = lo;                                          // every candidate equals T
+        need_eq = rem0;
+        tie = true;
+    } else {
+        const uint32_t my_cnt = s_cnt[wave];            // <= segcap here
+        uint32_t base = lo;
+        int wb = 32 - __clz((int)(hi - lo));            // candidates lie in [base, base + 2^wb)
+        uint32_t rem = rem0;
+        for (;;) {
+            const int nb = min(kRegDigitBits, wb);
+            const int sh = wb - nb;
+            const uint32_t nbins = 1u << nb;
+            const uint32_t span = wb >= 32 ? 0xFFFFFFFFu : (1u << wb) - 1u;
+            __syncthreads();                            // previous readers of hist / s_*
+            for (uint32_t b = tid; b < nbins; b += kBlock) hist[b] = 0u;
+            if (tid == 0) s_nc = 0u;
+            __syncthreads();
+            for (uint32_t c = lane; c < my_cnt; c += 64) {
+                const uint32_t off = wkey[c] - base;
+                if (off <= span) atomicAdd(&hist[off >> sh], 1u);
+            }
+            __syncthreads();
+            find_digit<kBlock>(hist, nbins, rem, tid, lane, wave, s_run, &s_digit, &s_above, &s_inbin);
+            __syncthreads();
+            const uint32_t d = s_digit & (nbins - 1u);
+            const uint32_t in_bin = s_inbin;
+            rem -= s_above;
+            base += d << sh;
+            wb = sh;
+            if (rem == in_bin) {                        // the whole bin is kept
+                T = base;
+                need_eq = 0u;
+                tie = false;
+                break;
+            }
+            if (wb == 0) {                              // one key value straddles the budget
+                T = base;
+                need_eq = rem;
+                tie = true;
+                break;
+            }
+            if (in_bin <= 64u) {
+                // the few candidates left: one wave ranks them (each counts
+                // those above it and equal to it; the rem-th largest has
+                // gt < rem <= gt + eq)
+                const uint32_t cspan = (1u << wb) - 1u;
+                for (uint32_t c = lane; c < my_cnt; c += 64) {
+                    const uint32_t k = wkey[c];
+                    if (k - base <= cspan) {
+                        const uint32_t at = atomicAdd(&s_nc, 1u);
+                        if (at < 64u) s_cand[at] = k;
+                    }
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    const uint32_t v = (uint32_t)lane < in_bin ? s_cand[lane] : 0u;
+                    uint32_t gt = 0u, eq = 0u;
+                    for (uint32_t j = 0; j < in_bin; ++j) {
+                        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)j);
+                        gt += o > v ? 1u : 0u;
+                        eq += o == v ? 1u : 0u;
+                    }
+                    const bool hit = (uint32_t)lane < in_bin && gt < rem && rem <= gt + eq;
+                    const int src = __ffsll((unsigned long long)__ballot(hit)) - 1;   // one exists
+                    const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+                    const uint32_t g = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+                    const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)eq, src);
+                    if (lane == 0) {
+                        s_T = t;
+                        s_need = rem - g;
+                        s_tie = (rem - g) != e;
+                    }
+                }
+                __syncthreads();
+                T = s_T;
+                need_eq = s_need;
+                tie = s_tie != 0u;
+                break;
+            }
+        }
+        // candidates above T (or at least T) join "above"; those equal to T
+        // (with a tie) become the candidate bitmap
+        __syncthreads();
+        for (int w = tid; w < W64; w += kBlock) cand_bm[w] = 0ull;
+        __syncthreads();
+        for (uint32_t c = lane; c < my_cnt; c += 64) {
+            const uint32_t key = wkey[c];
+            const uint32_t slot = wslot[c];
+            if (tie ? key > T : key >= T) atomicOr(&above_bm[slot >> 6], 1ull << (slot & 63u));
+            else if (tie && key == T) atomicOr(&cand_bm[slot >> 6], 1ull << (slot & 63u));
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. the kept list in slot order: wave w owns a run of 64-slot
+    // blocks, and each lane a contiguous part of it; the kept slots before a
+    // lane's part come from a scan of the per-lane counts
+    const int per_wave = (W64 + kWaves - 1) / kWaves;
+    const int per_lane = (per_wave + 63) / 64;
+    const int lb0 = min(W64, wave * per_wave + lane * per_lane);
+    const int lb1 = min(min(W64, (wave + 1) * per_wave), lb0 + per_lane);
+    uint32_t ca = 0u, ce = 0u;
+    for (int b = lb0; b < lb1; ++b) {
+        ca += (uint32_t)__popcll(above_bm[b]);
+        ce += (uint32_t)__popcll(cand_bm[b]);
+    }
+    const uint32_t ia = wave_incl_scan(ca, lane);
+    const uint32_t ie = wave_incl_scan(ce, lane);
+    if (lane == 63) {
+        s_wa[wave] = ia;
+        s_wb[wave] = ie;
+    }
+    __syncthreads();
+    uint32_t a_before = ia - ca, e_before = ie - ce;
+    for (int x = 0; x < wave; ++x) {
+        a_before += s_wa[x];
+        e_before += s_wb[x];
+    }
+    for (int b = lb0; b < lb1; ++b) {
+        const unsigned long long ma = above_bm[b];
+        unsigned long long m = ma | cand_bm[b];
+        while (m) {
+            const int bit = __ffsll(m) - 1;
+            m &= m - 1ull;
+            uint32_t at = 0xFFFFFFFFu;
+            if ((ma >> bit) & 1ull) {
+                at = a_before + min(e_before, need_eq);
+                ++a_before;
+            } else {
+                if (e_before < need_eq) at = a_before + e_before;
+                ++e_before;
+            }
+            if (at < (uint32_t)budget) out[at] = 64 * b + bit;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Head-specific budgets: the n_kv heads of a layer share total = budget *
@@ -1209,6 +1703,17 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
     } else if (n <= kBlock * 32) {
         hipLaunchKernelGGL((select_reg_kernel<32, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
                            scores, n, budget, kept, kept_stride, head_len);
+    } else if (n <= kWideMax && !head_len) {
+        // dynamic LDS: two bitmaps, the histogram, then the candidate list
+        const int64_t words = 2 * 2 * (((int64_t)n + 63) / 64) + kWideBins;   // two 64-bit bitmaps
+        const int cmax = (int)((kWideLdsBytes / 4 - words) / 2);
+        if (cmax < 1024) return hipErrorInvalidValue;
+        // the attribute belongs to the current device: set it on every call
+        hipError_t e = hipFuncSetAttribute((const void*)select_wide_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kWideLdsBytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(select_wide_kernel, dim3(n_heads), dim3(kBlock), (size_t)kWideLdsBytes,
+                           stream, scores, n, budget, kept, kept_stride, cmax);
     } else if (n <= kLdsKeysMax) {
         const size_t lds = (size_t)(kHistBins + n) * sizeof(uint32_t);
         // the attribute belongs to the current device: set it on every call
@@ -1226,6 +1731,79 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
     return hipGetLastError();
 }
 
+
+hipError_t launch_select_gqa(int group, const float* raw, const double2* stats, int len,
+                             int n_heads, int budget, int32_t* kept, int kept_stride,
+                             hipStream_t stream)
+{
+    if (n_heads <= 0 || len <= budget) return hipSuccess;
+    if (len > kBlock * 32) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)n_heads), block(kBlock);
+#define TRI_GQA_SEL(KPT, G)                                                                       \
+    hipLaunchKernelGGL((select_gqa_kernel<KPT, G>), grid, block, 0, stream, raw, stats, len,      \
+                       budget, kept, kept_stride)
+#define TRI_GQA_SEL_G(KPT)                                                                        \
+    switch (group) {                                                                              \
+    case 2: TRI_GQA_SEL(KPT, 2); break;                                                           \
+    case 3: TRI_GQA_SEL(KPT, 3); break;                                                           \
+    case 4: TRI_GQA_SEL(KPT, 4); break;                                                           \
+    case 5: TRI_GQA_SEL(KPT, 5); break;                                                           \
+    case 6: TRI_GQA_SEL(KPT, 6); break;                                                           \
+    case 7: TRI_GQA_SEL(KPT, 7); break;                                                           \
+    case 8: TRI_GQA_SEL(KPT, 8); break;                                                           \
+    default: return hipErrorInvalidValue;                                                         \
+    }
+    if (len <= kBlock * 8) {
+        TRI_GQA_SEL_G(8)
+    } else if (len <= kBlock * 16) {
+        TRI_GQA_SEL_G(16)
+    } else {
+        TRI_GQA_SEL_G(32)
+    }
+#undef TRI_GQA_SEL_G
+#undef TRI_GQA_SEL
+    return hipGetLastError();
+}
+
+hipError_t launch_select_batch(int n_seq, const float* const* scores, int32_t* const* kept,
+                               const int* n, int n_heads, int budget, hipStream_t stream)
+{
+    if (n_heads <= 0) return hipSuccess;
+    // register-resident length classes; longer heads go one sequence at a time
+    std::vector<int> cls[3];
+    for (int s = 0; s < n_seq; ++s) {
+        if (n[s] <= budget) continue;
+        if (n[s] <= kBlock * 8) cls[0].push_back(s);
+        else if (n[s] <= kBlock * 16) cls[1].push_back(s);
+        else if (n[s] <= kBlock * 32) cls[2].push_back(s);
+        else {
+            hipError_t e = launch_select(scores[s], n[s], n_heads, budget, kept[s], budget, nullptr,
+                                         stream);
+            if (e != hipSuccess) return e;
+        }
+    }
+    for (int c = 2; c >= 0; --c) {
+        std::vector<int>& v = cls[c];
+        // longest heads first: the dispatcher hands out workgroups in order
+        std::stable_sort(v.begin(), v.end(), [&](int a, int b) { return n[a] > n[b]; });
+        for (size_t i0 = 0; i0 < v.size(); i0 += kSelectBatch) {
+            const int cnt = (int)std::min<size_t>(kSelectBatch, v.size() - i0);
+            if ((int64_t)cnt * n_heads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+            SelectBatch b{};
+            for (int j = 0; j < cnt; ++j) {
+                const int s = v[i0 + j];
+                b.seq[j] = SelectSeq{scores[s], kept[s], n[s], 0};
+            }
+            const dim3 grid((unsigned)(cnt * n_heads)), block(kBlock);
+            if (c == 0) hipLaunchKernelGGL(select_batch_kernel<8>, grid, block, 0, stream, b, n_heads, budget);
+            else if (c == 1) hipLaunchKernelGGL(select_batch_kernel<16>, grid, block, 0, stream, b, n_heads, budget);
+            else hipLaunchKernelGGL(select_batch_kernel<32>, grid, block, 0, stream, b, n_heads, budget);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
 
 // Workspace of one sequence: per-head records, two banks of per-head
 // histograms, the layer states of three passes.

@@ -301,7 +301,9 @@ tri_status tri_score_ws(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs
     if (st != TRI_OK) return st;
     if (!supported(ctx->head_dim, dtype)) return TRI_E_UNSUPPORTED;
     const int64_t total = tri_scores_count(ctx, seqs, n_seq);
-    if (total > 0 && (!scores || ((uintptr_t)scores & 3u))) return TRI_E_INVAL;
+    // GQA contexts may pass no score array: the workspace then holds the raw
+    // scores and their statistics for tri_select_topb_ws
+    if (total > 0 && ((!scores && ctx->group == 1) || ((uintptr_t)scores & 3u))) return TRI_E_INVAL;
     const int64_t need = tri_score_workspace_bytes(ctx, seqs, n_seq);
     if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
         return TRI_E_INVAL;
@@ -321,7 +323,7 @@ tri_status tri_score_ws(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs
             } else {
                 e = tri::launch_gqa_score(dtype, ctx->head_dim, ctx->group, q.k, q.cap, q.len,
                                           ctx->n_heads, q.p_now, ctx->omega, ctx->qa, ctx->w, ws,
-                                          scores + off, q.head_len, hs);
+                                          scores ? scores + off : nullptr, q.head_len, hs);
                 ws += tri::gqa_workspace_bytes(ctx->n_heads, q.len, ctx->group);
             }
             if (e != hipSuccess) return hip_fail(e);
@@ -352,15 +354,77 @@ tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_se
     st = check_device(ctx);
     if (st != TRI_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (n_seq == 1) {
+        hipError_t e = tri::launch_select(scores, seqs[0].len, ctx->n_heads, budget, kept, budget,
+                                          nullptr, hs);
+        return e == hipSuccess ? TRI_OK : hip_fail(e);
+    }
+    // several sequences: one table of the firing ones, as few launches as
+    // their length classes allow
+    std::vector<const float*> sc;
+    std::vector<int32_t*> kp;
+    std::vector<int> n;
     int64_t off = 0;
     for (int32_t s = 0; s < n_seq; ++s) {
         const tri_seq& q = seqs[s];
         if (fires(q, budget, window)) {
-            hipError_t e = tri::launch_select(scores + off, q.len, ctx->n_heads, budget,
-                                              kept + (int64_t)s * ctx->n_heads * budget, budget,
-                                              nullptr, hs);
+            sc.push_back(scores + off);
+            kp.push_back(kept + (int64_t)s * ctx->n_heads * budget);
+            n.push_back(q.len);
+        }
+        off += (int64_t)ctx->n_heads * q.len;
+    }
+    hipError_t e = tri::launch_select_batch((int)n.size(), sc.data(), kp.data(), n.data(),
+                                            ctx->n_heads, budget, hs);
+    return e == hipSuccess ? TRI_OK : hip_fail(e);
+}
+
+tri_status tri_select_topb_ws(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq,
+                              float* scores, const void* workspace, int64_t workspace_bytes,
+                              int32_t budget, int32_t window, int32_t* kept, void* stream)
+{
+    tri_status st = check_seqs(ctx, seqs, n_seq, false);
+    if (st != TRI_OK) return st;
+    if (ctx->group == 1 || budget < 1 || window < 0 || any_ragged(seqs, n_seq)) return TRI_E_INVAL;
+    bool any = false, long_heads = false;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        if (!fires(seqs[s], budget, window)) continue;
+        any = true;
+        long_heads = long_heads || seqs[s].len > 32768;
+    }
+    if (!any) return TRI_OK;
+    const int64_t need = tri_score_workspace_bytes(ctx, seqs, n_seq);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return TRI_E_INVAL;
+    if (!kept || ((uintptr_t)kept & 3u)) return TRI_E_INVAL;
+    if ((long_heads && !scores) || ((uintptr_t)scores & 3u)) return TRI_E_INVAL;
+    st = check_device(ctx);
+    if (st != TRI_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    // the workspace is sliced per sequence exactly as tri_score_ws slices it
+    unsigned char* ws = static_cast<unsigned char*>(const_cast<void*>(workspace));
+    int64_t off = 0;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        const tri_seq& q = seqs[s];
+        if (q.len > 0 && fires(q, budget, window)) {
+            float* raw = nullptr;
+            double2* stats = nullptr;
+            tri::gqa_workspace_views(ws, ctx->n_heads, q.len, ctx->group, &raw, &stats);
+            int32_t* kp = kept + (int64_t)s * ctx->n_heads * budget;
+            hipError_t e;
+            if (q.len <= 32768) {
+                e = tri::launch_select_gqa(ctx->group, raw, stats, q.len, ctx->n_heads, budget, kp,
+                                           budget, hs);
+            } else {
+                // longer heads: the normalized scores first, then the plain selection
+                e = tri::launch_gqa_normalize(ctx->group, raw, stats, q.len, ctx->n_heads,
+                                              scores + off, hs);
+                if (e == hipSuccess)
+                    e = tri::launch_select(scores + off, q.len, ctx->n_heads, budget, kp, budget,
+                                           nullptr, hs);
+            }
             if (e != hipSuccess) return hip_fail(e);
         }
+        if (q.len > 0) ws += tri::gqa_workspace_bytes(ctx->n_heads, q.len, ctx->group);
         off += (int64_t)ctx->n_heads * q.len;
     }
     return TRI_OK;
@@ -381,15 +445,35 @@ tri_status tri_compact_kv(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, in
     if (st != TRI_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int row_bytes = ctx->head_dim * elem_size(dtype);
-    for (int32_t s = 0; s < n_seq; ++s) {
-        tri_seq& q = seqs[s];
-        if (!fires(q, budget, window)) continue;
+    if (n_seq == 1) {
+        tri_seq& q = seqs[0];
         hipError_t e = tri::launch_compact(row_bytes, q.k, q.v, q.pos, q.cap, q.len, ctx->n_heads,
-                                           kept + (int64_t)s * ctx->n_heads * budget, budget,
-                                           budget, nullptr, nullptr, nullptr, hs);
+                                           kept, budget, budget, nullptr, nullptr, nullptr, hs);
         if (e != hipSuccess) return hip_fail(e);
         q.len = budget;
+        return TRI_OK;
     }
+    // several sequences: the firing ones in one table
+    std::vector<void*> k, v;
+    std::vector<int32_t*> pos;
+    std::vector<int> cap, len;
+    std::vector<const int32_t*> kp;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        const tri_seq& q = seqs[s];
+        if (!fires(q, budget, window)) continue;
+        k.push_back(q.k);
+        v.push_back(q.v);
+        pos.push_back(q.pos);
+        cap.push_back(q.cap);
+        len.push_back(q.len);
+        kp.push_back(kept + (int64_t)s * ctx->n_heads * budget);
+    }
+    hipError_t e = tri::launch_compact_batch(row_bytes, (int)k.size(), k.data(), v.data(),
+                                             pos.data(), cap.data(), len.data(), kp.data(),
+                                             ctx->n_heads, budget, hs);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int32_t s = 0; s < n_seq; ++s)
+        if (fires(seqs[s], budget, window)) seqs[s].len = budget;
     return TRI_OK;
 }
 
@@ -443,10 +527,14 @@ int64_t tri_compact_kv_counts_workspace_bytes(const tri_ctx* ctx)
     return tri::compact_queue_bytes(ctx->n_heads);
 }
 
-tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
-                                 int32_t n_seq, const int32_t* kept, int32_t kept_stride,
-                                 const int32_t* kept_count, void* workspace,
-                                 int64_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the counted compaction (everything but the workspace).
+tri_status check_compact_counts(const tri_ctx* ctx, tri_dtype dtype, const tri_seq* seqs,
+                                int32_t n_seq, const int32_t* kept, int32_t kept_stride,
+                                const int32_t* kept_count)
 {
     tri_status st = check_seqs(ctx, seqs, n_seq, true);
     if (st != TRI_OK) return st;
@@ -457,10 +545,15 @@ tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* s
         if (!seqs[s].head_len) return TRI_E_INVAL;
     if (!kept || !kept_count || ((uintptr_t)kept & 3u) || ((uintptr_t)kept_count & 3u))
         return TRI_E_INVAL;
-    if (!workspace || ((uintptr_t)workspace & 3u) ||
-        workspace_bytes < tri::compact_queue_bytes(ctx->n_heads))
-        return TRI_E_INVAL;
-    st = check_device(ctx);
+    return TRI_OK;
+}
+
+// The counted compaction's launches, with the queue at `queue`.
+tri_status compact_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs, int32_t n_seq,
+                          const int32_t* kept, int32_t kept_stride, const int32_t* kept_count,
+                          void* queue, void* stream)
+{
+    tri_status st = check_device(ctx);
     if (st != TRI_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int row_bytes = ctx->head_dim * elem_size(dtype);
@@ -471,10 +564,27 @@ tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* s
         hipError_t e = tri::launch_compact(row_bytes, q.k, q.v, q.pos, q.cap, q.len, ctx->n_heads,
                                            kept + s * heads * kept_stride, 0, kept_stride,
                                            kept_count + s * heads, q.head_len,
-                                           static_cast<uint32_t*>(workspace), hs);
+                                           static_cast<uint32_t*>(queue), hs);
         if (e != hipSuccess) return hip_fail(e);
     }
     return TRI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
+                                 int32_t n_seq, const int32_t* kept, int32_t kept_stride,
+                                 const int32_t* kept_count, void* workspace,
+                                 int64_t workspace_bytes, void* stream)
+{
+    tri_status st = check_compact_counts(ctx, dtype, seqs, n_seq, kept, kept_stride, kept_count);
+    if (st != TRI_OK || n_seq == 0) return st;
+    if (!workspace || ((uintptr_t)workspace & 3u) ||
+        workspace_bytes < tri::compact_queue_bytes(ctx->n_heads))
+        return TRI_E_INVAL;
+    return compact_counts(ctx, dtype, seqs, n_seq, kept, kept_stride, kept_count, workspace, stream);
 }
 
 }  // extern "C"

@@ -58,6 +58,19 @@ hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void
                             int len, int n_heads, int64_t p_now, const double* omega,
                             const double2* qa, const float* w, void* workspace, float* scores,
                             const int32_t* head_len, hipStream_t stream);
+// The raw scores [n_heads][len][group] and statistics [n_heads][group] in a
+// GQA workspace laid out by launch_gqa_score (scores == nullptr there stops
+// after the statistics); launch_gqa_normalize writes the normalized scores
+// of such a workspace.
+void gqa_workspace_views(void* workspace, int64_t n_heads, int64_t len, int group, float** raw,
+                         double2** stats);
+hipError_t launch_gqa_normalize(int group, const float* raw, const double2* stats, int len,
+                                int n_heads, float* scores, hipStream_t stream);
+// Top-`budget` of heads of len <= 32768 keys, keyed by the normalized GQA
+// score formed from a workspace's raw scores and statistics.
+hipError_t launch_select_gqa(int group, const float* raw, const double2* stats, int len,
+                             int n_heads, int budget, int32_t* kept, int kept_stride,
+                             hipStream_t stream);
 
 // Top-`budget` of each of n_heads score rows of length n.
 // Heads of `n` keys (stride n; with head_len, head h has its own length up
@@ -65,6 +78,12 @@ hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void
 // start at kept + h * kept_stride.
 hipError_t launch_select(const float* scores, int n, int n_heads, int budget, int32_t* kept,
                          int kept_stride, const int32_t* head_len, hipStream_t stream);
+
+// Top-`budget` of the n_heads heads of each of n_seq sequences (host
+// arrays: scores[s], kept[s] and n[s] keys per head; sequences with
+// n[s] <= budget are skipped), in as few launches as the length classes allow.
+hipError_t launch_select_batch(int n_seq, const float* const* scores, int32_t* const* kept,
+                               const int* n, int n_heads, int budget, hipStream_t stream);
 
 // Head-specific budgets over one sequence's n_layers x n_kv heads.
 int64_t shared_workspace_bytes(int64_t n_seq, int64_t n_layers, int64_t n_kv);
@@ -82,5 +101,13 @@ hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t
                           int n_heads, const int32_t* kept, int budget, int kept_stride,
                           const int32_t* counts, int32_t* head_len, uint32_t* queue,
                           hipStream_t stream);
+
+// Uniform-budget compaction of n_seq sequences in as few launches as the
+// kernel-argument table allows (host arrays, one entry per firing sequence;
+// kept[s] holds that sequence's [n_heads][budget] lists).
+hipError_t launch_compact_batch(int row_bytes, int n_seq, void* const* k, void* const* v,
+                                int32_t* const* pos, const int* cap, const int* len,
+                                const int32_t* const* kept, int n_heads, int budget,
+                                hipStream_t stream);
 
 }  // namespace tri

@@ -480,7 +480,11 @@ def make_scores(kind: str, n_heads: int, n: int, seed: int = 0) -> np.ndarray:
     ``ulp`` (clusters of values one fp32 ulp apart), ``wide`` (positive
     values spread over the exponents from 2e-9 to 3e38, with +inf mixed in: the
     order-preserving keys span more than a quarter of the uint32 range, all in
-    its top half).
+    its top half), ``runs_high`` (normal, except 32 evenly spaced runs of 128
+    consecutive slots, run c starting at slot c * (n - 128) / 31, which hold
+    the largest values: high scores clustered in runs), ``cluster`` (40% of
+    the keys within 1000 ulps of 3.0, the rest normal: the budget's threshold
+    falls inside a dense cluster of distinct values).
     """
     rng = _np_rng(seed, "scores", kind, n_heads, n)
     if kind == "normal":
@@ -522,6 +526,16 @@ def make_scores(kind: str, n_heads: int, n: int, seed: int = 0) -> np.ndarray:
     elif kind == "wide":
         s = np.exp(rng.uniform(-20.0, 88.0, size=(n_heads, n))).astype(np.float32)
         s[rng.random((n_heads, n)) < 0.01] = np.inf
+    elif kind == "runs_high":
+        s = rng.standard_normal((n_heads, n)).astype(np.float32)
+        for c in range(32):
+            a = c * (n - 128) // 31
+            s[:, a:a + 128] = (10.0 + rng.standard_normal((n_heads, 128))).astype(np.float32)
+    elif kind == "cluster":
+        s = rng.standard_normal((n_heads, n)).astype(np.float32)
+        m = rng.random((n_heads, n)) < 0.4
+        steps = rng.integers(0, 1000, size=int(m.sum())).astype(np.int32)
+        s[m] = (np.full(int(m.sum()), 3.0, dtype=np.float32).view(np.int32) + steps).view(np.float32)
     else:
         raise KeyError(kind)
     return np.ascontiguousarray(s, dtype=np.float32)

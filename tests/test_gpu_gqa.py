@@ -205,3 +205,123 @@ def test_gqa_fused_pass(orc, name, sample):
     for (l, h), (K, _, P) in inputs.items():
         s_ref, tol = oracle_gqa(orc, cache, 0, l, h, K, P)
         check_kept(orc, s_ref, tol, P, kg[l, h], B, W, "%s l%d h%d" % (name, l, h))
+
+
+# ------------------------------------------- selection without the score array
+
+@pytest.mark.parametrize("name,over", [
+    ("gqa_toy", None), ("gqa_small", None), ("gqa_g7", None), ("gqa_g8_d64", None),
+    ("gqa_small", {"dtype": "f32", "name": "gqa_small_f32"}),
+    # two sequences of different lengths (the workspace sliced per sequence),
+    # one that does not fire, and a length that ends inside a row group
+    ("gqa_small", {"lengths": (4001, 300, 2600), "name": "gqa_small_three"}),
+])
+def test_gqa_select_from_the_workspace_equals_the_two_step_path(name, over):
+    """tri_select_topb_ws (keys formed from the raw scores and statistics)
+    keeps exactly the slots tri_select_topb keeps on the scores tri_score_ws
+    writes: the same fp64 operations, rounded once."""
+    spec = synth.workload(name)
+    if over:
+        spec = spec.replace(**over)
+    B, W = min(spec.budget, 1000), 64
+    say("gqa select from the workspace", spec.name, spec.lengths)
+    cache = synth.make_cache(spec, "cuda", seed=21)
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    total = sum(spec.heads * n for n in cache.lens)
+    scores = torch.empty(total, device="cuda")
+    kept_a = torch.full((spec.n_seq * spec.heads * B,), -5, dtype=torch.int32, device="cuda")
+    kept_b = torch.full_like(kept_a, -5)
+    tri.tri_score(ctx, seqs, scores, workspace=ws)
+    tri.tri_select_topb(ctx, seqs, scores, B, W, kept_a)
+    tri.tri_score(ctx, seqs, None, workspace=ws)
+    tri.tri_select_topb_ws(ctx, seqs, ws, B, W, kept_b)
+    torch.cuda.synchronize()
+    assert torch.equal(kept_a, kept_b)
+    fired = [tri.fires(q, B, W) for q in seqs]
+    assert any(fired)
+    say("  kept lists identical on %d sequences (%d fire)" % (len(seqs), sum(fired)))
+
+
+def test_gqa_select_from_the_workspace_long_heads():
+    """Heads longer than 32768 keys: the normalized scores go to the score
+    array first (required then), and the kept lists still equal the two-step
+    path's."""
+    spec = synth.workload("gqa_toy").replace(name="gqa_long", lengths=(40000,))
+    B, W = 3000, 128
+    cache = synth.make_cache(spec, "cuda", seed=22)
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    n = cache.lens[0]
+    scores = torch.empty(spec.heads * n, device="cuda")
+    scores_b = torch.empty_like(scores)
+    kept_a = torch.empty(spec.heads * B, dtype=torch.int32, device="cuda")
+    kept_b = torch.empty_like(kept_a)
+    tri.tri_score(ctx, seqs, scores, workspace=ws)
+    tri.tri_select_topb(ctx, seqs, scores, B, W, kept_a)
+    tri.tri_score(ctx, seqs, None, workspace=ws)
+    with pytest.raises(tri.TriError) as e:
+        tri.tri_select_topb_ws(ctx, seqs, ws, B, W, kept_b)      # no score array
+    assert e.value.status == tri.TRI_E_INVAL
+    tri.tri_select_topb_ws(ctx, seqs, ws, B, W, kept_b, scores=scores_b)
+    torch.cuda.synchronize()
+    assert torch.equal(kept_a, kept_b)
+    assert torch.equal(bits(scores), bits(scores_b))
+
+
+def test_gqa_select_from_the_workspace_rejects_bad_arguments():
+    spec = synth.workload("gqa_toy")
+    cache = synth.make_cache(spec, "cuda", seed=23)
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    kept = torch.empty(spec.heads * 100, dtype=torch.int32, device="cuda")
+    small = ws[:ws.numel() - 512]
+    with pytest.raises(tri.TriError) as e:
+        tri.tri_select_topb_ws(ctx, seqs, small, 100, 0, kept)
+    assert e.value.status == tri.TRI_E_INVAL
+    single = synth.workload("toy")
+    c1 = synth.make_cache(single, "cuda", seed=24)
+    ctx1 = tri.tri_calibrate_load(single.n_layers, single.n_kv_heads, single.head_dim, c1.calib.qc_re,
+                                  c1.calib.qc_im, c1.calib.q_mean_norm, c1.calib.q_mrl, c1.calib.offsets,
+                                  rope_theta=c1.calib.rope_theta, device=0)
+    with pytest.raises(tri.TriError) as e:          # one query table per KV head: no GQA workspace
+        tri.tri_select_topb_ws(ctx1, seqs_for(c1), ws, 100, 0, kept)
+    assert e.value.status == tri.TRI_E_INVAL
+
+
+@pytest.mark.parametrize("name,sample", [("gqa_small", None), ("qwen3_32k_gqa", [(0, 0), (17, 3), (35, 7)])])
+def test_gqa_prune_step_without_scores(orc, name, sample):
+    """The GQA prune step the benchmark times (score into the workspace,
+    select from it, compact): kept sets against the oracle, the top-B of the
+    GPU's own aggregated scores (taken by tri_score_ws on a copy), bit-exact
+    compaction."""
+    spec = synth.workload(name)
+    B, W = spec.budget, spec.window
+    say("gqa prune step without scores", name)
+    cache = synth.make_cache(spec, "cuda", seed=6)
+    n = cache.lens[0]
+    pairs = sample or [(l, h) for l in range(spec.n_layers) for h in range(spec.n_kv_heads)]
+    inputs = {(l, h): head_inputs(cache, 0, l, h) for l, h in pairs}
+    k_in, v_in, p_in = cache.k[0].clone(), cache.v[0].clone(), cache.pos[0].clone()
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    scores = torch.empty(spec.heads * n, device="cuda")
+    tri.tri_score(ctx, seqs, scores, workspace=ws)     # the GPU's own scores, for the property
+    kept = torch.empty(spec.heads * B, dtype=torch.int32, device="cuda")
+    tri.prune_step_gqa(ctx, seqs, B, W, kept, ws)
+    torch.cuda.synchronize()
+    assert seqs[0].len == B
+    check_topb_property(scores.view(spec.heads, n), kept.view(spec.heads, B), n)
+    kl = kept.view(spec.n_layers, spec.n_kv_heads, B).long()
+    for t_in, t_out in ((k_in, cache.k[0]), (v_in, cache.v[0])):
+        g = torch.gather(t_in, 2, kl[..., None].expand(-1, -1, -1, spec.head_dim))
+        assert torch.equal(bits(g), bits(t_out[:, :, :B]))
+    assert torch.equal(torch.gather(p_in, 2, kl), cache.pos[0][:, :, :B])
+    kg = kept.view(spec.n_layers, spec.n_kv_heads, B).cpu().numpy()
+    for (l, h), (K, _, P) in inputs.items():
+        s_ref, tol = oracle_gqa(orc, cache, 0, l, h, K, P)
+        check_kept(orc, s_ref, tol, P, kg[l, h], B, W, "%s l%d h%d" % (name, l, h))

@@ -103,15 +103,23 @@ def bits(t):
     return t.view({2: torch.int16, 4: torch.int32}[t.element_size()])
 
 
-def check_scores(s_gpu, s_ref, M, what):
-    err = np.abs(s_gpu.astype(np.float64) - s_ref) / M
-    say("  %s: max |ds|/M = %.3g over %d keys" % (what, err.max(), len(err)))
-    assert np.all(np.isfinite(s_gpu))
-    assert err.max() <= TOL
-    return err.max()
+def check_scores(s_gpu, s_ref, M, what, quiet=False):
+    """Scores within TOL * M; NaN exactly where the oracle has NaN (keys with
+    a non-finite element), and no other non-finite value."""
+    nan_ref = np.isnan(s_ref)
+    assert np.array_equal(np.isnan(s_gpu), nan_ref), what + ": NaN pattern differs from the oracle"
+    assert np.all(np.isfinite(s_gpu[~nan_ref]))
+    ok = ~nan_ref
+    err = np.abs(s_gpu[ok].astype(np.float64) - s_ref[ok]) / M[ok] if ok.any() else np.zeros(1)
+    worst = float(err.max()) if len(err) else 0.0
+    if not quiet:
+        say("  %s: max |ds|/M = %.3g over %d keys (%d NaN)" % (what, worst, int(ok.sum()),
+                                                               int(nan_ref.sum())))
+    assert worst <= TOL
+    return worst
 
 
-def check_kept_vs_oracle(orc, s_ref, M, P, kept_gpu, B, window, what):
+def check_kept_vs_oracle(orc, s_ref, M, P, kept_gpu, B, window, what, quiet=False):
     n = len(s_ref)
     kept_ref = orc.select_head(s_ref, P, B, window)
     order = np.lexsort((P, -s_ref))
@@ -128,7 +136,8 @@ def check_kept_vs_oracle(orc, s_ref, M, P, kept_gpu, B, window, what):
     dis = np.nonzero(ref != sel)[0]
     if len(dis):
         assert np.all(np.abs(s_ref[dis] - t) <= TIGHT * (M[dis] + Mt)), what
-    say("  %s: kept-set disagreements with the oracle: %d of %d" % (what, len(dis), B))
+    if not quiet:
+        say("  %s: kept-set disagreements with the oracle: %d of %d" % (what, len(dis), B))
     return kept_ref, len(dis)
 
 
@@ -137,6 +146,13 @@ def check_topb_property(scores_hn, kept_hb, n):
     scores to the lower slot, strictly ascending slots in [0, n)."""
     H, B = kept_hb.shape
     kept_l = kept_hb.long()
+    nan = torch.isnan(scores_hn)
+    if bool(nan.any()):
+        # NaN ranks below every number: a kept NaN means every number is kept
+        kept_nan = torch.gather(nan, 1, kept_l).sum(1)
+        assert bool(((kept_nan == 0) | ((~nan).sum(1) <= B)).all()), "a NaN score was kept"
+        # the GPU writes no -inf (non-finite totals become NaN), so -inf can stand for NaN
+        scores_hn = torch.where(nan, torch.tensor(float("-inf"), device=scores_hn.device), scores_hn)
     assert bool((kept_l[:, 1:] > kept_l[:, :-1]).all())
     assert int(kept_l.min()) >= 0 and int(kept_l.max()) < n
     mask = torch.zeros((H, n), dtype=torch.bool, device=scores_hn.device)
@@ -237,6 +253,69 @@ def test_score_special_tables(orc):
     check_scores(sg[1], s_ref, M, "explicit inv_freq")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+def test_nonfinite_keys_score_nan_and_are_evicted(orc, dtype, d):
+    """Keys whose stored row holds +inf, -inf or NaN (one element, or +inf in
+    both halves of a band) score NaN exactly where the oracle does, every
+    other key within the score bar; the fused step then evicts every such
+    key and compacts the rest bit for bit."""
+    n, B, W = 700, 128, 128
+    spec = synth.workload("toy").replace(name="nonfinite", dtype=dtype, head_dim=d, lengths=(n,),
+                                         n_kv_heads=2, budget=B, window=W)
+    say("non-finite keys", dtype, d)
+    cache = synth.make_cache(spec, "cuda", seed=21)
+    K = cache.k[0]
+    rng = np.random.default_rng(21 + d)
+    bad = {}
+    for l in range(spec.n_layers):
+        for h in range(spec.n_kv_heads):
+            slots = rng.choice(n, 40, replace=False)
+            bad[(l, h)] = np.sort(slots)
+            for j, i in enumerate(slots):
+                col = int(rng.integers(0, d))
+                kind = j % 4
+                if kind == 0:
+                    K[l, h, i, col] = float("inf")
+                elif kind == 1:
+                    K[l, h, i, col] = float("-inf")
+                elif kind == 2:
+                    K[l, h, i, col] = float("nan")
+                else:
+                    f = col % (d // 2)
+                    K[l, h, i, f] = float("inf")
+                    K[l, h, i, f + d // 2] = float("inf")
+    ctx = ctx_for(cache)
+    seqs = seqs_for(cache)
+    H = spec.heads
+    ins = {(l, h): head_inputs(cache, 0, l, h) for l in range(spec.n_layers)
+           for h in range(spec.n_kv_heads)}
+    K0 = cache.k[0].clone()
+    V0 = cache.v[0].clone()
+    scores = torch.full((H * n,), 7.0, device="cuda")
+    tri.tri_score(ctx, seqs, scores)
+    torch.cuda.synchronize()
+    sg = scores.cpu().numpy().reshape(spec.n_layers, spec.n_kv_heads, n)
+    refs = {}
+    for (l, h), (Kh, Vh, P) in ins.items():
+        s_ref, M = oracle_scores(orc, cache, 0, l, h, Kh, P)
+        assert np.array_equal(np.nonzero(np.isnan(s_ref))[0], bad[(l, h)])
+        check_scores(sg[l, h], s_ref, M, "%s d%d l%d h%d" % (dtype, d, l, h))
+        refs[(l, h)] = (s_ref, M, P)
+    kept = torch.empty(H * B, dtype=torch.int32, device="cuda")
+    tri.prune_step(ctx, seqs, B, W, torch.empty(H * n, device="cuda"), kept)
+    torch.cuda.synchronize()
+    assert seqs[0].len == B
+    kg = kept.view(spec.n_layers, spec.n_kv_heads, B)
+    for (l, h), (s_ref, M, P) in refs.items():
+        k_np = kg[l, h].cpu().numpy()
+        assert not np.isin(k_np, bad[(l, h)]).any(), "a key with a non-finite element was kept"
+        check_kept_vs_oracle(orc, s_ref, M, P, k_np, B, W, "%s d%d l%d h%d" % (dtype, d, l, h))
+        idx = kg[l, h].long()
+        assert torch.equal(bits(cache.k[0][l, h, :B]), bits(K0[l, h, idx]))
+        assert torch.equal(bits(cache.v[0][l, h, :B]), bits(V0[l, h, idx]))
+        assert torch.equal(cache.pos[0][l, h, :B], kg[l, h])
+
+
 # ------------------------------------------------------------------- select
 
 SELECT_CASES = [
@@ -249,6 +328,14 @@ SELECT_CASES = [
     ("straddle", 131072, 8192), ("outlier", 36000, 1000),
     # positive keys whose live range runs past 2^32 - 1, with padding slots
     ("wide", 5000, 1234), ("wide", 20000, 2048), ("wide", 32768, 4096),
+    # heads past the register-resident sizes (the sampled single-read
+    # selection): its bracket, all keys equal, a sample that misses the
+    # high runs, a threshold inside a dense cluster (too many candidates),
+    # and the largest size it takes and one past it
+    ("normal", 32769, 4096), ("allequal", 131072, 8192), ("ties", 131072, 8192),
+    ("dups", 131072, 8192), ("runs_high", 131072, 8192), ("runs_high", 70001, 4096),
+    ("cluster", 131072, 8192), ("special", 131072, 1), ("wide", 131072, 8192),
+    ("normal", 262144, 16384), ("straddle", 262145, 1000),
 ]
 
 
@@ -315,21 +402,64 @@ def test_compact_bit_exact_on_synthetic_kept_lists(orc, dtype, d, kind):
 
 # -------------------------------------------------------------- fused pass
 
-def _fused(orc, spec, seed, sample, full_compaction_check=True, positions=None, p_now=None):
-    """Runs one prune step on the GPU as the benchmark does and checks it."""
+def row_fingerprints(X, w):
+    """int64 [L][H][cap] fingerprint of every row of X [L][H][cap][d]: the
+    sum over the row of its elements' bit patterns times fixed random weights
+    (equal rows give equal fingerprints; rows that differ in any bit differ
+    unless the weighted differences cancel exactly)."""
+    out = torch.empty(X.shape[:3], dtype=torch.int64, device=X.device)
+    for l in range(X.shape[0]):
+        out[l] = (bits(X[l]).to(torch.int64) * w).sum(-1)
+    return out
+
+
+def _oracle_threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _fused(orc, spec, seed, sample, compaction="pristine", positions=None, p_now=None):
+    """Runs one prune step on the GPU as the benchmark does and checks it.
+
+    sample      heads (s, l, h) compared with the oracle (scores, kept set,
+                compacted rows), or "all" for every head of every sequence;
+                the oracle runs on the host cores, one head per thread
+    compaction  "pristine": a device copy of the cache checks the compacted
+                K, V and positions of every head bit for bit;
+                "fingerprint": per-row fingerprints of K and V taken before
+                the step check every head's compacted rows (for caches with
+                no room for a copy)
+    """
     t0 = time.time()
     say("fused %s: generating %d keys on the GPU" % (spec.name, spec.keys))
     cache = synth.make_cache(spec, "cuda", seed=seed, positions=positions, p_now=p_now)
     torch.cuda.synchronize()
     say("  generated in %.1fs" % (time.time() - t0))
     H, B, W = spec.heads, spec.budget, spec.window
-    ins = {}
+    if sample == "all":
+        sample = [(s, l, h) for s in range(spec.n_seq) for l in range(spec.n_layers)
+                  for h in range(spec.n_kv_heads)]
+    # inputs of the oracle's heads, on the host before the pass
+    by_seq = {}
     for (s, l, h) in sample:
-        ins[(s, l, h)] = head_inputs(cache, s, l, h)
-    pristine = None
-    if full_compaction_check:
+        by_seq.setdefault(s, set()).add((l, h))
+    host_in = {}
+    for s, heads in by_seq.items():
+        if len(heads) == H:
+            host_in[s] = (cache.k[s].cpu(), bits(cache.v[s]).cpu(), cache.pos[s].cpu())
+        else:
+            for (l, h) in heads:
+                host_in[(s, l, h)] = (cache.k[s][l, h].cpu(), bits(cache.v[s][l, h]).cpu(),
+                                      cache.pos[s][l, h].cpu())
+    pristine, fps = None, None
+    if compaction == "pristine":
         pristine = [(cache.k[s].clone(), cache.v[s].clone(), cache.pos[s].clone())
                     for s in range(spec.n_seq)]
+    else:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed + 1)
+        w = torch.randint(1, 1 << 31, (spec.head_dim,), generator=g, device="cuda", dtype=torch.int64)
+        fps = [(row_fingerprints(cache.k[s], w), row_fingerprints(cache.v[s], w), w)
+               for s in range(spec.n_seq)]
     ctx = ctx_for(cache)
     seqs = seqs_for(cache)
     offs, total = score_offsets(cache)
@@ -341,6 +471,7 @@ def _fused(orc, spec, seed, sample, full_compaction_check=True, positions=None, 
     torch.cuda.synchronize()
     say("  prune step done (%.3fs incl. launch)" % (time.time() - t1))
     kept3 = kept.view(spec.n_seq, H, B)
+    heads_compacted = 0
     for s in range(spec.n_seq):
         n = cache.lens[s]
         if not fired[s]:
@@ -349,43 +480,73 @@ def _fused(orc, spec, seed, sample, full_compaction_check=True, positions=None, 
         assert seqs[s].len == B
         sc = scores[offs[s]:offs[s] + H * n].view(H, n)
         check_topb_property(sc, kept3[s], n)
+        idx = kept3[s].long().view(spec.n_layers, spec.n_kv_heads, B)
         if pristine is not None:
             K0, V0, P0 = pristine[s]
-            idx = kept3[s].long().view(spec.n_layers, spec.n_kv_heads, B)
             for X, X0 in ((cache.k[s], K0), (cache.v[s], V0)):
                 g = torch.gather(X0, 2, idx[..., None].expand(-1, -1, -1, X0.shape[-1]))
                 assert torch.equal(bits(X[:, :, :B]), bits(g))
                 del g
-            assert torch.equal(cache.pos[s][:, :, :B], torch.gather(P0, 2, idx.int().long()).int())
-        elif positions is None:
-            # positions were 0..n-1, so compacted positions equal the kept slots
-            assert torch.equal(cache.pos[s][:, :, :B].reshape(H, B), kept3[s])
-    worst = 0.0
-    for (s, l, h), (K, V, P) in ins.items():
+            assert torch.equal(cache.pos[s][:, :, :B], torch.gather(P0, 2, idx).int())
+        else:
+            fk, fv, w = fps[s]
+            for X, f0 in ((cache.k[s], fk), (cache.v[s], fv)):
+                f1 = row_fingerprints(X[:, :, :B], w)
+                assert torch.equal(f1, torch.gather(f0, 2, idx)), "compacted rows differ from the kept rows"
+            if positions is None:
+                # positions were 0..n-1, so compacted positions equal the kept slots
+                assert torch.equal(cache.pos[s][:, :, :B].reshape(H, B), kept3[s])
+        heads_compacted += H
+    say("  compaction checked bit for bit on %d heads (%s)" % (heads_compacted, compaction))
+
+    # oracle checks, one head per host thread
+    sc_host = {s: scores[offs[s]:offs[s] + H * cache.lens[s]].view(H, -1).cpu().numpy()
+               for s in by_seq}
+    kept_host = kept3.cpu().numpy()
+    out_host = {s: (cache.k[s][:, :, :B].cpu(), bits(cache.v[s][:, :, :B]).cpu(),
+                    cache.pos[s][:, :, :B].cpu().numpy()) for s in by_seq if fired[s]}
+
+    def one(key):
+        s, l, h = key
         n = cache.lens[s]
-        hi = l * spec.n_kv_heads + h
+        if s in host_in:
+            Kx, Vx, Px = (x[l, h] for x in host_in[s])
+        else:
+            Kx, Vx, Px = host_in[key]
+        Kb, V, P = Kx[:n], Vx[:n], Px[:n].numpy()
+        K = Kb.float().numpy()
         s_ref, M = oracle_scores(orc, cache, s, l, h, K, P)
-        sg = scores[offs[s] + hi * n: offs[s] + (hi + 1) * n].cpu().numpy()
-        worst = max(worst, check_scores(sg, s_ref, M, "s%d l%d h%d" % (s, l, h)))
+        hi = l * spec.n_kv_heads + h
+        worst = check_scores(sc_host[s][hi], s_ref, M, "s%d l%d h%d" % key, quiet=True)
         if not fired[s]:
-            continue
-        kg = kept3[s, hi].cpu().numpy()
-        kept_ref, ndis = check_kept_vs_oracle(orc, s_ref, M, P, kg, B, W, "s%d l%d h%d" % (s, l, h))
-        Kc = cache.k[s][l, h, :B].cpu()
-        Vc = cache.v[s][l, h, :B].cpu()
-        Pc = cache.pos[s][l, h, :B].cpu().numpy()
-        Kin = torch.from_numpy(K).to(cache.k[s].dtype)      # exact: K came from this dtype
+            return worst, 0
+        kg = kept_host[s, hi]
+        kept_ref, ndis = check_kept_vs_oracle(orc, s_ref, M, P, kg, B, W, "s%d l%d h%d" % key,
+                                              quiet=True)
+        Kc, Vc, Pc = out_host[s]
         kgl = torch.from_numpy(kg).long()
-        np.testing.assert_array_equal(Pc, P[kg])
-        assert torch.equal(bits(Kc), bits(Kin[kgl]))
-        assert torch.equal(bits(Vc), bits(V[kgl]))
+        np.testing.assert_array_equal(Pc[l, h], P[kg])
+        assert torch.equal(bits(Kc[l, h]), bits(Kb)[kgl])
+        assert torch.equal(Vc[l, h], V[kgl])
         if ndis == 0:
-            np.testing.assert_array_equal(Pc, orc.gather_rows(kept_ref, P))
-            np.testing.assert_array_equal(bits(Kc).numpy(), orc.gather_rows(kept_ref, bits(Kin).numpy()))
-            np.testing.assert_array_equal(bits(Vc).numpy(), orc.gather_rows(kept_ref, bits(V).numpy()))
-    say("  %s: worst |ds|/M on sampled heads %.3g; total %.1fs" % (spec.name, worst, time.time() - t0))
-    del cache, pristine, scores, kept
+            np.testing.assert_array_equal(Pc[l, h], orc.gather_rows(kept_ref, P))
+            np.testing.assert_array_equal(bits(Kc[l, h]).numpy(), orc.gather_rows(kept_ref, bits(Kb).numpy()))
+            np.testing.assert_array_equal(Vc[l, h].numpy(), orc.gather_rows(kept_ref, V.numpy()))
+        return worst, ndis
+
+    t2 = time.time()
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=_oracle_threads()) as ex:
+        res = list(ex.map(one, sample))
+    worst = max(r[0] for r in res)
+    ndis = sum(r[1] for r in res)
+    say("  %s: oracle checked %d heads (%d keys) on %d threads in %.1fs: worst |ds|/M %.3g, "
+        "kept-set disagreements %d; total %.1fs"
+        % (spec.name, len(sample), sum(cache.lens[s] for s, _, _ in sample), _oracle_threads(),
+           time.time() - t2, worst, ndis, time.time() - t0))
+    del cache, pristine, fps, scores, kept, host_in, out_host
     torch.cuda.empty_cache()
+    return len(sample)
 
 
 def test_fused_toy_all_heads(orc):
@@ -402,32 +563,58 @@ def test_fused_toy_pruned_positions(orc):
 
 
 def test_fused_llama8b_full(orc):
+    """Every one of the 256 heads against the oracle."""
     spec = synth.workload("llama8b")
-    _fused(orc, spec, 0, [(0, 0, 0), (0, 5, 3), (0, 17, 7), (0, 31, 2)])
+    assert _fused(orc, spec, 0, "all") == spec.heads
 
 
 def test_fused_qwen3_32k_full(orc):
+    """Every one of the 288 heads against the oracle."""
     spec = synth.workload("qwen3_32k")
-    _fused(orc, spec, 0, [(0, 0, 0), (0, 11, 4), (0, 35, 7)])
+    assert _fused(orc, spec, 0, "all") == spec.heads
 
 
 def test_fused_wide_near_ties_full(orc):
+    """One head of every layer (64 of 512) against the oracle; every head's
+    compaction bit for bit."""
     spec = synth.workload("wide")
-    _fused(orc, spec, 0, [(0, 0, 0), (0, 63, 7)])
+    sample = [(0, l, (5 * l) % spec.n_kv_heads) for l in range(spec.n_layers)]
+    assert _fused(orc, spec, 0, sample) == spec.n_layers
 
 
 def test_fused_batched_full(orc):
+    """64 ragged sequences: the compaction of all 16,384 heads checked by row
+    fingerprints, the top-B property on every head, sampled heads against
+    the oracle."""
     spec = synth.workload("batched")
     lens = spec.lengths
     s_max = int(np.argmax(lens))
     s_min = int(np.argmin(lens))
-    _fused(orc, spec, 0, [(s_min, 0, 0), (s_max, 31, 7), (7, 13, 2)], full_compaction_check=False)
+    sample = [(s_min, 0, 0), (s_max, 31, 7), (7, 13, 2)] + [(s, s % spec.n_layers, s % spec.n_kv_heads)
+                                                            for s in range(0, spec.n_seq, 8)]
+    _fused(orc, spec, 0, sample, compaction="fingerprint")
 
 
 def test_fused_mixed_firing_batch(orc):
     """Ragged batch where some sequences do not fire (len <= B + window)."""
     spec = synth.workload("llama8b").replace(name="mixed", n_layers=2, lengths=(2176, 2177, 5000, 100, 9000))
     _fused(orc, spec, 9, [(1, 0, 0), (2, 1, 7), (4, 0, 3), (0, 1, 1)])
+
+
+def test_fused_many_sequences_every_length_class(orc):
+    """70 sequences in one call: more than one launch's table of sequences
+    for the batched selection (64) and compaction (32), every register-
+    resident length class (up to 8192, 16384 and 32768 keys), heads longer
+    than 32768 keys (selected one sequence at a time), and sequences at the
+    firing boundary that do not fire."""
+    B, W = 300, 128
+    edge = [B + W, B + W + 1, 8192, 8193, 16384, 16385, 32768, 32769, 40000]
+    rng = np.random.default_rng(31)
+    lens = edge + [int(x) for x in rng.integers(B + W - 50, 33000, size=70 - len(edge))]
+    spec = synth.workload("llama8b").replace(name="many", n_layers=1, n_kv_heads=2,
+                                             lengths=tuple(lens), budget=B, window=W)
+    sample = [(s, 0, s % 2) for s in range(0, len(lens), 3)]
+    assert _fused(orc, spec, 13, sample) == len(sample)
 
 
 def test_exact_duplicate_rows_keep_the_lower_slot(orc):

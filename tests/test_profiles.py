@@ -1,7 +1,7 @@
 """The committed rocprofv3 summaries stay tied to the code they measure.
 
 The byte counters behind ``roofline.traffic`` (profiles/
-score_kernel_qwen3_32k_traffic.json) carry the hash of the score kernel's
+score_kernel_<workload>_traffic.json) carry the hash of the score kernel's
 sources they were taken on; bench.py reports them only while the hash
 matches.  A change to those sources must come with new counter runs, so the
 hash is checked here, on the CPU.  The kernel summaries must name every
@@ -18,14 +18,20 @@ import bench  # noqa: E402
 
 
 def test_traffic_counters_match_the_score_kernel_source():
-    with open(bench.TRAFFIC_FILE) as f:
+    with open(bench.traffic_file("qwen3_32k")) as f:
         t = json.load(f)
     assert t["kernel_hash"] == bench.kernel_hash(), \
-        "score kernel sources changed since the byte counters were taken: re-run the two --pmc runs"
+        "score kernel sources changed since the byte counters were taken: re-run the --pmc runs"
     assert t["workload"] == "qwen3_32k"
-    # K read once, scores written once: within 2% of the algorithmic bytes
-    alg = 9437184 * 260
-    assert abs(t["traffic_bytes_per_launch"] / alg - 1.0) < 0.02
+    # the request counters, turned into bytes by request size, read the plain
+    # 1 GiB copy as 1 GiB read and 1 GiB written
+    c = t["copy_requests"]
+    assert abs(c["read_scale"] - 1.0) < 1e-3 and abs(c["write_scale"] - 1.0) < 1e-3
+    # K read once (2,415,919,104 bytes), scores written once (37,748,736)
+    k = t["kernels"]["score_kernel"]["requests"]
+    assert abs(k["read_bytes_scaled"] / 2415919104 - 1.0) < 0.02
+    assert abs(k["write_bytes_scaled"] / 37748736 - 1.0) < 0.02
+    assert t["traffic_bytes_per_launch"] == k["read_bytes_scaled"] + k["write_bytes_scaled"]
 
 
 def test_kernel_summaries_name_the_step_kernels():
