@@ -56,7 +56,8 @@ typedef enum {
     TRI_E_INVAL = 1,        /* NULL pointer, size out of range, misaligned pointer, wrong device */
     TRI_E_UNSUPPORTED = 2,  /* head_dim / dtype combination not built (head_dim 64 or 128; f32 or bf16) */
     TRI_E_HIP = 3,          /* a HIP runtime call or launch failed; see tri_last_hip_error() */
-    TRI_E_NOMEM = 4         /* device or host allocation for the context failed */
+    TRI_E_NOMEM = 4,        /* device or host allocation for the context failed */
+    TRI_E_SCRATCH = 5       /* an allocation-free call needs more than the library's static scratch */
 } tri_status;
 
 typedef enum { TRI_F32 = 0, TRI_BF16 = 1 } tri_dtype;
@@ -381,6 +382,25 @@ tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* s
                                  int32_t n_seq, const int32_t* kept, int32_t kept_stride,
                                  const int32_t* kept_count, void* workspace,
                                  int64_t workspace_bytes, void* stream);
+
+/*
+ * tri_compact_kv_counts without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the queue of column parts lives in a
+ * static device array of the library, one copy per GPU, held from the first
+ * context loaded on that GPU until the process ends.  Arguments, effects and
+ * results are those of tri_compact_kv_counts.  The array holds the queue of
+ * at most 65,536 (layer, KV head) streams per context (n_layers *
+ * n_kv_heads <= 65536, 2 MiB); larger contexts get TRI_E_SCRATCH before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array (each
+ * call's first kernel re-initialises it), so calls that overlap in time on
+ * one GPU, from any stream or thread, race and must not be issued.  Makes no
+ * HIP allocation of any kind.
+ * Errors: TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_SCRATCH, TRI_E_HIP.
+ */
+tri_status tri_compact_kv_counts_noalloc(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
+                                         int32_t n_seq, const int32_t* kept, int32_t kept_stride,
+                                         const int32_t* kept_count, void* stream);
 
 /* Device workspace bytes tri_compact_kv_counts needs (it orders the column
  * parts of the heads' K and V rows there, longest first):

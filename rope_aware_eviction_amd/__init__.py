@@ -27,7 +27,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libtri.so")
 
-TRI_OK, TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP, TRI_E_NOMEM = 0, 1, 2, 3, 4
+TRI_OK, TRI_E_INVAL, TRI_E_UNSUPPORTED, TRI_E_HIP, TRI_E_NOMEM, TRI_E_SCRATCH = 0, 1, 2, 3, 4, 5
 TRI_F32, TRI_BF16 = 0, 1
 
 EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last_hip_error",
@@ -35,7 +35,8 @@ EXPORTED = ("tri_calibrate_load", "tri_ctx_destroy", "tri_status_str", "tri_last
             "tri_select_topb", "tri_select_topb_ws", "tri_compact_kv", "tri_calibrate_stats",
             "tri_distance_curve",
             "tri_offset_set", "tri_select_shared_workspace_bytes", "tri_select_shared",
-            "tri_compact_kv_counts", "tri_compact_kv_counts_workspace_bytes")
+            "tri_compact_kv_counts", "tri_compact_kv_counts_workspace_bytes",
+            "tri_compact_kv_counts_noalloc")
 
 
 class TriError(RuntimeError):
@@ -121,6 +122,9 @@ def library() -> ctypes.CDLL:
         lib.tri_compact_kv_counts.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq),
                                               ctypes.c_int32, vp, ctypes.c_int32, vp, vp,
                                               ctypes.c_int64, vp]
+        lib.tri_compact_kv_counts_noalloc.restype = ctypes.c_int
+        lib.tri_compact_kv_counts_noalloc.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Seq),
+                                                      ctypes.c_int32, vp, ctypes.c_int32, vp, vp]
         lib.tri_compact_kv_counts_workspace_bytes.restype = ctypes.c_int64
         lib.tri_compact_kv_counts_workspace_bytes.argtypes = [vp]
         _lib = lib
@@ -496,6 +500,23 @@ def tri_compact_kv_counts(ctx: Context, seqs: Sequence[Seq], kept: torch.Tensor,
                                            int(kept_stride), kept_count.data_ptr(),
                                            workspace.data_ptr(), nbytes, _stream_ptr(stream)),
            "tri_compact_kv_counts")
+
+
+def tri_compact_kv_counts_noalloc(ctx: Context, seqs: Sequence[Seq], kept: torch.Tensor,
+                                  kept_stride: int, kept_count: torch.Tensor, stream=None):
+    """tri_compact_kv_counts with the library's static scratch instead of a
+    caller workspace (no device allocation; calls on one GPU must not overlap)."""
+    arr, dtype = _seq_array(ctx, seqs, need_kv=True)
+    if kept.dtype != torch.int32 or not kept.is_cuda or not kept.is_contiguous() \
+            or kept.numel() < len(seqs) * ctx.n_heads * kept_stride:
+        raise ValueError("kept must be a contiguous int32 GPU tensor of n_seq*n_heads*kept_stride")
+    if kept_count.dtype != torch.int32 or not kept_count.is_cuda \
+            or not kept_count.is_contiguous() or kept_count.numel() < len(seqs) * ctx.n_heads:
+        raise ValueError("kept_count must be a contiguous int32 GPU tensor of n_seq*n_heads")
+    _check(library().tri_compact_kv_counts_noalloc(ctx.handle, dtype, arr, len(seqs), kept.data_ptr(),
+                                                   int(kept_stride), kept_count.data_ptr(),
+                                                   _stream_ptr(stream)),
+           "tri_compact_kv_counts_noalloc")
 
 
 def prune_step_shared(ctx: Context, seqs: List[Seq], budget: int, floor: int, window: int,

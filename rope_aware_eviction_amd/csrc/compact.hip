@@ -35,8 +35,17 @@
 // take parts from that order through an atomic counter: the longest parts
 // start first and the short ones fill in.
 #include <algorithm>
+#include <mutex>
 
 #include "tri_internal.h"
+
+// Scratch memory of the allocation-free counted compaction
+// (tri_compact_kv_counts_noalloc): the queue of column parts of up to
+// tri::kScratchHeads (layer, KV head) streams.  One copy per GPU, alive until
+// the process ends.  Host code never uses this name as an address: the
+// device address of each GPU's copy comes from hipGetSymbolAddress
+// (tri::scratch_address).
+static __device__ __align__(256) uint32_t scratch[2 + 2 * 4 * tri::kScratchHeads];
 
 namespace tri {
 namespace {
@@ -368,6 +377,29 @@ hipError_t launch_compact_batch(int row_bytes, int n_seq, void* const* k, void* 
 
 // counter, item count and one entry per column part (at most 512 / 128 per stream)
 int64_t compact_queue_bytes(int64_t n_heads) { return 8 + 4 * 2 * 4 * n_heads; }
+
+static_assert(sizeof(scratch) == 8 + 4 * 2 * 4 * kScratchHeads, "scratch holds the queue of kScratchHeads");
+
+int64_t scratch_bytes() { return (int64_t)sizeof(scratch); }
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (the first call with that device current) and kept.
+hipError_t scratch_address(int device, void** out)
+{
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    *out = nullptr;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[device] = p;
+    }
+    *out = addr[device];
+    return hipSuccess;
+}
 
 hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
                           int n_heads, const int32_t* kept, int budget, int kept_stride,

@@ -80,6 +80,7 @@ const char* tri_status_str(tri_status s)
     case TRI_E_UNSUPPORTED: return "unsupported head_dim or dtype";
     case TRI_E_HIP: return "HIP runtime error";
     case TRI_E_NOMEM: return "out of memory";
+    case TRI_E_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }
@@ -190,6 +191,10 @@ tri_status tri_calibrate_load(const tri_calib_desc* d, int device, tri_ctx** out
             qc[2 * i + 1] = d->qc_im[i];
         }
         put(ctx->qc, qc.data(), sizeof(double2) * nb);
+    }
+    if (st == TRI_OK) {   // this device's static scratch (allocation-free calls), once per device
+        e = tri::scratch_address(device, &ctx->scratch);
+        if (e != hipSuccess) st = hip_fail(e);
     }
     if (st == TRI_OK) {
         e = tri::launch_calibrate(n_heads * group, d->head_dim, d->rope_theta, r_inv, r_off, d->n_offsets,
@@ -585,6 +590,18 @@ tri_status tri_compact_kv_counts(const tri_ctx* ctx, tri_dtype dtype, tri_seq* s
         workspace_bytes < tri::compact_queue_bytes(ctx->n_heads))
         return TRI_E_INVAL;
     return compact_counts(ctx, dtype, seqs, n_seq, kept, kept_stride, kept_count, workspace, stream);
+}
+
+tri_status tri_compact_kv_counts_noalloc(const tri_ctx* ctx, tri_dtype dtype, tri_seq* seqs,
+                                         int32_t n_seq, const int32_t* kept, int32_t kept_stride,
+                                         const int32_t* kept_count, void* stream)
+{
+    tri_status st = check_compact_counts(ctx, dtype, seqs, n_seq, kept, kept_stride, kept_count);
+    if (st != TRI_OK || n_seq == 0) return st;
+    if (tri::compact_queue_bytes(ctx->n_heads) > tri::scratch_bytes() || !ctx->scratch)
+        return TRI_E_SCRATCH;
+    return compact_counts(ctx, dtype, seqs, n_seq, kept, kept_stride, kept_count, ctx->scratch,
+                          stream);
 }
 
 }  // extern "C"

@@ -17,6 +17,7 @@ struct tri_ctx {
     double2* qa;          // device [n_heads][group][head_dim/2] E[q_f] * A_f (complex, fp64)
     float* w;             // device [n_heads][group][head_dim/2] (1 - R_f) * E|q_f|
     double2* qc;          // device [n_heads][group][head_dim/2] E[q_f] as loaded (complex, fp64)
+    void* scratch;        // device address of this device's static scratch (allocation-free calls)
 };
 
 namespace tri {
@@ -97,6 +98,15 @@ hipError_t launch_select_shared(const float* scores, int stride, int n_layers, i
 // (-1: untouched) and head_len[h] takes that count.
 // queue: device scratch of compact_queue_bytes(n_heads), needed with counts.
 int64_t compact_queue_bytes(int64_t n_heads);
+
+// The allocation-free counted compaction keeps its queue in a static device
+// array of scratch_bytes() (= compact_queue_bytes(kScratchHeads)), one copy
+// per GPU; scratch_address gives the copy of `device` (which must be the
+// current device on the first call for it).
+constexpr int64_t kScratchHeads = 65536;
+constexpr int kMaxDevices = 64;
+int64_t scratch_bytes();
+hipError_t scratch_address(int device, void** out);
 hipError_t launch_compact(int row_bytes, void* k, void* v, int32_t* pos, int64_t cap, int len,
                           int n_heads, const int32_t* kept, int budget, int kept_stride,
                           const int32_t* counts, int32_t* head_len, uint32_t* queue,
