@@ -849,7 +849,7 @@ __global__ __launch_bounds__(kBlock) void select_batch_kernel(const SelectBatch 
 //    vary periodically with the position, as the distance preference makes
 //    them, are not sampled at one phase).  With r the number of sample keys
 //    expected among the head's top B (B * kSample / n, rounded up) and
-//    delta = max(32, 6 sqrt(r)), two levels of 4096-bin histograms of the
+//    delta = max(32, 10 sqrt(r)), two levels of 4096-bin histograms of the
 //    sample find the bins of its (r - delta)-th and (r + delta)-th largest
 //    keys: hi is the top of the first, lo the bottom of the second.  The
 //    bracket [lo, hi] holds the head's B-th largest key unless the sample
@@ -875,10 +875,11 @@ __global__ __launch_bounds__(kBlock) void select_batch_kernel(const SelectBatch 
 // histogram, and the candidate list (cmax keys, then cmax slots, in kWaves
 // equal segments).
 constexpr int kWideMax = 1 << 18;
-constexpr int kSampleRuns = 128;
+constexpr int kSampleRuns = 512;
 constexpr int kSampleRun = 32;
 constexpr int kSample = kSampleRuns * kSampleRun;
-static_assert(kSample == 4 * kBlock, "four sample keys per thread");
+constexpr int kSamplePerThread = kSample / kBlock;
+static_assert(kSample == kSamplePerThread * kBlock, "whole sample keys per thread");
 constexpr int kWideBins = 1 << kRegDigitBits;
 constexpr int kWideLdsBytes = 155648;          // dynamic LDS of the wide selection
 constexpr int kPassBatch = 16;                 // score loads per thread in flight in the pass
@@ -914,24 +915,29 @@ __global__ __launch_bounds__(kBlock) void select_wide_kernel(const float* __rest
     // ---- 1. the bracket from the sample
     uint32_t lo, hi;
     {
-        // run c of kSampleRun keys at a hashed offset inside the c-th
-        // 1/kSampleRuns of the head; thread t reads keys t % 8, +8, +16, +24
-        // of run t / 8
-        const int run = tid / (kSampleRun / 4);
-        const int j = tid % (kSampleRun / 4);
+        // sample key q = tid + kBlock * u is key q % kSampleRun of run
+        // q / kSampleRun, which starts at a hashed offset inside the run's
+        // 1/kSampleRuns of the head (a wave reads two whole runs per load)
         const int stride = n / kSampleRuns;
-        uint32_t hsh = (uint32_t)run * 0x9E3779B1u + 0x7F4A7C15u;
-        hsh ^= hsh >> 15;
-        hsh *= 0x2C1B3C6Du;
-        hsh ^= hsh >> 12;
-        const int start = run * stride + (int)(hsh % (uint32_t)(stride - kSampleRun + 1));
-        uint32_t sk[4];
+        uint32_t sk[kSamplePerThread];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kSamplePerThread; ++u) {
+            const int q = tid + kBlock * u;
+            const int run = q / kSampleRun;
+            uint32_t hsh = (uint32_t)run * 0x9E3779B1u + 0x7F4A7C15u;
+            hsh ^= hsh >> 15;
+            hsh *= 0x2C1B3C6Du;
+            hsh ^= hsh >> 12;
+            const int start = run * stride + (int)(hsh % (uint32_t)(stride - kSampleRun + 1));
             sk[u] = ordered_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                rsrc, (start + j + u * (kSampleRun / 4)) * 4, 0, 0)));
-        uint32_t smn = min(min(sk[0], sk[1]), min(sk[2], sk[3]));
-        uint32_t smx = max(max(sk[0], sk[1]), max(sk[2], sk[3]));
+                rsrc, (start + q % kSampleRun) * 4, 0, 0)));
+        }
+        uint32_t smn = 0xFFFFFFFFu, smx = 0u;
+#pragma unroll
+        for (int u = 0; u < kSamplePerThread; ++u) {
+            smn = min(smn, sk[u]);
+            smx = max(smx, sk[u]);
+        }
         smn = wave_min(smn);
         smx = wave_max(smx);
         if (lane == 0) {
@@ -948,7 +954,7 @@ __global__ __launch_bounds__(kBlock) void select_wide_kernel(const float* __rest
         // sample ranks (from the top) of the bracket's ends, then two levels
         // of histograms narrow [base, top] down to the bins that hold them
         const int64_t r = ((int64_t)budget * kSample + n - 1) / n;
-        const int64_t delta = max((int64_t)32, (int64_t)ceil(6.0 * sqrt((double)r)));
+        const int64_t delta = max((int64_t)32, (int64_t)ceil(10.0 * sqrt((double)r)));
         uint32_t r_hi = (uint32_t)max((int64_t)1, r - delta);
         uint32_t r_lo = (uint32_t)min((int64_t)kSample, r + delta);
         uint32_t base = smn, top = smx;
@@ -961,7 +967,7 @@ __global__ __launch_bounds__(kBlock) void select_wide_kernel(const float* __rest
             for (uint32_t b = tid; b < nbins; b += kBlock) hist[b] = 0u;
             __syncthreads();
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < kSamplePerThread; ++u)
                 if (sk[u] >= base && sk[u] <= top) atomicAdd(&hist[(sk[u] - base) >> sh], 1u);
             __syncthreads();
             find_digit<kBlock>(hist, nbins, r_hi, tid, lane, wave, s_run, &s_digit, &s_above, &s_inbin);
