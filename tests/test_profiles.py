@@ -15,6 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+import synth  # noqa: E402
 
 
 def test_traffic_counters_match_the_score_kernel_source():
@@ -34,13 +35,38 @@ def test_traffic_counters_match_the_score_kernel_source():
     assert t["traffic_bytes_per_launch"] == k["read_bytes_scaled"] + k["write_bytes_scaled"]
 
 
+def test_every_workload_has_fresh_counters():
+    # each single-GPU workload whose score kernel was counted carries the
+    # same source hash, and its score kernel reads each K row about once
+    for w in ("qwen3_32k", "llama8b", "wide", "batched"):
+        with open(bench.traffic_file(w)) as f:
+            t = json.load(f)
+        assert t["workload"] == w
+        assert t["kernel_hash"] == bench.kernel_hash(), w
+        k = t["kernels"]["score_kernel"]["requests"]
+        _, k_read, _ = bench.workload_bytes(synth.workload(w))
+        assert 0.99 < k["read_bytes_scaled"] / k_read < 1.03, w
+
+
+STEP_KERNELS = {
+    "qwen3_32k": ("score_kernel<128, true>", "select_reg_kernel<32, 1024, false>",
+                  "compact_kernel<256, 1>"),
+    "llama8b": ("score_kernel<128, true>", "select_reg_kernel<", "compact_kernel<256, 1>"),
+    "wide": ("score_kernel<128, true>", "select_wide_kernel", "compact_kernel<256, 1>"),
+    "batched": ("score_kernel<128, true>", "select_batch_kernel<32>", "select_batch_kernel<16>",
+                "select_batch_kernel<8>", "compact_batch_kernel<256>"),
+    "qwen3_32k_gqa": ("gqa_mfma_kernel<128, 4>", "gqa_stats_kernel", "select_gqa_kernel<32, 4>",
+                      "compact_kernel<256, 1>"),
+    "shared_floor1024": ("select_reg_kernel<32, 1024, true>", "shared_pass_kernel",
+                         "shared_write_kernel<32>", "order_kernel", "compact_kernel<256, 2>"),
+}
+
+
 def test_kernel_summaries_name_the_step_kernels():
-    with open(os.path.join(ROOT, "profiles", "prune_step_qwen3_32k_kernel_stats.md")) as f:
-        text = f.read()
-    for k in ("score_kernel<128, true>", "select_reg_kernel<32, 1024, false>", "compact_kernel<256, 1>"):
-        assert k in text, k
-    with open(os.path.join(ROOT, "profiles", "shared_prune_step_qwen3_32k_kernel_stats.md")) as f:
-        text = f.read()
-    for k in ("select_reg_kernel<32, 1024, true>", "shared_pass_kernel", "shared_write_kernel<32>",
-              "order_kernel", "compact_kernel<256, 2>"):
-        assert k in text, k
+    for w, kernels in STEP_KERNELS.items():
+        path = os.path.join(ROOT, "profiles", "prune_step_%s_kernel_stats.md" % w)
+        with open(path) as f:
+            text = f.read()
+        assert "rocprofv3 --kernel-trace --stats" in text, w
+        for k in kernels:
+            assert k in text, (w, k)
