@@ -617,6 +617,23 @@ def test_fused_many_sequences_every_length_class(orc):
     assert _fused(orc, spec, 13, sample) == len(sample)
 
 
+def test_degenerate_calls(orc):
+    """No sequences at all; a batch with empty sequences, a one-key sequence,
+    one exactly at the firing boundary (len = budget + window, does not fire)
+    and one just past it (fires) beside a long one."""
+    spec = synth.workload("toy")
+    cache = synth.make_cache(spec, "cuda", seed=0)
+    ctx = ctx_for(cache)
+    empty_f = torch.empty(0, device="cuda")
+    empty_i = torch.empty(0, dtype=torch.int32, device="cuda")
+    tri.prune_step(ctx, [], spec.budget, spec.window, empty_f, empty_i)
+    torch.cuda.synchronize()
+    B, W = spec.budget, spec.window
+    spec2 = spec.replace(name="degenerate", lengths=(0, 1, 700, 0, B + W, B + W + 1))
+    sample = [(2, 0, 0), (2, 0, 1), (5, 0, 1), (1, 0, 0), (4, 0, 0)]
+    assert _fused(orc, spec2, 17, sample) == len(sample)
+
+
 def test_exact_duplicate_rows_keep_the_lower_slot(orc):
     """Bit-identical stored rows score bit-identically on the GPU.  With every
     row stored twice (slots i and i + 2000) and an odd budget 2m - 1, the top
