@@ -12,10 +12,9 @@ flush buffer leaves up to 256 MB of dirty lines whose write-back then lands
 inside the timed step (measured: ~12 us per step), while a read evicts the
 restore's dirty lines before the first event.  Times come from HIP events
 recorded on the stream the kernels run on: the timed steps carry one event
-before the first launch and one after the last; the per-phase breakdown comes
-from up to ten further steps with events between the launches, and the score
-kernel's duration for the roofline from as many score phases run back to back
-between two events.
+before the first launch and one after the last; the per-phase breakdown (and
+the score kernel's duration for the roofline) comes from up to ten further
+steps with events between the launches.
 
 Prints one JSON line.  Extra modes:
   --pmc-steps N      a plain 1 GiB device copy, then N steps with no restores
@@ -179,7 +178,7 @@ def cpu_baseline_shared(cache, n_layers_sample: int, floor: int):
     dt = time.perf_counter() - t0
     keys = n_layers_sample * sp.n_kv_heads * n
     return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": min(threads, sp.n_kv_heads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of %d layers x %d KV heads x %d keys (score, shared select, gather), "
                       "%.1f s wall" % (n_layers_sample, sp.n_layers, sp.n_kv_heads, n, dt)}
 
@@ -564,22 +563,13 @@ def main():
     t_select = [e[1].elapsed_time(e[2]) for e in pev]
     t_compact = [e[2].elapsed_time(e[3]) for e in pev]
 
-    # The score kernel's duration for the roofline: n_phase score phases back
-    # to back between two events, after a restore and a flush.  Each event
-    # interval above also holds one dispatch gap (~5 us); here it is spread
-    # over n_phase launches, as in the profiler's per-dispatch durations.  The
-    # score phase only reads K and rewrites the same scores, so repeating it
-    # leaves every input as it was, and K (2.4 GB and up) is far larger than
-    # the 256 MB last-level cache, so no launch finds the previous one's rows.
-    restore()
-    s = seqs()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for _ in range(n_phase):
-        score(s)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    t_score_run = r0.elapsed_time(r1) / n_phase
+    # The score kernel's duration for the roofline is the score interval of
+    # these steps: it holds one dispatch gap (~5 us) that the profiler's
+    # per-dispatch durations do not.  Timing score phases back to back instead
+    # hides the gap but not the write-back of the previous phase's scores
+    # (151 MB with four query heads per KV head), so each phase here starts
+    # after a restore and a flush, as in a step.
+    t_score_run = sum(t_score) / len(t_score)
 
     mean = lambda x: sum(x) / len(x)
     ms = mean(t_step)
@@ -621,11 +611,14 @@ def main():
                      "alg_bytes_per_launch": bytes_k,
                      # not algorithmic: fp32 scores written (and GQA raw scores written and read)
                      "intermediate_bytes_per_launch": bytes_score_io,
-                     # score phases per step and the duration of one, from
-                     # n_phase phases back to back between two events
+                     # score-kernel launches per step (one per sequence) and
+                     # the score phase's event-timed duration
                      "launches": spec.n_seq, "launch_ms": t_score_run,
                      "timed_phases": n_phase},
         "pass": {"alg_bytes": bytes_pass, "achieved_gbs": pass_gbs, "frac": pass_gbs / HBM_PEAK_GBS,
+                 # with the scores written by the score phase and read back by
+                 # the selection (not algorithmic: an intermediate)
+                 "bytes_with_scores": bytes_pass + 2 * bytes_score_io,
                  "phase_ms": {"score": mean(t_score), "select": mean(t_select),
                               "compact": mean(t_compact)},
                  "step_ms_min": min(t_step), "step_ms_max": max(t_step)},

@@ -223,6 +223,65 @@ def test_score_parity_short_and_ragged_heads(orc, dtype, d, n):
             check_scores(sg[l, h], s_ref, M, "%s d%d n%d l%d h%d" % (dtype, d, n, l, h))
 
 
+SENTINEL = 0x7F80BEEF     # a signalling-NaN pattern the score kernel never writes
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+def test_score_writes_its_range_at_any_alignment(orc, dtype, d):
+    """Tiles follow the 128-byte lines of the score array, so the tiling
+    depends on where the array starts and on the head length.  At start
+    offsets across a line and head lengths around a line and a tile: every
+    score is written, bit-identical to those of a line-aligned array (each
+    key's arithmetic does not depend on its tile), the aligned scores meet
+    the oracle, and nothing outside the array is written.  Several sequences
+    in one call start their score ranges anywhere in a line too."""
+    for n in (1, 31, 33, 129, 300, 513):
+        spec = synth.workload("toy").replace(dtype=dtype, head_dim=d, lengths=(n,), n_kv_heads=3)
+        cache = synth.make_cache(spec, "cuda", seed=n)
+        ctx = ctx_for(cache)
+        seqs = seqs_for(cache)
+        total = spec.heads * n
+        ref = None
+        for off in (0, 1, 5, 16, 31):
+            buf = torch.empty(32 + off + total + 64, dtype=torch.int32, device="cuda").fill_(SENTINEL)
+            assert buf.data_ptr() % 128 == 0
+            out = buf[32 + off:32 + off + total].view(torch.float32)
+            tri.tri_score(ctx, seqs, out)
+            torch.cuda.synchronize()
+            assert bool((buf[:32 + off] == SENTINEL).all()), "written before the array (off %d)" % off
+            assert bool((buf[32 + off + total:] == SENTINEL).all()), "written past the array (off %d)" % off
+            got = buf[32 + off:32 + off + total].clone()
+            assert not bool((got == SENTINEL).any()), "a score was not written (n %d, off %d)" % (n, off)
+            if ref is None:
+                ref = got
+                sg = got.view(torch.float32).cpu().numpy().reshape(spec.n_layers, spec.n_kv_heads, n)
+                for h in range(spec.n_kv_heads):
+                    K, _, P = head_inputs(cache, 0, 0, h)
+                    s_ref, M = oracle_scores(orc, cache, 0, 0, h, K, P)
+                    check_scores(sg[0, h], s_ref, M, "%s d%d n%d h%d" % (dtype, d, n, h), quiet=True)
+            else:
+                assert torch.equal(got, ref), "scores depend on the array's alignment (n %d, off %d)" % (n, off)
+    # several sequences: each one's range starts wherever the previous ended
+    lens = (33, 1, 129, 300, 31)
+    spec = synth.workload("toy").replace(dtype=dtype, head_dim=d, lengths=lens, n_kv_heads=3)
+    cache = synth.make_cache(spec, "cuda", seed=7)
+    ctx = ctx_for(cache)
+    seqs = seqs_for(cache)
+    offs, total = score_offsets(cache)
+    for off in (0, 7):
+        buf = torch.empty(32 + off + total + 64, dtype=torch.int32, device="cuda").fill_(SENTINEL)
+        tri.tri_score(ctx, seqs, buf[32 + off:32 + off + total].view(torch.float32))
+        torch.cuda.synchronize()
+        assert bool((buf[:32 + off] == SENTINEL).all()) and bool((buf[32 + off + total:] == SENTINEL).all())
+        for s in range(len(lens)):
+            one = torch.empty(spec.heads * lens[s], device="cuda")
+            tri.tri_score(ctx, [seqs[s]], one)
+            torch.cuda.synchronize()
+            part = buf[32 + off + offs[s]:32 + off + offs[s] + spec.heads * lens[s]]
+            assert torch.equal(part, bits(one)), "sequence %d of the batch (off %d)" % (s, off)
+    say("  %s d%d: scores identical at every alignment" % (dtype, d))
+
+
 def test_score_special_tables(orc):
     """q-centre 0 (norm term only), R = 1 (trig term only), explicit
     frequencies, non-identity positions and p_now well past the newest key."""
