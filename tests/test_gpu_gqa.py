@@ -133,6 +133,35 @@ def test_gqa_scores_match_oracle(orc, name, heads, over):
         check_agg(sg[l, h], s_ref, tol, "%s l%d h%d" % (spec.name, l, h))
 
 
+@pytest.mark.parametrize("name,over", [
+    ("gqa_small", {"lengths": (4001, 301), "name": "gqa_small_two"}),
+    ("gqa_g7", {"lengths": (530,), "name": "gqa_g7_530"}),
+    ("gqa_g8_d64", {"lengths": (530,), "name": "gqa_g8_d64_530"}),
+    ("gqa_small", {"lengths": (777,), "dtype": "f32", "name": "gqa_small_f32_777"})])
+def test_gqa_scores_do_not_depend_on_the_workspace_address(name, over):
+    """A head's score tiles follow from its length alone, so the per-tile
+    statistics are summed in the same groups wherever the workspace lies:
+    scores from a workspace at several 16-byte offsets are bit-identical."""
+    spec = synth.workload(name).replace(**over)
+    say("gqa workspace address", spec.name, "G =", spec.group, spec.lengths)
+    cache = synth.make_cache(spec, "cuda", seed=5)
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    need = tri.score_workspace_bytes(ctx, seqs)
+    big = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    total = sum(spec.heads * n for n in cache.lens)
+    ref = None
+    for off in (0, 16, 80):
+        scores = torch.full((total,), float("nan"), device="cuda")
+        tri.tri_score(ctx, seqs, scores, workspace=big[off:off + need])
+        torch.cuda.synchronize()
+        got = scores.view(torch.int32).clone()
+        if ref is None:
+            ref = got
+        else:
+            assert torch.equal(got, ref), "workspace offset %d" % off
+
+
 def test_gqa_needs_its_workspace():
     spec = synth.workload("gqa_toy")
     cache = synth.make_cache(spec, "cuda", seed=4)
