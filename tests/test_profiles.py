@@ -5,7 +5,7 @@ score_kernel_<workload>_traffic.json) carry the hash of the score kernel's
 sources they were taken on; bench.py reports them only while the hash
 matches.  A change to those sources must come with new counter runs, so the
 hash is checked here, on the CPU.  The kernel summaries must name every
-kernel of the prune step.
+kernel of the prune step, and bench.py refuses to report more than one GPU.
 """
 import json
 import os
@@ -70,3 +70,12 @@ def test_kernel_summaries_name_the_step_kernels():
         assert "rocprofv3 --kernel-trace --stats" in text, w
         for k in kernels:
             assert k in text, (w, k)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stdout + r.stderr
+    assert r.stdout.strip() == "" or not r.stdout.strip().startswith("{")
