@@ -770,3 +770,127 @@ def test_prune_then_append_then_prune(orc):
                                           orc.gather_rows(r2["kept"], Kin_b))
             np.testing.assert_array_equal(bits(V[l, h, :B]).cpu().numpy(), r2["V"])
     say("  two uniform prune cycles agree with the oracle on all %d heads" % (L * H1))
+
+
+def test_prune_steps_on_two_streams_from_two_threads():
+    """The library keeps no per-call state outside its arguments: two host
+    threads, each pruning its own caches on a stream of its own, give bit for
+    bit the results of the same calls made one after the other on one
+    stream (a single sequence and a three-sequence batch, run four times
+    each, interleaved)."""
+    import threading
+    specs = [synth.workload("llama8b").replace(name="thread_a", n_layers=2, lengths=(3001,)),
+             synth.workload("llama8b").replace(name="thread_b", n_layers=2, lengths=(2500, 9000, 2200),
+                                               budget=1000)]
+    caches = [synth.make_cache(sp, "cuda", seed=30 + i) for i, sp in enumerate(specs)]
+    ctxs = [ctx_for(c) for c in caches]
+    pristine = [[(k.clone(), v.clone(), p.clone()) for k, v, p in zip(c.k, c.v, c.pos)] for c in caches]
+
+    def restore(i):
+        for (k0, v0, p0), k, v, p in zip(pristine[i], caches[i].k, caches[i].v, caches[i].pos):
+            k.copy_(k0)
+            v.copy_(v0)
+            p.copy_(p0)
+
+    def step(i, stream):
+        sp, c = specs[i], caches[i]
+        seqs = seqs_for(c)
+        _, total = score_offsets(c)
+        scores = torch.empty(total, device="cuda")
+        kept = torch.full((sp.n_seq * sp.heads * sp.budget,), -1, dtype=torch.int32, device="cuda")
+        tri.prune_step(ctxs[i], seqs, sp.budget, sp.window, scores, kept, stream)
+        return kept, [s.len for s in seqs]
+
+    def snapshot(i, kept, lens):
+        return (kept.clone(), lens, [(k.clone(), v.clone(), p.clone())
+                                     for k, v, p in zip(caches[i].k, caches[i].v, caches[i].pos)])
+
+    # one after the other on the current stream
+    ref = []
+    for i in range(2):
+        restore(i)
+        kept, lens = step(i, None)
+        torch.cuda.synchronize()
+        ref.append(snapshot(i, kept, lens))
+    # two threads, two streams (default priority), several rounds each
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    out = [None, None]
+    errors = []
+
+    def worker(i):
+        try:
+            torch.cuda.set_device(0)
+            with torch.cuda.stream(streams[i]):
+                for _ in range(4):
+                    restore(i)
+                    kept, lens = step(i, streams[i])
+                streams[i].synchronize()
+                out[i] = snapshot(i, kept, lens)
+                streams[i].synchronize()
+        except Exception as e:   # surfaced in the main thread
+            errors.append(e)
+
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(2):
+        kept_r, lens_r, rows_r = ref[i]
+        kept_o, lens_o, rows_o = out[i]
+        assert lens_o == lens_r
+        assert torch.equal(kept_o, kept_r), specs[i].name
+        for (k0, v0, p0), (k1, v1, p1) in zip(rows_r, rows_o):
+            assert torch.equal(bits(k0), bits(k1)) and torch.equal(bits(v0), bits(v1))
+            assert torch.equal(p0, p1)
+    say("  two threads on two streams: identical to the serial calls")
+
+
+@pytest.mark.parametrize("lengths", [(3001,), (2500, 9000, 2200)])
+def test_prune_step_replays_from_a_hip_graph(lengths):
+    """A step's calls launch kernels only (no allocation, copy or memset), so
+    a caller can capture them in a HIP graph.  The graph is replayed three
+    times, the cache restored eagerly and synchronized between replays, and
+    every replay equals the eager step bit for bit."""
+    sp = synth.workload("llama8b").replace(name="graph", n_layers=2, lengths=lengths, budget=1000)
+    cache = synth.make_cache(sp, "cuda", seed=40)
+    ctx = ctx_for(cache)
+    pristine = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
+
+    def restore():
+        for (k0, v0, p0), k, v, p in zip(pristine, cache.k, cache.v, cache.pos):
+            k.copy_(k0)
+            v.copy_(v0)
+            p.copy_(p0)
+
+    _, total = score_offsets(cache)
+    scores = torch.empty(total, device="cuda")
+    kept = torch.full((sp.n_seq * sp.heads * sp.budget,), -1, dtype=torch.int32, device="cuda")
+    restore()
+    tri.prune_step(ctx, seqs_for(cache), sp.budget, sp.window, scores, kept)
+    torch.cuda.synchronize()
+    ref_kept = kept.clone()
+    ref_rows = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
+
+    restore()
+    kept.fill_(-1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tri.prune_step(ctx, seqs_for(cache), sp.budget, sp.window, scores, kept)
+    torch.cuda.synchronize()
+    for r in range(3):
+        restore()
+        kept.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(kept, ref_kept), "replay %d: kept lists" % r
+        for (k0, v0, p0), k, v, p in zip(ref_rows, cache.k, cache.v, cache.pos):
+            assert torch.equal(bits(k), bits(k0)) and torch.equal(bits(v), bits(v0)), "replay %d" % r
+            assert torch.equal(p, p0), "replay %d: positions" % r
+    say("  %d sequence(s): three graph replays equal the eager step" % sp.n_seq)
