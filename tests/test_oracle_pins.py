@@ -62,6 +62,57 @@ def test_omega_matches_standard_rope(oracle_lib):
         assert oracle_lib.omega(d, th)[0] == 1.0
 
 
+def _library_rope(d, theta):
+    """The rotary embedding of a widely used model library (the Llama
+    rotary embedding of `transformers`): its band frequencies and a function
+    that rotates rows [n, d] to the given positions.  The library computes
+    the angles in fp32."""
+    pytest.importorskip("transformers")
+    import torch
+    from transformers import LlamaConfig
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding, apply_rotary_pos_emb
+
+    cfg = LlamaConfig(hidden_size=2 * d, num_attention_heads=2, num_key_value_heads=2, head_dim=d,
+                      rope_theta=theta)
+    emb = LlamaRotaryEmbedding(cfg)
+
+    def rotate(x, positions):
+        t = torch.from_numpy(np.asarray(x, dtype=np.float64))[None, None]
+        cos, sin = emb(t, torch.as_tensor(np.asarray(positions), dtype=torch.long)[None])
+        out, _ = apply_rotary_pos_emb(t, t, cos, sin)
+        return out[0, 0].numpy()
+
+    return emb.inv_freq.double().numpy(), rotate
+
+
+@pytest.mark.parametrize("d,theta", [(64, 1e4), (128, 5e5), (128, 1e6)])
+def test_omega_and_bands_match_a_model_library(oracle_lib, d, theta):
+    """Readings A1 (w_f = theta^(-2f/d)) and A2 (band f = dims f and f + d/2,
+    turned by +w_f * p) against the RoPE of a model library instead of a
+    restatement: the oracle's frequencies equal the library's (to its fp32),
+    and the oracle's trig term of keys the library rotated to their
+    positions equals the mean over the offsets of the dot products with the
+    query centre the library rotated to p_now + delta."""
+    lib_om, rotate = _library_rope(d, theta)
+    om = oracle_lib.omega(d, theta)
+    np.testing.assert_allclose(om, lib_om, rtol=2e-7, atol=0)
+    rng = np.random.default_rng(d)
+    n = 40
+    k = rng.standard_normal((n, d))
+    pos = np.sort(rng.choice(150, size=n, replace=False)).astype(np.int64)
+    K = rotate(k, pos)                              # stored post-RoPE keys
+    qc_re, qc_im = rng.standard_normal(d // 2), rng.standard_normal(d // 2)
+    q = np.concatenate([qc_re, qc_im])
+    offsets = np.array([1, 2, 4, 8], dtype=np.int64)
+    p_now = int(pos[-1]) + 3
+    ones = np.ones(d // 2)
+    trig, _, _ = oracle_lib.score_head(K, pos, p_now, om, offsets, qc_re, qc_im,
+                                       np.hypot(qc_re, qc_im), ones)
+    lib = np.mean([K @ rotate(q[None], [p_now + int(t)])[0] for t in offsets], axis=0)
+    scale = np.abs(q).sum() * np.abs(k).sum(axis=1)
+    assert np.all(np.abs(trig - lib) <= 1e-6 * scale), np.max(np.abs(trig - lib) / scale)
+
+
 @pytest.mark.parametrize("d", [2, 8, 64, 128])
 def test_unrotate_inverts_a_dense_rotation(oracle_lib, d):
     rng = np.random.default_rng(d)

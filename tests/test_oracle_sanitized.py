@@ -30,7 +30,9 @@ def test_oracle_pins_pass_under_asan_and_ubsan():
     if asan is None:
         pytest.skip("gcc's AddressSanitizer runtime is not installed")
     env = dict(os.environ)
-    env.update(TRI_ORACLE_SANITIZE="1", LD_PRELOAD=asan,
+    # the ASan runtime must come first; anything already preloaded stays
+    pre = os.environ.get("LD_PRELOAD", "").strip()
+    env.update(TRI_ORACLE_SANITIZE="1", LD_PRELOAD=asan + (" " + pre if pre else ""),
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
