@@ -112,9 +112,14 @@ def check_scores(s_gpu, s_ref, M, what, quiet=False):
     ok = ~nan_ref
     err = np.abs(s_gpu[ok].astype(np.float64) - s_ref[ok]) / M[ok] if ok.any() else np.zeros(1)
     worst = float(err.max()) if len(err) else 0.0
+    # the plain relative error where it is well posed: keys whose score is
+    # not a cancellation, |s| >= 0.1 * M (reported; implied <= 10 * TOL)
+    big = ok & (np.abs(s_ref) >= 0.1 * M)
+    rel = float((np.abs(s_gpu[big].astype(np.float64) - s_ref[big]) / np.abs(s_ref[big])).max()) \
+        if big.any() else 0.0
     if not quiet:
-        say("  %s: max |ds|/M = %.3g over %d keys (%d NaN)" % (what, worst, int(ok.sum()),
-                                                               int(nan_ref.sum())))
+        say("  %s: max |ds|/M = %.3g over %d keys (%d NaN); max |ds|/|s| = %.3g over the %d keys "
+            "with |s| >= 0.1 M" % (what, worst, int(ok.sum()), int(nan_ref.sum()), rel, int(big.sum())))
     assert worst <= TOL
     return worst
 
