@@ -621,7 +621,8 @@ def main():
                  "bytes_with_scores": bytes_pass + 2 * bytes_score_io,
                  "phase_ms": {"score": mean(t_score), "select": mean(t_select),
                               "compact": mean(t_compact)},
-                 "step_ms_min": min(t_step), "step_ms_max": max(t_step)},
+                 "step_ms_min": min(t_step), "step_ms_max": max(t_step),
+                 "step_ms_median": sorted(t_step)[len(t_step) // 2]},
         "wall_s_timed_loop_incl_restores": wall,
         "cpu_baseline": None,
     }
