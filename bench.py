@@ -141,9 +141,10 @@ def cpu_baseline(cache, n_heads_sample: int):
     dt1 = time.perf_counter() - t1
     keys1 = cache.lens[picks[0][0]]
     return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model(),
-            "sample": "%d of %d heads, %d keys (full score+select+gather per head), one head per "
-                      "thread, %.1f s wall" % (len(picks), sp.heads * sp.n_seq, keys, dt),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": "%d of %d heads, %d keys (full score+select+gather per head), %d threads "
+                      "taking one head at a time, %.1f s wall"
+                      % (len(picks), sp.heads * sp.n_seq, keys, threads, dt),
             "single_thread": {"value": keys1 / dt1 / 1e9, "unit": "G keys/s", "cores": 1,
                               "sample": "1 head, %d keys, %.2f s" % (keys1, dt1)}}
 
@@ -178,7 +179,7 @@ def cpu_baseline_shared(cache, n_layers_sample: int, floor: int):
     dt = time.perf_counter() - t0
     keys = n_layers_sample * sp.n_kv_heads * n
     return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": min(threads, sp.n_kv_heads),
-            "kind": "oracle", "cpu_model": cpu_model(),
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "%d of %d layers x %d KV heads x %d keys (score, shared select, gather), "
                       "%.1f s wall" % (n_layers_sample, sp.n_layers, sp.n_kv_heads, n, dt)}
 
