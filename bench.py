@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP64_PEAK_TFLOPS = 78.6
 METRIC = "cached keys scored+pruned/sec (G keys/s) and achieved HBM GB/s vs peak"
 SCORE_KERNEL = "score_kernel"
 # the score kernel's source (tri_internal.h holds only declarations shared by
@@ -369,9 +370,14 @@ def bench_distance_curve(args, torch, synth, tri, dev):
         "data": "synthetic",
         "config": {"workload": "qwen3_32k_gqa query heads: 36 x 8 x 4, head_dim 128",
                    "query_heads": spec.heads * spec.group, "deltas": args.distance_curve},
+        # fp64 vector arithmetic: each (entry, band) term is two multiply-adds
+        # (4 flops) against the accumulator; the phasors (one sincos per
+        # distance, band and 64-head tile) are not counted.  Peak: MI355X fp64
+        # vector, 78.6 TFLOP/s (256 CUs x 2.4 GHz x 128 flops per clock).
         "roofline": {"bound": "alu", "kernel": "distance_curve_kernel",
-                     "achieved": terms / (ms * 1e-3) / 1e9, "unit": "G band terms/s",
-                     "peak": None, "frac": None, "traffic": None}}), flush=True)
+                     "achieved": 4 * terms / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                     "peak": FP64_PEAK_TFLOPS, "frac": 4 * terms / (ms * 1e-3) / 1e12 / FP64_PEAK_TFLOPS,
+                     "traffic": None, "band_terms_per_s": terms / (ms * 1e-3)}}), flush=True)
 
 
 def main():

@@ -150,7 +150,9 @@ tri_status tri_calibrate_stats(tri_dtype dtype, const void* q, int64_t n_samples
  *   curve[qh][j] = sum_f Re( E[q_f] * conj(kc_f) * exp(i*w_f*delta_j) ),
  * the RoPE logit of a query at the query head's calibrated centre E[q_f] and
  * a key at its KV head's pre-RoPE key centre kc_f, delta_j positions earlier
- * (delta may be negative).  Computed in fp64, one thread per entry.
+ * (delta may be negative).  Computed in fp64; each entry sums its bands in
+ * order, and the phasors exp(i*w_f*delta_j) are evaluated once per tile of
+ * 64 query heads.
  *   kc_re, kc_im  device fp64 [n_layers*n_kv_heads][head_dim/2] key centres
  *                 (e.g. tri_calibrate_stats of pre-RoPE key samples)
  *   deltas        device int64 [n_delta], |delta| <= 2^40

@@ -47,36 +47,88 @@ __global__ void calibrate_kernel(int n_heads, int head_dim, double rope_theta,
     w[i] = (float)((1.0 - q_mrl[i]) * q_mean_norm[i]);
 }
 
-// One thread per (query head, distance): the distance-preference curve
-// sum_f Re(E[q_f] * conj(kc_f) * exp(i*w_f*delta)) in fp64.
+// Distance-preference curves: curve[qh][j] = sum_f Re(E[q_f] * conj(kc_f) *
+// exp(i*w_f*delta_j)) in fp64.
 // Source: dimensionstp.github.io "TriAttention ... Review", section 2-1
 // item 2 and section 2-2 (Q/K centres turn the RoPE logit into a curve of
 // the query-key distance), section 6 item 2 (per-head curves).
-__global__ void distance_curve_kernel(int n_q_heads, int group, int half,
-                                      const double* __restrict__ omega,
-                                      const double2* __restrict__ qc,
-                                      const double* __restrict__ kc_re,
-                                      const double* __restrict__ kc_im,
-                                      const int64_t* __restrict__ deltas, int n_delta,
-                                      double* __restrict__ curve)
+//
+// The phasor exp(i*w_f*delta_j) does not depend on the query head, so each
+// workgroup takes a tile of kCurveTile distances x kCurveTile query heads:
+// for kBandChunk bands at a time it evaluates the tile's phasors (one sincos
+// per distance and band) and the products E[q_f] * conj(kc_f) of its heads
+// into LDS, and every thread accumulates a 4 x 4 block of entries over the
+// bands in order.  The band chunks keep the LDS of a workgroup at 32 KB, so
+// several workgroups share a compute unit and hide each other's latency.
+constexpr int kCurveTile = 64;
+constexpr int kCurveBlock = 256;
+constexpr int kBandChunk = 16;
+static_assert(kCurveTile * kCurveTile == 16 * kCurveBlock, "a 4 x 4 block of entries per thread");
+
+__global__ __launch_bounds__(kCurveBlock) void distance_curve_kernel(
+    int n_q_heads, int group, int half, const double* __restrict__ omega,
+    const double2* __restrict__ qc, const double* __restrict__ kc_re,
+    const double* __restrict__ kc_im, const int64_t* __restrict__ deltas, int n_delta,
+    double* __restrict__ curve)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)n_q_heads * n_delta) return;
-    const int qh = (int)(i / n_delta);
-    const int j = (int)(i - (int64_t)qh * n_delta);
-    const int kv = qh / group;
-    const double dl = (double)deltas[j];
-    double s = 0.0;
-    for (int f = 0; f < half; ++f) {
-        const double2 q = qc[(size_t)qh * half + f];
-        const double kr = kc_re[(size_t)kv * half + f], ki = kc_im[(size_t)kv * half + f];
-        // q * conj(k) = (q.x*kr + q.y*ki) + i*(q.y*kr - q.x*ki)
-        const double pr = q.x * kr + q.y * ki, pi = q.y * kr - q.x * ki;
-        double sn, cs;
-        sincos(omega[f] * dl, &sn, &cs);
-        s += pr * cs - pi * sn;
+    __shared__ double2 s_ph[kBandChunk][kCurveTile];   // (cos, sin) of w_f * delta_j
+    __shared__ double2 s_qk[kBandChunk][kCurveTile];   // E[q_f] * conj(kc_f) of the tile's heads
+    const int j0 = blockIdx.x * kCurveTile;
+    const int h0 = blockIdx.y * kCurveTile;
+    const int tid = threadIdx.x;
+    const int hb = (tid / 16) * 4;   // the thread's four query heads in the tile
+    const int jb = (tid % 16) * 4;   // and its four distances
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int f0 = 0; f0 < half; f0 += kBandChunk) {
+        if (f0 > 0) __syncthreads();   // the previous chunk has been read
+        for (int i = tid; i < kBandChunk * kCurveTile; i += kCurveBlock) {
+            const int fc = i / kCurveTile, t = i - fc * kCurveTile;
+            const int f = f0 + fc;
+            const int j = j0 + t;
+            double sn = 0.0, cs = 0.0;
+            if (f < half && j < n_delta) sincos(omega[f] * (double)deltas[j], &sn, &cs);
+            s_ph[fc][t] = make_double2(cs, sn);
+            const int qh = h0 + t;
+            double pr = 0.0, pi = 0.0;
+            if (f < half && qh < n_q_heads) {
+                const double2 q = qc[(size_t)qh * half + f];
+                const int kv = qh / group;
+                const double kr = kc_re[(size_t)kv * half + f], ki = kc_im[(size_t)kv * half + f];
+                // q * conj(k) = (q.x*kr + q.y*ki) + i*(q.y*kr - q.x*ki)
+                pr = q.x * kr + q.y * ki;
+                pi = q.y * kr - q.x * ki;
+            }
+            s_qk[fc][t] = make_double2(pr, pi);
+        }
+        __syncthreads();
+        const int nf = min(kBandChunk, half - f0);
+        for (int fc = 0; fc < nf; ++fc) {
+            double2 ph[4], qk[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                ph[x] = s_ph[fc][jb + x];
+                qk[x] = s_qk[fc][hb + x];
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] += qk[a].x * ph[b].x - qk[a].y * ph[b].y;
+        }
     }
-    curve[i] = s;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int qh = h0 + hb + a;
+        if (qh >= n_q_heads) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = j0 + jb + b;
+            if (j < n_delta) curve[(size_t)qh * n_delta + j] = acc[a][b];
+        }
+    }
 }
 
 }  // namespace
@@ -86,13 +138,13 @@ hipError_t launch_distance_curve(int n_q_heads, int group, int head_dim, const d
                                  const int64_t* deltas, int n_delta, double* curve,
                                  hipStream_t stream)
 {
-    const int64_t total = (int64_t)n_q_heads * n_delta;
-    if (total <= 0) return hipSuccess;
-    const int block = 256;
-    const int64_t grid = (total + block - 1) / block;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(distance_curve_kernel, dim3((unsigned)grid), dim3(block), 0, stream,
-                       n_q_heads, group, head_dim / 2, omega, qc, kc_re, kc_im, deltas, n_delta,
+    if (n_q_heads <= 0 || n_delta <= 0) return hipSuccess;
+    const int half = head_dim / 2;
+    const int64_t gx = ((int64_t)n_delta + kCurveTile - 1) / kCurveTile;
+    const int64_t gy = ((int64_t)n_q_heads + kCurveTile - 1) / kCurveTile;
+    if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(distance_curve_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kCurveBlock),
+                       0, stream, n_q_heads, group, half, omega, qc, kc_re, kc_im, deltas, n_delta,
                        curve);
     return hipGetLastError();
 }

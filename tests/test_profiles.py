@@ -62,6 +62,14 @@ STEP_KERNELS = {
 }
 
 
+def test_next_row_summaries_exist():
+    for name, kernel in (("calib_stats_qwen3_kernel_stats.md", "calib_stats_kernel<128, true>"),
+                         ("distance_curve_qwen3_gqa_kernel_stats.md", "distance_curve_kernel")):
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            text = f.read()
+        assert "rocprofv3 --kernel-trace --stats" in text and kernel in text, name
+
+
 def test_kernel_summaries_name_the_step_kernels():
     for w, kernels in STEP_KERNELS.items():
         path = os.path.join(ROOT, "profiles", "prune_step_%s_kernel_stats.md" % w)
