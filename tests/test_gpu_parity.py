@@ -400,6 +400,10 @@ SELECT_CASES = [
     ("dups", 131072, 8192), ("runs_high", 131072, 8192), ("runs_high", 70001, 4096),
     ("cluster", 131072, 8192), ("special", 131072, 1), ("wide", 131072, 8192),
     ("normal", 262144, 16384), ("straddle", 262145, 1000),
+    # budgets near the head length and tiny ones on long heads (the bracket
+    # at the ends of the sample)
+    ("normal", 40000, 39999), ("ties", 100000, 90000), ("normal", 262144, 250000),
+    ("outlier", 200000, 7), ("cluster", 65536, 60000),
 ]
 
 
