@@ -1706,6 +1706,9 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
     } else if (n <= kBlock * 16) {
         hipLaunchKernelGGL((select_reg_kernel<16, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
                            scores, n, budget, kept, kept_stride, head_len);
+    } else if (n <= kBlock * 24) {
+        hipLaunchKernelGGL((select_reg_kernel<24, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
+                           scores, n, budget, kept, kept_stride, head_len);
     } else if (n <= kBlock * 32) {
         hipLaunchKernelGGL((select_reg_kernel<32, kBlock>), dim3(n_heads), dim3(kBlock), 0, stream,
                            scores, n, budget, kept, kept_stride, head_len);
@@ -1776,19 +1779,20 @@ hipError_t launch_select_batch(int n_seq, const float* const* scores, int32_t* c
 {
     if (n_heads <= 0) return hipSuccess;
     // register-resident length classes; longer heads go one sequence at a time
-    std::vector<int> cls[3];
+    std::vector<int> cls[4];
     for (int s = 0; s < n_seq; ++s) {
         if (n[s] <= budget) continue;
         if (n[s] <= kBlock * 8) cls[0].push_back(s);
         else if (n[s] <= kBlock * 16) cls[1].push_back(s);
-        else if (n[s] <= kBlock * 32) cls[2].push_back(s);
+        else if (n[s] <= kBlock * 24) cls[2].push_back(s);
+        else if (n[s] <= kBlock * 32) cls[3].push_back(s);
         else {
             hipError_t e = launch_select(scores[s], n[s], n_heads, budget, kept[s], budget, nullptr,
                                          stream);
             if (e != hipSuccess) return e;
         }
     }
-    for (int c = 2; c >= 0; --c) {
+    for (int c = 3; c >= 0; --c) {
         std::vector<int>& v = cls[c];
         // longest heads first: the dispatcher hands out workgroups in order
         std::stable_sort(v.begin(), v.end(), [&](int a, int b) { return n[a] > n[b]; });
@@ -1803,6 +1807,7 @@ hipError_t launch_select_batch(int n_seq, const float* const* scores, int32_t* c
             const dim3 grid((unsigned)(cnt * n_heads)), block(kBlock);
             if (c == 0) hipLaunchKernelGGL(select_batch_kernel<8>, grid, block, 0, stream, b, n_heads, budget);
             else if (c == 1) hipLaunchKernelGGL(select_batch_kernel<16>, grid, block, 0, stream, b, n_heads, budget);
+            else if (c == 2) hipLaunchKernelGGL(select_batch_kernel<24>, grid, block, 0, stream, b, n_heads, budget);
             else hipLaunchKernelGGL(select_batch_kernel<32>, grid, block, 0, stream, b, n_heads, budget);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
