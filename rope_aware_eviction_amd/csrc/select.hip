@@ -1766,6 +1766,8 @@ hipError_t launch_select_gqa(int group, const float* raw, const double2* stats, 
         TRI_GQA_SEL_G(8)
     } else if (len <= kBlock * 16) {
         TRI_GQA_SEL_G(16)
+    } else if (len <= kBlock * 24) {
+        TRI_GQA_SEL_G(24)
     } else {
         TRI_GQA_SEL_G(32)
     }
