@@ -147,3 +147,18 @@ def test_offset_sets_match_the_oracle(lib, oracle_lib):
     assert lib.tri_offset_set(0, 0, 0, None, 0) == -1
     assert lib.tri_offset_set(1, 10, 0, None, 0) == -1
     assert lib.tri_offset_set(2, 10, 3, None, 0) == -1
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: with libtri.so absent, the first call raises."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "tri_missing", os.path.join(ROOT, "rope_aware_eviction_amd", "__init__.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    m.LIBRARY = str(tmp_path / "libtri.so")
+    with pytest.raises(ImportError):
+        m.library()
+    with pytest.raises(ImportError):
+        m.tri_calibrate_load(1, 2, 64, np.zeros((1, 2, 32)), np.zeros((1, 2, 32)),
+                             np.ones((1, 2, 32)), np.ones((1, 2, 32)), [1], device=0)
