@@ -94,7 +94,8 @@ typedef struct {
     int32_t cap;      /* rows allocated per head, >= len */
     int32_t len;      /* rows in use per head (with head_len: an upper bound on every head's rows,
                          and the per-head stride of the score layout); tri_compact_kv sets it to
-                         budget when it fires */
+                         budget when it fires.  len * head_dim * 4 < 2^31 (at most 4,194,303
+                         keys per head at head_dim 128), else TRI_E_INVAL */
     int64_t p_now;    /* position of the newest cached token; future queries sit at p_now + delta */
     int32_t* head_len;/* NULL: every head holds len rows.  Otherwise device int32
                          [n_layers][n_kv_heads], 4-byte aligned: head (l, h) holds rows

@@ -45,6 +45,8 @@ tri_status check_seqs(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_seq, bo
     for (int32_t s = 0; s < n_seq; ++s) {
         const tri_seq& q = seqs[s];
         if (q.cap < 0 || q.len < 0 || q.len > q.cap) return TRI_E_INVAL;
+        // the kernels address a head's rows with 32-bit byte offsets
+        if ((int64_t)q.len * ctx->head_dim * 4 >= (int64_t(1) << 31)) return TRI_E_INVAL;
         if (q.p_now < -(int64_t(1) << 52) || q.p_now > (int64_t(1) << 52)) return TRI_E_INVAL;
         if ((uintptr_t)q.head_len & 3u) return TRI_E_INVAL;
         if (q.len == 0) continue;

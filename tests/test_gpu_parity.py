@@ -903,3 +903,28 @@ def test_prune_step_replays_from_a_hip_graph(lengths):
             assert torch.equal(bits(k), bits(k0)) and torch.equal(bits(v), bits(v0)), "replay %d" % r
             assert torch.equal(p, p0), "replay %d: positions" % r
     say("  %d sequence(s): three graph replays equal the eager step" % sp.n_seq)
+
+
+def test_rows_per_head_limit():
+    """The kernels address a head's rows with 32-bit byte offsets: len *
+    head_dim * 4 must stay below 2^31.  At the limit every call is an
+    argument error (nothing enqueued); one key below it the score runs."""
+    d = 128
+    lim = (1 << 31) // (4 * d)
+    ctx = tri.tri_calibrate_load(1, 1, d, np.zeros((1, 1, 64)), np.full((1, 1, 64), 0.5),
+                                 np.ones((1, 1, 64)), np.full((1, 1, 64), 0.5), [1, 2], device=0)
+    k = torch.zeros((1, 1, lim, d), dtype=torch.bfloat16, device="cuda")
+    scores = torch.empty(lim, device="cuda")
+    kept = torch.empty(16, dtype=torch.int32, device="cuda")
+    with pytest.raises(tri.TriError) as e:
+        tri.tri_score(ctx, [tri.Seq(k, None, None, lim, lim - 1)], scores)
+    assert e.value.status == tri.TRI_E_INVAL
+    with pytest.raises(tri.TriError) as e:
+        tri.tri_select_topb(ctx, [tri.Seq(k, None, None, lim, lim - 1)], scores, 16, 0, kept)
+    assert e.value.status == tri.TRI_E_INVAL
+    tri.tri_score(ctx, [tri.Seq(k, None, None, lim - 1, lim - 2)], scores)
+    torch.cuda.synchronize()
+    # zero keys score zero: trig and norm both vanish
+    assert float(scores[:lim - 1].abs().max()) == 0.0
+    del k, scores
+    torch.cuda.empty_cache()
