@@ -243,8 +243,8 @@ int64_t tri_score_workspace_bytes(const tri_ctx* ctx, const tri_seq* seqs, int32
  * each query head's scores are z-normalized over the head's cached keys,
  *   z_g = (s_g - mean_g) / sd_g   (mean and population deviation of the finite s_g),
  * and the key's score is the largest z_g.  K is read once.  With GQA
- * contexts `scores` may be NULL: then only the raw scores and their
- * statistics are computed, into the workspace, for tri_select_topb_ws.
+ * contexts `scores` may be NULL: then only the raw scores and their per-tile
+ * partial sums are computed, into the workspace, for tri_select_topb_ws.
  * Readings: a
  * deviation at most 1e-9 of the largest |s_g| counts as zero and gives
  * z_g = 0; a non-finite s_g gives NaN, which loses to every number; mean_g
@@ -283,11 +283,12 @@ tri_status tri_select_topb(const tri_ctx* ctx, const tri_seq* seqs, int32_t n_se
  * tri_select_topb for GQA contexts without the normalized score array: the
  * keys are ranked by the GQA score of tri_score_ws (the largest z-normalized
  * per-query-head score), formed on the fly from the raw per-query-head
- * scores and statistics that a tri_score_ws call on the same sequences, with
- * scores == NULL, left in `workspace`.  The kept lists are those
+ * scores and per-tile partial sums that a tri_score_ws call on the same
+ * sequences, with scores == NULL, left in `workspace` (the statistics are
+ * summed from them in the same fixed order).  The kept lists are those
  * tri_select_topb gives on the scores tri_score_ws would have written (the
  * same fp64 operations, rounded once to fp32).  Saves writing and reading
- * back the normalized scores.
+ * back the normalized scores, and the statistics launch.
  *   scores     NULL, unless a firing sequence holds more than 32768 keys per
  *              head: then device fp32 in the layout of tri_score, where the
  *              normalized scores of those sequences are written first

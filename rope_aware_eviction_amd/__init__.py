@@ -336,8 +336,8 @@ def tri_score(ctx: Context, seqs: Sequence[Seq], scores: torch.Tensor, stream=No
     score_workspace_bytes(ctx, seqs) bytes (tri_score_ws)."""
     arr, dtype = _seq_array(ctx, seqs, need_kv=False)
     if scores is None:
-        # GQA contexts: raw per-query-head scores and statistics only, into
-        # the workspace (for tri_select_topb_ws)
+        # GQA contexts: raw per-query-head scores and their per-tile partial
+        # sums only, into the workspace (for tri_select_topb_ws)
         if workspace is None:
             raise ValueError("scores=None needs the GQA workspace")
     elif scores.dtype != torch.float32 or not scores.is_cuda or not scores.is_contiguous() \
@@ -361,7 +361,7 @@ def tri_select_topb_ws(ctx: Context, seqs: Sequence[Seq], workspace: torch.Tenso
                        window: int, kept: torch.Tensor, stream=None,
                        scores: Optional[torch.Tensor] = None):
     """GQA contexts: top-``budget`` kept slots per head ranked by the GQA score
-    formed on the fly from the raw scores and statistics a
+    formed on the fly from the raw scores and per-tile partial sums a
     tri_score(..., scores=None, workspace=workspace) call left in
     ``workspace``.  ``scores`` (fp32, the layout of tri_score) is needed only
     when a firing sequence has more than 32768 keys per head."""

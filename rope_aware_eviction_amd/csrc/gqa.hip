@@ -22,20 +22,20 @@
 //      over the group, rounded once to fp32 into the caller's score array.
 #include <type_traits>
 
+#include "gqa_stats.h"
 #include "tri_internal.h"
 
 namespace tri {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kTileRows = 512;
+constexpr int kTileRows = kGqaTileRows;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer resource word 3, gfx9 family
 constexpr int kSC1 = 16;                   // cache-policy bits: sc1
 constexpr int kNT = 2;                     // cache-policy bits: non-temporal
 constexpr uint32_t kDrop = 0xFFFFFFC0u;    // buffer offset that is always out of range
 // matrix-core B operands of one head: at most 8 k-blocks x 64 lanes x 16 bytes
 constexpr int64_t kBopBytesPerHead = 8 * 64 * 16;
-constexpr double kFlat = 1e-9;             // deviation at or below kFlat * max|s| counts as zero
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -595,28 +595,10 @@ __global__ __launch_bounds__(64) void gqa_stats_kernel(const double* __restrict_
     const int lane = threadIdx.x;
     const int n_h = head_len ? max(0, min(head_len[head], len)) : len;
     const int tiles = (n_h + kTileRows - 1) / kTileRows;   // tiles the score kernel wrote
+    const double* ph = partial + (size_t)head * tiles_per_head * group * 4;
     for (int g = 0; g < group; ++g) {
-        double s1 = 0.0, s2 = 0.0, cnt = 0.0, big = 0.0;
-        for (int tile = lane; tile < tiles; tile += 64) {
-            const double* p = partial + (((size_t)head * tiles_per_head + tile) * group + g) * 4;
-            s1 += p[0];
-            s2 += p[1];
-            cnt += p[2];
-            big = fmax(big, p[3]);
-        }
-        s1 = wave_sum_d(s1);
-        s2 = wave_sum_d(s2);
-        cnt = wave_sum_d(cnt);
-        big = wave_max_d(big);
-        if (lane == 0) {
-            double mean = 0.0, sd = 0.0;
-            if (cnt > 0.0) {
-                mean = s1 / cnt;
-                sd = sqrt(fmax(s2 / cnt - mean * mean, 0.0));
-                if (sd <= kFlat * big) sd = 0.0;
-            }
-            stats[(size_t)head * group + g] = make_double2(mean, sd);
-        }
+        const double2 st = gqa_query_head_stats(ph, tiles, group, g, lane);
+        if (lane == 0) stats[(size_t)head * group + g] = st;
     }
 }
 
@@ -682,11 +664,13 @@ hipError_t launch_g(const void* k, int64_t cap, int len, int n_heads, int64_t p_
                            (double)p_now, omega, qa, w, raw, partial, head_len);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // no score array: the raw scores and the per-tile partial sums only (the
+    // GQA selection forms the statistics itself)
+    if (e != hipSuccess || !scores) return e;
     hipLaunchKernelGGL(gqa_stats_kernel, dim3(n_heads), dim3(64), 0, stream, partial, tiles, G,
                        len, head_len, stats);
     e = hipGetLastError();
-    if (e != hipSuccess || !scores) return e;   // no score array: raw scores and statistics only
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gqa_norm_kernel<G>), dim3((unsigned)grid), dim3(kBlock), 0, stream, raw,
                        stats, len, tiles, scores, head_len);
     return hipGetLastError();
@@ -726,14 +710,25 @@ int64_t gqa_workspace_bytes(int64_t n_heads, int64_t len, int group)
 }
 
 void gqa_workspace_views(void* workspace, int64_t n_heads, int64_t len, int group, float** raw,
-                         double2** stats)
+                         double** partial, double2** stats)
 {
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t tiles = (len + kTileRows - 1) / kTileRows;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     *raw = reinterpret_cast<float*>(ws);
+    *partial = reinterpret_cast<double*>(ws + up(n_heads * len * group * 4));
     *stats = reinterpret_cast<double2*>(ws + up(n_heads * len * group * 4) +
                                         up(n_heads * tiles * group * 4 * 8));
+}
+
+hipError_t launch_gqa_stats(int group, const double* partial, int len, int n_heads,
+                            double2* stats, hipStream_t stream)
+{
+    if (len <= 0 || n_heads <= 0) return hipSuccess;
+    const int tiles = (len + kTileRows - 1) / kTileRows;
+    hipLaunchKernelGGL(gqa_stats_kernel, dim3(n_heads), dim3(64), 0, stream, partial, tiles, group,
+                       len, nullptr, stats);
+    return hipGetLastError();
 }
 
 hipError_t launch_gqa_normalize(int group, const float* raw, const double2* stats, int len,

@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <vector>
 
+#include "gqa_stats.h"
 #include "tri_internal.h"
 
 namespace tri {
@@ -794,18 +795,29 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(const float* __restrict_
 
 // GQA without the normalized score array: one workgroup per head of `len`
 // keys selects on the max-z keys formed from the raw per-query-head scores
-// [head][len][G] and the statistics [head][G] (GqaKeys).
+// [head][len][G] (GqaKeys); wave g first forms query head g's statistics
+// from the per-tile partial sums [head][tiles][G][4] exactly as the
+// statistics kernel does.
 template <int KPT, int G>
 __global__ __launch_bounds__(kBlock) void select_gqa_kernel(const float* __restrict__ raw,
-                                                            const double2* __restrict__ stats,
-                                                            int len, int budget,
+                                                            const double* __restrict__ partial,
+                                                            int tiles, int len, int budget,
                                                             int32_t* __restrict__ kept,
                                                             int kept_stride)
 {
     __shared__ RegLds<kBlock> L;
+    __shared__ double2 s_stats[G];
     const int h = blockIdx.x;
+    static_assert(G <= kBlock / 64, "one wave per query head");
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    if (wave < G) {   // wave g forms query head g's statistics
+        const double2 st = gqa_query_head_stats(partial + (size_t)h * tiles * G * 4, tiles, G, wave,
+                                                lane);
+        if (lane == 0) s_stats[wave] = st;
+    }
+    __syncthreads();
     select_reg_head<KPT, kBlock, false>(
-        L, GqaKeys<G>{raw + (size_t)h * (size_t)len * G, stats + (size_t)h * G}, len, budget,
+        L, GqaKeys<G>{raw + (size_t)h * (size_t)len * G, s_stats}, len, budget,
         kept + (size_t)h * (size_t)kept_stride, nullptr, nullptr);
 }
 
@@ -1741,16 +1753,17 @@ hipError_t launch_select(const float* scores, int n, int n_heads, int budget, in
 }
 
 
-hipError_t launch_select_gqa(int group, const float* raw, const double2* stats, int len,
+hipError_t launch_select_gqa(int group, const float* raw, const double* partial, int len,
                              int n_heads, int budget, int32_t* kept, int kept_stride,
                              hipStream_t stream)
 {
     if (n_heads <= 0 || len <= budget) return hipSuccess;
     if (len > kBlock * 32) return hipErrorInvalidValue;
+    const int tiles = (len + kGqaTileRows - 1) / kGqaTileRows;
     const dim3 grid((unsigned)n_heads), block(kBlock);
 #define TRI_GQA_SEL(KPT, G)                                                                       \
-    hipLaunchKernelGGL((select_gqa_kernel<KPT, G>), grid, block, 0, stream, raw, stats, len,      \
-                       budget, kept, kept_stride)
+    hipLaunchKernelGGL((select_gqa_kernel<KPT, G>), grid, block, 0, stream, raw, partial, tiles,  \
+                       len, budget, kept, kept_stride)
 #define TRI_GQA_SEL_G(KPT)                                                                        \
     switch (group) {                                                                              \
     case 2: TRI_GQA_SEL(KPT, 2); break;                                                           \

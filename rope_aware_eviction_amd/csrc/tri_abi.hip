@@ -414,17 +414,21 @@ tri_status tri_select_topb_ws(const tri_ctx* ctx, const tri_seq* seqs, int32_t n
         const tri_seq& q = seqs[s];
         if (q.len > 0 && fires(q, budget, window)) {
             float* raw = nullptr;
+            double* partial = nullptr;
             double2* stats = nullptr;
-            tri::gqa_workspace_views(ws, ctx->n_heads, q.len, ctx->group, &raw, &stats);
+            tri::gqa_workspace_views(ws, ctx->n_heads, q.len, ctx->group, &raw, &partial, &stats);
             int32_t* kp = kept + (int64_t)s * ctx->n_heads * budget;
             hipError_t e;
             if (q.len <= 32768) {
-                e = tri::launch_select_gqa(ctx->group, raw, stats, q.len, ctx->n_heads, budget, kp,
-                                           budget, hs);
+                e = tri::launch_select_gqa(ctx->group, raw, partial, q.len, ctx->n_heads, budget,
+                                           kp, budget, hs);
             } else {
-                // longer heads: the normalized scores first, then the plain selection
-                e = tri::launch_gqa_normalize(ctx->group, raw, stats, q.len, ctx->n_heads,
-                                              scores + off, hs);
+                // longer heads: the statistics and the normalized scores first,
+                // then the plain selection
+                e = tri::launch_gqa_stats(ctx->group, partial, q.len, ctx->n_heads, stats, hs);
+                if (e == hipSuccess)
+                    e = tri::launch_gqa_normalize(ctx->group, raw, stats, q.len, ctx->n_heads,
+                                                  scores + off, hs);
                 if (e == hipSuccess)
                     e = tri::launch_select(scores + off, q.len, ctx->n_heads, budget, kp, budget,
                                            nullptr, hs);

@@ -59,17 +59,22 @@ hipError_t launch_gqa_score(tri_dtype dtype, int head_dim, int group, const void
                             int len, int n_heads, int64_t p_now, const double* omega,
                             const double2* qa, const float* w, void* workspace, float* scores,
                             const int32_t* head_len, hipStream_t stream);
-// The raw scores [n_heads][len][group] and statistics [n_heads][group] in a
-// GQA workspace laid out by launch_gqa_score (scores == nullptr there stops
-// after the statistics); launch_gqa_normalize writes the normalized scores
-// of such a workspace.
+// The raw scores [n_heads][len][group], per-tile partial sums
+// [n_heads][tiles][group][4] and statistics [n_heads][group] in a GQA
+// workspace laid out by launch_gqa_score (scores == nullptr there stops after
+// the raw scores and partial sums: launch_gqa_stats then forms the
+// statistics); launch_gqa_normalize writes the normalized scores of such a
+// workspace.
 void gqa_workspace_views(void* workspace, int64_t n_heads, int64_t len, int group, float** raw,
-                         double2** stats);
+                         double** partial, double2** stats);
+hipError_t launch_gqa_stats(int group, const double* partial, int len, int n_heads,
+                            double2* stats, hipStream_t stream);
 hipError_t launch_gqa_normalize(int group, const float* raw, const double2* stats, int len,
                                 int n_heads, float* scores, hipStream_t stream);
 // Top-`budget` of heads of len <= 32768 keys, keyed by the normalized GQA
-// score formed from a workspace's raw scores and statistics.
-hipError_t launch_select_gqa(int group, const float* raw, const double2* stats, int len,
+// score formed from a workspace's raw scores and per-tile partial sums (each
+// workgroup forms its head's statistics as the statistics kernel does).
+hipError_t launch_select_gqa(int group, const float* raw, const double* partial, int len,
                              int n_heads, int budget, int32_t* kept, int kept_stride,
                              hipStream_t stream);
 
