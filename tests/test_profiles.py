@@ -55,8 +55,8 @@ STEP_KERNELS = {
     "wide": ("score_kernel<128, true>", "select_wide_kernel", "compact_kernel<256, 1>"),
     "batched": ("score_kernel<128, true>", "select_batch_kernel<32>", "select_batch_kernel<24>",
                 "select_batch_kernel<16>", "select_batch_kernel<8>", "compact_batch_kernel<256>"),
-    "qwen3_32k_gqa": ("gqa_mfma_kernel<128, 4>", "gqa_stats_kernel", "select_gqa_kernel<32, 4>",
-                      "compact_kernel<256, 1>"),
+    "qwen3_32k_gqa": ("gqa_prep_kernel<128, 4>", "gqa_mfma_kernel<128, 4>",
+                      "select_gqa_kernel<32, 4>", "compact_kernel<256, 1>"),
     "shared_floor1024": ("select_reg_kernel<32, 1024, true>", "shared_pass_kernel",
                          "shared_write_kernel<32>", "order_kernel", "compact_kernel<256, 2>"),
 }
