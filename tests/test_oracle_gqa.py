@@ -144,3 +144,22 @@ def test_gqa_max_over_the_group_of_separately_normalized_heads(oracle_lib):
     each = [oracle_lib.gqa_head(K, pos, 4000, om, [1, 2, 4], qr[g:g + 1], qi[g:g + 1],
                                 m[g:g + 1], R[g:g + 1])[2] for g in range(3)]
     np.testing.assert_array_equal(score, np.max(np.vstack(each), axis=0))
+
+
+def test_gqa_z_rows_equal_a_library_zscore(oracle_lib):
+    """The per-query-head normalization against a library routine
+    (scipy.stats.zscore, population deviation) over the finite scores of each
+    row; a key with a non-finite element has NaN in every row."""
+    stats = pytest.importorskip("scipy.stats")
+    rng = np.random.default_rng(11)
+    qr, qi, m, R, pos, K = _random_group(rng, 16, 257, 4)
+    K[[5, 100]] = np.nan
+    K[200, 3] = np.inf
+    om = oracle_lib.omega(16, 1e4)
+    raw, z, score = oracle_lib.gqa_head(K, pos, 5000, om, [1, 2, 4, 8, 16], qr, qi, m, R)
+    fin = np.isfinite(K).all(axis=1)
+    for g in range(4):
+        assert np.all(np.isnan(z[g][~fin]))
+        np.testing.assert_allclose(z[g][fin], stats.zscore(raw[g][fin], ddof=0), rtol=0, atol=1e-12)
+    assert np.all(np.isnan(score[~fin]))
+    np.testing.assert_array_equal(score[fin], np.max(z[:, fin], axis=0))
