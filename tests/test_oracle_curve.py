@@ -75,3 +75,25 @@ def test_offset_sets(oracle_lib):
     np.testing.assert_array_equal(oracle_lib.offset_set("linear", 1000, 7),
                                   [143, 286, 429, 571, 714, 857, 1000])
     np.testing.assert_array_equal(oracle_lib.offset_set("linear", 3, 6), [1, 1, 2, 2, 3, 3])
+
+
+def test_curve_is_the_logit_of_a_model_librarys_rope(oracle_lib):
+    """The curve with the oracle's own frequencies against a model library's
+    RoPE (the Llama rotary embedding of `transformers`): the dot product of
+    the query centre rotated to position i + delta and the key centre rotated
+    to position i (the library computes its angles in fp32, so positions stay
+    small)."""
+    from test_oracle_pins import _library_rope
+    rng = np.random.default_rng(31)
+    for d, theta in ((64, 1e4), (128, 1e6)):
+        _, rotate = _library_rope(d, theta)
+        qr, qi, kr, ki = _pair(rng, d)
+        q = np.concatenate([qr, qi])
+        k = np.concatenate([kr, ki])
+        deltas = np.array([0, 1, 2, 7, 40, 100, -5], dtype=np.int64)
+        got = oracle_lib.distance_curve(oracle_lib.omega(d, theta), qr, qi, kr, ki, deltas)
+        i = 120
+        kk = rotate(k[None], [i])[0]
+        for dj, g in zip(deltas, got):
+            ref = float(rotate(q[None], [i + int(dj)])[0] @ kk)
+            assert abs(g - ref) <= 1e-6 * np.abs(q).sum() * np.abs(k).sum(), (d, dj, g, ref)
