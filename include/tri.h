@@ -29,14 +29,17 @@
  *   - All device pointers are owned by the caller.  The library owns only
  *     the calibration tables inside a tri_ctx.
  *   - The per-step calls (tri_score, tri_score_ws, tri_select_topb,
- *     tri_compact_kv, tri_select_shared, tri_compact_kv_counts) and
+ *     tri_select_topb_ws, tri_compact_kv, tri_select_shared,
+ *     tri_compact_kv_counts, tri_compact_kv_counts_noalloc) and
  *     tri_calibrate_stats / tri_distance_curve enqueue work on the given
  *     stream (a hipStream_t; NULL is the null stream) and never synchronise.
  *     Argument errors are reported synchronously before anything is
  *     enqueued.  The device current on the calling thread must be the
  *     context's device.  None of them allocates: scratch memory, where a
  *     call needs it, is a caller-owned workspace of the size its
- *     *_workspace_bytes call gives.
+ *     *_workspace_bytes call gives (tri_compact_kv_counts_noalloc uses the
+ *     library's static device scratch instead).  They launch kernels only,
+ *     so a caller may capture them in a HIP graph.
  *   - A head fires iff len > budget + window; the calls with a budget skip
  *     sequences that do not fire.  With head-specific budgets
  *     (tri_select_shared) a whole layer fires or not; see there.
