@@ -928,3 +928,42 @@ def test_rows_per_head_limit():
     assert float(scores[:lim - 1].abs().max()) == 0.0
     del k, scores
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n", [8192, 8193, 16384, 16385, 24576, 24577, 32768, 32769])
+@pytest.mark.parametrize("frac", [0.0, 0.33, 1.0])
+def test_select_at_the_length_class_edges(orc, n, frac):
+    """Heads at and one past each register-resident length class (8, 16, 24
+    and 32 keys per thread) and the single-read long-head path, with budgets
+    of 1, a third and n - 1: kept lists bit-exact with the oracle, alone and
+    as one sequence of a batch beside a head of another class."""
+    B = max(1, min(n - 1, int(n * frac)))
+    kind = ("ties", "normal", "straddle")[int(frac * 2)]
+    H = 2
+    sc = synth.make_scores(kind, H, n, seed=n + B)
+    pos = np.arange(n)
+    ctx = tri.tri_calibrate_load(1, H, 64, np.zeros((1, H, 32)), np.zeros((1, H, 32)),
+                                 np.ones((1, H, 32)), np.ones((1, H, 32)), [1], device=0)
+    k = torch.zeros((1, H, n, 64), dtype=torch.float32, device="cuda")
+    other = 5000 if n > 9000 else 20000
+    k2 = torch.zeros((1, H, other, 64), dtype=torch.float32, device="cuda")
+    sc2 = synth.make_scores("normal", H, other, seed=other)
+    ref = [orc.select_head(sc[h].astype(np.float64), pos, B, 0) for h in range(H)]
+    # alone
+    kept = torch.full((H * B,), -7, dtype=torch.int32, device="cuda")
+    tri.tri_select_topb(ctx, [tri.Seq(k, None, None, n, n - 1)], torch.from_numpy(sc.reshape(-1)).cuda(),
+                        B, 0, kept)
+    kg = kept.cpu().numpy().reshape(H, B)
+    for h in range(H):
+        np.testing.assert_array_equal(kg[h], ref[h])
+    # in a batch, after a sequence of another length class
+    if other > B:
+        both = torch.from_numpy(np.concatenate([sc2.reshape(-1), sc.reshape(-1)])).cuda()
+        kept2 = torch.full((2 * H * B,), -7, dtype=torch.int32, device="cuda")
+        tri.tri_select_topb(ctx, [tri.Seq(k2, None, None, other, other - 1),
+                                  tri.Seq(k, None, None, n, n - 1)], both, B, 0, kept2)
+        kg2 = kept2.cpu().numpy().reshape(2, H, B)
+        for h in range(H):
+            np.testing.assert_array_equal(kg2[1, h], ref[h])
+            np.testing.assert_array_equal(
+                kg2[0, h], orc.select_head(sc2[h].astype(np.float64), np.arange(other), B, 0))
