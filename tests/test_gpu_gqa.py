@@ -246,6 +246,8 @@ def test_gqa_fused_pass(orc, name, sample):
     ("gqa_small", {"lengths": (4001, 300, 2600), "name": "gqa_small_three"}),
     # every register-resident length class (8, 16, 24 and 32 keys per thread)
     ("gqa_small", {"lengths": (20000, 9000, 30000, 5000), "name": "gqa_small_classes"}),
+    # one past each class edge, and the largest head the register-resident path takes
+    ("gqa_small", {"lengths": (8193, 16385, 24577, 32768, 24576), "name": "gqa_small_edges"}),
 ])
 def test_gqa_select_from_the_workspace_equals_the_two_step_path(name, over):
     """tri_select_topb_ws (keys formed from the raw scores and statistics)
