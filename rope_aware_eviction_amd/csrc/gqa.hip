@@ -388,14 +388,17 @@ __global__ __launch_bounds__(64) void gqa_prep_kernel(double p_now, const double
     __shared__ float s_w[G][kHalf];
     const int head = blockIdx.x;
     const int lane = threadIdx.x;
-    for (int t = lane; t < G * kHalf; t += 64) {
-        const int g = t / kHalf, f = t - g * kHalf;
+    // one rotation e^{i w_f p_now} per band, shared by the G query heads
+    for (int f = lane; f < kHalf; f += 64) {
         double sn, cs;
         sincos(omega[f] * p_now, &sn, &cs);
-        const double2 a = qa[((size_t)head * G + g) * kHalf + f];
-        s_u[g][f] = (float)(a.x * cs - a.y * sn);
-        s_u[g][f + kHalf] = (float)(a.x * sn + a.y * cs);
-        s_w[g][f] = w[((size_t)head * G + g) * kHalf + f];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const double2 a = qa[((size_t)head * G + g) * kHalf + f];
+            s_u[g][f] = (float)(a.x * cs - a.y * sn);
+            s_u[g][f + kHalf] = (float)(a.x * sn + a.y * cs);
+            s_w[g][f] = w[((size_t)head * G + g) * kHalf + f];
+        }
     }
     __syncthreads();
     const int q = lane >> 4, rl = lane & 15;

@@ -58,12 +58,6 @@ __device__ __forceinline__ uint32_t ordered_key(float x)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inverse of ordered_key for keys of numbers (key >= 2).
-__device__ __forceinline__ float key_to_float(uint32_t k)
-{
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
 template <bool kInLds>
 __device__ __forceinline__ uint32_t key_at(const uint32_t* lds_keys, const float* sc, int i)
 {
