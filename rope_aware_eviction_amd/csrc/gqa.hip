@@ -9,17 +9,22 @@
 // the largest |score| counts as zero and gives z = 0; a non-finite score
 // gives NaN, which loses to every number in the max.
 //
-// Three launches per sequence:
-//   1. gqa_score_kernel: one pass over K.  Every row gets G raw scores (the
-//      score of the single-query-head kernel with query head g's folded
-//      constants); the band magnitudes |K_f| are shared by the G norm terms.
-//      Raw scores go to the workspace [head][row][g]; per 512-row tile and
-//      query head the kernel also writes fp64 partial statistics (sum, sum
-//      of squares, count of finite scores, largest |score|).
+// Launches per sequence:
+//   1. One pass over K.  Every row gets G raw scores (the score of the
+//      single-query-head kernel with query head g's folded constants); the
+//      band magnitudes |K_f| are shared by the G norm terms.  Raw scores go
+//      to the workspace [head][row][g]; per 512-row tile and query head the
+//      pass also writes fp64 partial statistics (sum, sum of squares, count
+//      of finite scores, largest |score|).  bf16 K: gqa_prep_kernel folds
+//      the constants into matrix-core operands, gqa_mfma_kernel scores;
+//      f32 K: gqa_score_kernel.
+//   With a score array:
 //   2. gqa_stats_kernel: per (head, g), the partials summed in tile order
 //      (deterministic) into the mean and the deviation (0 when flat).
 //   3. gqa_norm_kernel: z = (s - mean) / sd per query head in fp64, the max
 //      over the group, rounded once to fp32 into the caller's score array.
+//   Without one, the GQA selection forms the statistics (gqa_stats.h) and
+//   the max-z keys from the workspace itself (select_gqa_kernel).
 #include <type_traits>
 
 #include "gqa_stats.h"
