@@ -358,3 +358,63 @@ def test_gqa_prune_step_without_scores(orc, name, sample):
     for (l, h), (K, _, P) in inputs.items():
         s_ref, tol = oracle_gqa(orc, cache, 0, l, h, K, P)
         check_kept(orc, s_ref, tol, P, kg[l, h], B, W, "%s l%d h%d" % (name, l, h))
+
+
+def _random_gqa_spec(case):
+    """A seeded small GQA configuration: G from 2 to 8 (every instantiated
+    group size turns up), dtype, head_dim, layers, KV heads, one or two
+    sequences, budget, window, RoPE base, offset set and key recipe."""
+    rng = np.random.default_rng(2000 + case)
+    recipe = ["toy", "concentrated", "phase"][int(rng.integers(3))]
+    budget, window = int(rng.integers(1, 1200)), int(rng.integers(0, 200))
+    lengths = tuple(int(x) for x in rng.integers(budget + window + 1, 5000, size=int(rng.integers(1, 3))))
+    return synth.workload("gqa_small").replace(
+        name="gqa_random%d" % case, group=2 + case % 7, n_layers=int(rng.integers(1, 3)),
+        n_kv_heads=int(rng.integers(1, 3)), head_dim=[64, 128][int(rng.integers(2))],
+        dtype=["bf16", "f32"][int(rng.integers(2))], rope_theta=float([1e4, 5e5, 1e6][int(rng.integers(3))]),
+        lengths=lengths, budget=budget, window=window, recipe=recipe,
+        offsets=synth.pow2_offsets(int(rng.integers(8, 17))),
+        outlier_frac=0.05 if recipe == "concentrated" else 0.0)
+
+
+@pytest.mark.parametrize("case", range(14))
+def test_gqa_random_small_configs(orc, case):
+    """Seeded random GQA configurations through the prune step the benchmark
+    times (score into the workspace, select from it, compact): every head's
+    kept set against the oracle, the top-B of the GPU's own aggregated scores,
+    bit-exact compaction."""
+    spec = _random_gqa_spec(case)
+    B, W = spec.budget, spec.window
+    say("gqa random config", case, "G =", spec.group, spec.dtype, spec.head_dim, spec.n_layers,
+        spec.n_kv_heads, spec.lengths, B, W, spec.recipe)
+    cache = synth.make_cache(spec, "cuda", seed=case)
+    inputs = {(s, l, h): head_inputs(cache, s, l, h) for s in range(spec.n_seq)
+              for l in range(spec.n_layers) for h in range(spec.n_kv_heads)}
+    before = [(k.clone(), v.clone(), p.clone()) for k, v, p in zip(cache.k, cache.v, cache.pos)]
+    ctx = ctx_gqa(cache)
+    seqs = seqs_for(cache)
+    ws = workspace_for(ctx, seqs)
+    scores = torch.empty(tri.scores_count(ctx, seqs), device="cuda")
+    tri.tri_score(ctx, seqs, scores, workspace=ws)     # the GPU's own scores, for the property
+    kept = torch.empty(spec.n_seq * spec.heads * B, dtype=torch.int32, device="cuda")
+    tri.prune_step_gqa(ctx, seqs, B, W, kept, ws)
+    torch.cuda.synchronize()
+    off = 0
+    for s in range(spec.n_seq):
+        n = cache.lens[s]
+        assert seqs[s].len == B
+        ks = kept[s * spec.heads * B:(s + 1) * spec.heads * B]
+        check_topb_property(scores[off:off + spec.heads * n].view(spec.heads, n), ks.view(spec.heads, B), n)
+        off += spec.heads * n
+        kl = ks.view(spec.n_layers, spec.n_kv_heads, B).long()
+        k_in, v_in, p_in = before[s]
+        for t_in, t_out in ((k_in, cache.k[s]), (v_in, cache.v[s])):
+            g = torch.gather(t_in, 2, kl[..., None].expand(-1, -1, -1, spec.head_dim))
+            assert torch.equal(bits(g), bits(t_out[:, :, :B]))
+        assert torch.equal(torch.gather(p_in, 2, kl), cache.pos[s][:, :, :B])
+        kg = kl.cpu().numpy()
+        for l in range(spec.n_layers):
+            for h in range(spec.n_kv_heads):
+                K, _, P = inputs[(s, l, h)]
+                s_ref, tol = oracle_gqa(orc, cache, s, l, h, K, P)
+                check_kept(orc, s_ref, tol, P, kg[l, h], B, W, "%s s%d l%d h%d" % (spec.name, s, l, h))

@@ -685,6 +685,39 @@ def test_fused_many_sequences_every_length_class(orc):
     assert _fused(orc, spec, 13, sample) == len(sample)
 
 
+def _random_spec(case):
+    """A seeded small configuration: dtype, head_dim, layers, KV heads,
+    ragged lengths (some at or below the firing boundary), budget, window,
+    RoPE base, offset set and key recipe."""
+    rng = np.random.default_rng(1000 + case)
+    recipe = ["toy", "concentrated", "phase", "neartie"][int(rng.integers(4))]
+    dtype = "bf16" if recipe == "neartie" else ["bf16", "f32"][int(rng.integers(2))]
+    d = [64, 128][int(rng.integers(2))]
+    budget, window = int(rng.integers(1, 1500)), int(rng.integers(0, 200))
+    lengths = [int(x) for x in rng.integers(1, 5000, size=int(rng.integers(1, 4)))]
+    if rng.random() < 0.4:
+        lengths[int(rng.integers(len(lengths)))] = int(rng.integers(1, budget + window + 1))
+    return synth.workload("toy").replace(
+        name="random%d" % case, n_layers=int(rng.integers(1, 3)), n_kv_heads=int(rng.integers(1, 4)),
+        head_dim=d, rope_theta=float([1e4, 5e5, 1e6][int(rng.integers(3))]), lengths=tuple(lengths),
+        budget=budget, window=window, dtype=dtype, recipe=recipe,
+        offsets=synth.pow2_offsets(int(rng.integers(8, 17))),
+        dup_frac=0.1 if recipe == "neartie" else 0.0,
+        outlier_frac=0.05 if recipe == "concentrated" else 0.0)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_fused_random_small_configs(orc, case):
+    """Seeded random small configurations through the whole prune step, every
+    head against the oracle (scores, kept set, compaction bit for bit)."""
+    spec = _random_spec(case)
+    say("random config", case, spec.dtype, spec.head_dim, spec.n_layers, spec.n_kv_heads,
+        spec.lengths, spec.budget, spec.window, spec.recipe, spec.rope_theta)
+    sample = [(s, l, h) for s in range(spec.n_seq) for l in range(spec.n_layers)
+              for h in range(spec.n_kv_heads)]
+    assert _fused(orc, spec, case, sample) == len(sample)
+
+
 def test_degenerate_calls(orc):
     """No sequences at all; a batch with empty sequences, a one-key sequence,
     one exactly at the firing boundary (len = budget + window, does not fire)
