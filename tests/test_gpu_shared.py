@@ -128,6 +128,30 @@ def test_shared_select_bit_exact_on_synthetic_scores(orc, kind, L, H, n, budget,
     say("  layers fired: %d of %d" % (fired, L))
 
 
+def _random_shared_case(case):
+    """A seeded draw of score kind, layers, KV heads, keys per head, budget,
+    floor, window and head lengths for the shared selection."""
+    rng = np.random.default_rng(3000 + case)
+    kinds = ["normal", "ties", "allequal", "special", "dups", "straddle", "narrow", "ulp",
+             "outlier", "wide"]
+    L, H = int(rng.integers(1, 4)), int(rng.integers(1, 17))
+    n = int(rng.integers(50, 20000))
+    budget = int(rng.integers(1, max(2, n // 2)))
+    floor = int(rng.integers(0, budget + 1))
+    window = int(rng.integers(0, 100))
+    lengths = ["full", "ragged", "extreme"][int(rng.integers(3))]
+    return kinds[int(rng.integers(len(kinds)))], L, H, n, budget, floor, window, lengths
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_shared_select_random_synthetic_scores(orc, case):
+    """Seeded random shared selections on synthetic scores, bit-exact with the
+    oracle's shared selection on every layer."""
+    kind, L, H, n, budget, floor, window, lengths = _random_shared_case(case)
+    test_shared_select_bit_exact_on_synthetic_scores(orc, kind, L, H, n, budget, floor, window,
+                                                     lengths)
+
+
 def test_shared_select_without_head_lengths(orc):
     """head_len NULL: every head holds len rows."""
     L, H, n, B, F = 2, 8, 4000, 300, 30
@@ -485,6 +509,30 @@ def test_fused_shared_extreme_lengths(orc):
 def test_fused_shared_gqa(orc):
     spec = synth.workload("gqa_small")
     fused_shared(orc, spec, 2, "ragged", spec.budget // 8, tuple(range(spec.n_layers)))
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_fused_shared_random_small_configs(orc, case):
+    """Seeded random small caches through the shared-budget prune step (single
+    table or GQA), every layer against the oracle and every compacted row bit
+    for bit."""
+    rng = np.random.default_rng(4000 + case)
+    recipe = ["toy", "concentrated", "phase", "neartie"][int(rng.integers(4))]
+    group = int(rng.choice([1, 1, 2, 4]))
+    dtype = "bf16" if recipe == "neartie" or group > 1 else ["bf16", "f32"][int(rng.integers(2))]
+    n = int(rng.integers(300, 6000))
+    budget = int(rng.integers(16, max(17, n // 3)))
+    spec = synth.workload("llama8b").replace(
+        name="shared_random%d" % case, n_layers=int(rng.integers(1, 4)),
+        n_kv_heads=int(rng.integers(1, 9)), head_dim=[64, 128][int(rng.integers(2))], dtype=dtype,
+        rope_theta=float([1e4, 5e5, 1e6][int(rng.integers(3))]), lengths=(n,), budget=budget,
+        window=int(rng.integers(0, 150)), recipe=recipe, group=group,
+        offsets=synth.pow2_offsets(int(rng.integers(8, 17))),
+        dup_frac=0.1 if recipe == "neartie" else 0.0,
+        outlier_frac=0.05 if recipe == "concentrated" else 0.0)
+    floor = int(rng.integers(0, budget + 1))
+    lengths = ["full", "ragged", "extreme"][int(rng.integers(3))]
+    fused_shared(orc, spec, case, lengths, floor, tuple(range(spec.n_layers)))
 
 
 def test_shared_select_and_compaction_over_several_sequences(orc):
