@@ -89,3 +89,14 @@ def test_calibrated_context_scores_like_the_oracle(orc):
         _, _, s_ref = orc.score_head(K, P, cache.p_now[0], om, np.array(spec.offsets), *ref_stats)
         M = orc.bound_head(K, om, np.array(spec.offsets), *ref_stats)
         check_scores(sg[h], s_ref, M, "calibrated from samples h%d" % h)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_calib_stats_random_shapes(orc, case):
+    """Seeded random sample counts, query heads, head_dim and dtype."""
+    rng = np.random.default_rng(6000 + case)
+    dtype, d = ["bf16", "f32"][int(rng.integers(2))], [64, 128][int(rng.integers(2))]
+    n, H = int(rng.integers(1, 6000)), int(rng.integers(1, 20))
+    say("calibration statistics, random", case, dtype, d, n, H)
+    q, _, _ = synth.query_samples(H, d, n, seed=6000 + case, dtype=dtype, device="cuda")
+    _stats_vs_oracle(orc, q, range(H))

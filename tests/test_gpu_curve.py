@@ -84,3 +84,42 @@ def test_scores_with_other_offset_sets(orc, kind, maxd, count):
         _, _, s_ref = orc.score_head(K, P, cache.p_now[0], om, cal.offsets, *args)
         M = orc.bound_head(K, om, cal.offsets, *args)
         check_scores(sg[h], s_ref, M, "%s %d h%d" % (kind, maxd, h))
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_distance_curve_random_shapes(orc, case):
+    """Seeded random shapes for the tiled curve kernel (64 distances by 64
+    query heads per workgroup, bands in LDS 16 at a time): head_dim, layers,
+    KV heads, G, the number of distances (tile edges included) and their
+    values (negative, zero, far), with the oracle's frequencies."""
+    rng = np.random.default_rng(5000 + case)
+    d = [64, 128][int(rng.integers(2))]
+    spec = synth.workload("gqa_toy").replace(
+        name="curve_random%d" % case, n_layers=int(rng.integers(1, 4)),
+        n_kv_heads=int(rng.integers(1, 9)), head_dim=d, group=int(rng.integers(1, 9)),
+        rope_theta=float([1e4, 5e5, 1e6][int(rng.integers(3))]))
+    n_delta = int(rng.choice([1, 63, 64, 65, 128, 129, int(rng.integers(2, 400))]))
+    deltas = rng.integers(-(1 << 20), 1 << 20, size=n_delta).astype(np.int64)
+    deltas[::7] = rng.integers(-(1 << 40), 1 << 40, size=deltas[::7].size)
+    if n_delta > 2:
+        deltas[:2] = [0, 1]
+    cal = synth._model(spec, case)[2]
+    om = orc.omega(d, spec.rope_theta)
+    ctx = tri.tri_calibrate_load(spec.n_layers, spec.n_kv_heads, d, cal.qc_re, cal.qc_im,
+                                 cal.q_mean_norm, cal.q_mrl, cal.offsets, rope_theta=cal.rope_theta,
+                                 inv_freq=om, device=0, n_q_heads=spec.n_q_heads)
+    h = d // 2
+    kc = rng.standard_normal((spec.heads, 2, h))
+    say("curve random", case, "d", d, "kv heads", spec.heads, "G", spec.group, "distances", n_delta)
+    curve = tri.tri_distance_curve(ctx, torch.from_numpy(kc[:, 0].copy()).cuda(),
+                                   torch.from_numpy(kc[:, 1].copy()).cuda(),
+                                   torch.from_numpy(deltas).cuda()).cpu().numpy()
+    G = spec.group
+    qre = cal.qc_re.reshape(-1, h)
+    qim = cal.qc_im.reshape(-1, h)
+    assert curve.shape == (spec.heads * G, n_delta)
+    for qh in range(spec.heads * G):
+        kv = qh // G
+        ref = orc.distance_curve(om, qre[qh], qim[qh], kc[kv, 0], kc[kv, 1], deltas)
+        qk = np.hypot(qre[qh], qim[qh]) * np.hypot(kc[kv, 0], kc[kv, 1])
+        assert np.all(np.abs(curve[qh] - ref) <= 1e-9 * qk.sum()), qh
