@@ -15,8 +15,10 @@ Pinned by ``tests/test_oracle_pins.py`` against brute-force RoPE dot products,
 the pages' polar per-band form, closed-form special cases, hand-worked
 fixtures, library sorts, brute-force subset search and invariants;
 ``tests/test_oracle_mutants.py`` checks that planted mistakes fail those pins.
-Whole-score parity with the authors' own implementation is unpinned (the
-pages print no worked example, and the norm-term weight is a reading).
+Every function has such pins.  Agreement with the authors' own
+implementation cannot be checked (the pages print no worked score example);
+the norm-term weight (1 - R_f) * E|q_f| is a reading of the pages' list of
+calibrated quantities, stated in the C file's header.
 """
 from __future__ import annotations
 
