@@ -20,8 +20,9 @@ Prints one JSON line.  Extra modes:
   --pmc-steps N      a plain 1 GiB device copy, then N steps with no restores
                      (for rocprofv3 counter runs; see --summarize-pmc)
   --summarize-pmc D  turn rocprofv3 counter CSVs under D (runs of --pmc-steps N
-                     on --workload W) into profiles/score_kernel_W_traffic.json,
-                     which later runs report as roofline.traffic
+                     on --workload W) into profiles/K_W_traffic.json (K the
+                     score-phase kernel: score_kernel, or gqa_mfma_kernel for
+                     GQA), which later runs report as roofline.traffic
   --shared-floor F   head-specific budgets: the KV heads of a layer share
                      budget * n_kv_heads slots, each keeping at least its F
                      best keys (shared select and counted compaction)
@@ -45,19 +46,27 @@ HBM_PEAK_GBS = 8000.0
 FP64_PEAK_TFLOPS = 78.6
 METRIC = "cached keys scored+pruned/sec (G keys/s) and achieved HBM GB/s vs peak"
 SCORE_KERNEL = "score_kernel"
-# the score kernel's source (tri_internal.h holds only declarations shared by
-# every kernel file, so it is not part of the hash)
+GQA_SCORE_KERNEL = "gqa_mfma_kernel"
+# each score kernel's sources (tri_internal.h holds only declarations shared
+# by every kernel file, so it is not part of the hash)
 KERNEL_SOURCES = ["rope_aware_eviction_amd/csrc/score.hip"]
+GQA_KERNEL_SOURCES = ["rope_aware_eviction_amd/csrc/gqa.hip", "rope_aware_eviction_amd/csrc/gqa_stats.h"]
 
 
-def traffic_file(workload: str) -> str:
-    """Committed byte-counter summary of the score kernel on one workload."""
-    return os.path.join(ROOT, "profiles", "score_kernel_%s_traffic.json" % workload)
+def score_kernel_of(group: int):
+    """(name, sources) of the kernel of the score phase: the single-table
+    kernel, or the GQA matrix-core kernel (G > 1, the workloads' bf16 K)."""
+    return (SCORE_KERNEL, KERNEL_SOURCES) if group == 1 else (GQA_SCORE_KERNEL, GQA_KERNEL_SOURCES)
 
 
-def kernel_hash() -> str:
+def traffic_file(workload: str, kernel: str = SCORE_KERNEL) -> str:
+    """Committed byte-counter summary of a score kernel on one workload."""
+    return os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel, workload))
+
+
+def kernel_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -188,21 +197,22 @@ def cpu_baseline_shared(cache, n_layers_sample: int, floor: int):
 def load_traffic(spec):
     """roofline.traffic from the committed counter summary of this workload, or
     None when absent or taken on a different score kernel source."""
+    kernel, sources = score_kernel_of(spec.group)
     try:
-        with open(traffic_file(spec.name)) as f:
+        with open(traffic_file(spec.name, kernel)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != spec.name:
+    if t.get("kernel_hash") != kernel_hash(sources) or t.get("workload") != spec.name:
         return None
     return t.get("traffic_bytes_per_launch")
 
 
 # kernel classes the counter summaries report (the first name a kernel's
 # full name contains decides its class)
-PMC_KERNELS = ("gqa_score_kernel", "gqa_mfma_kernel", "gqa_norm_kernel", SCORE_KERNEL,
-               "select_batch_kernel", "select_reg_kernel", "select_kernel", "compact_batch_kernel",
-               "compact_kernel", "copyBuffer")
+PMC_KERNELS = ("gqa_score_kernel", "gqa_prep_kernel", "gqa_mfma_kernel", "gqa_norm_kernel",
+               SCORE_KERNEL, "select_batch_kernel", "select_reg_kernel", "select_gqa_kernel",
+               "select_kernel", "compact_batch_kernel", "compact_kernel", "copyBuffer")
 REQ_COUNTERS = ("TCC_EA0_RDREQ", "TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B",
                 "TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B")
 
@@ -258,8 +268,10 @@ def summarize_pmc(directory: str, workload: str, steps: int):
                 "wrreq": wr, "wrreq_64b": w64, "read_bytes": 32 * r32 + 64 * r64 + 128 * r128,
                 "write_bytes": 64 * w64 + 32 * (wr - w64)}
 
+    import synth
+    kernel, sources = score_kernel_of(synth.workload(workload).group)
     copy_bytes = float(1 << 30)
-    out = {"workload": workload, "kernel": SCORE_KERNEL, "kernel_hash": kernel_hash(),
+    out = {"workload": workload, "kernel": kernel, "kernel_hash": kernel_hash(sources),
            "steps": steps, "unit": "bytes per prune step (all launches of the kernel class)"}
     cr = req_bytes(copy_val)
     if cr:
@@ -287,14 +299,14 @@ def summarize_pmc(directory: str, workload: str, steps: int):
                                                vals["FETCH_SIZE"].get(k) or []) / steps
             per[k] = entry
     out["kernels"] = per
-    sk = per.get(SCORE_KERNEL, {})
+    sk = per.get(kernel, {})
     if "requests" in sk:
         out["traffic_bytes_per_launch"] = sk["requests"]["read_bytes_scaled"] + sk["requests"]["write_bytes_scaled"]
         out["traffic_from"] = "TCC_EA0 read and write requests by size, scaled by the 1 GiB copy"
     elif "derived" in sk:
         out["traffic_bytes_per_launch"] = sk["derived"]["fetch_bytes_scaled"] + sk["derived"]["write_bytes_scaled"]
         out["traffic_from"] = "FETCH_SIZE + WRITE_SIZE, scaled by the 1 GiB copy"
-    path = traffic_file(workload)
+    path = traffic_file(workload, kernel)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -391,8 +403,8 @@ def main():
                     help="heads of the cache the oracle baseline prunes (0 = skip)")
     ap.add_argument("--pmc-steps", type=int, default=0)
     ap.add_argument("--summarize-pmc", default=None, metavar="DIR",
-                    help="write profiles/score_kernel_<workload>_traffic.json from the counter CSVs "
-                         "under DIR (with --workload)")
+                    help="write profiles/<score kernel>_<workload>_traffic.json from the counter "
+                         "CSVs under DIR (with --workload)")
     ap.add_argument("--calib-stats", type=int, default=0, metavar="N_SAMPLES",
                     help="measure tri_calibrate_stats instead: N_SAMPLES pre-RoPE query samples of "
                          "the Qwen3-8B query heads (36 layers x 32 heads x head_dim 128, bf16)")

@@ -48,6 +48,27 @@ def test_every_workload_has_fresh_counters():
         assert 0.99 < k["read_bytes_scaled"] / k_read < 1.03, w
 
 
+def test_gqa_counters_match_the_gqa_kernel_source():
+    # the GQA line's counters were taken on the current GQA kernel sources; the
+    # kernel reads each K row about once and writes the raw scores and tile
+    # statistics once, and the selection reads them back once
+    kernel, sources = bench.score_kernel_of(4)
+    with open(bench.traffic_file("qwen3_32k_gqa", kernel)) as f:
+        t = json.load(f)
+    assert t["workload"] == "qwen3_32k_gqa" and t["kernel"] == "gqa_mfma_kernel"
+    assert t["kernel_hash"] == bench.kernel_hash(sources)
+    sp = synth.workload("qwen3_32k_gqa")
+    _, k_read, _ = bench.workload_bytes(sp)
+    n = sp.lengths[0]
+    inter = sp.heads * n * sp.group * 4 + sp.heads * ((n + 511) // 512) * sp.group * 32
+    k = t["kernels"]["gqa_mfma_kernel"]["requests"]
+    assert 0.99 < k["read_bytes_scaled"] / k_read < 1.03
+    assert 0.99 < k["write_bytes_scaled"] / inter < 1.03
+    sel = t["kernels"]["select_gqa_kernel"]["requests"]
+    assert 0.99 < sel["read_bytes_scaled"] / inter < 1.03
+    assert t["traffic_bytes_per_launch"] == k["read_bytes_scaled"] + k["write_bytes_scaled"]
+
+
 STEP_KERNELS = {
     "qwen3_32k": ("score_kernel<128, true>", "select_reg_kernel<32, 1024, false>",
                   "compact_kernel<256, 1>"),
