@@ -621,8 +621,8 @@ def main():
                    "budgets": ("shared per layer (budget x %d KV heads), floor %d per head"
                                % (spec.n_kv_heads, F)) if shared else "uniform per head"},
         "roofline": {"bound": "hbm", "kernel": SCORE_KERNEL if spec.group == 1 else
-                     "GQA score phase (gqa_prep_kernel, gqa_mfma_kernel, gqa_stats_kernel; f32 K: "
-                     "gqa_score_kernel); the selection forms the aggregated score",
+                     "GQA score phase (gqa_prep_kernel, gqa_mfma_kernel; f32 K: gqa_score_kernel); "
+                     "the selection forms the statistics and the aggregated score",
                      "achieved": score_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": score_gbs / HBM_PEAK_GBS,
                      "traffic": load_traffic(spec),
