@@ -434,7 +434,17 @@ struct GqaKeys {
         }
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc((void*)raw, 0, n * G * 4, kBufferWord3);
-        constexpr int kRows = G <= 4 ? 8 : 4;     // rows in flight per lane
+        // Rows in flight per lane.  With G <= 4 each group's loads are pinned
+        // ahead of its arithmetic by scheduling barriers (with more query
+        // heads they would push the kernel into spills).  Left alone, the
+        // compiler merges a row's G loads into one and interleaves them with
+        // the fp64 work, keeping only 1-4 rows in flight, so a head alone on
+        // a compute unit (the second round of a launch with more heads than
+        // compute units) paid about ten memory round trips for its 32 rows
+        // per lane.  Measured on the 288-head GQA cache (G = 4): 66.6 us
+        // against 69.8 us; 8 rows per group 67.0 us, two groups of 8 in turn
+        // 68.0 us.
+        constexpr int kRows = G <= 4 ? (KPT % 16 == 0 ? 16 : 8) : 4;
         static_assert(KPT % kRows == 0, "whole groups of rows");
 #pragma unroll
         for (int c0 = 0; c0 < KPT; c0 += kRows) {
@@ -445,6 +455,7 @@ struct GqaKeys {
                 for (int g = 0; g < G; ++g)
                     x[c][g] = __builtin_amdgcn_raw_buffer_load_b32(
                         rsrc, ((seg0 + 64 * (c0 + c)) * G + g) * 4, 0, 0);
+            if constexpr (G <= 4) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int c = 0; c < kRows; ++c) {
                 double best = __longlong_as_double(0x7FF8000000000000ll);   // NaN
@@ -459,6 +470,7 @@ struct GqaKeys {
                 key[c0 + c] = ordered_key((float)best) &
                               (0u - (seg0 + 64 * (c0 + c) < n ? 1u : 0u));
             }
+            if constexpr (G <= 4) __builtin_amdgcn_sched_barrier(0);
         }
     }
 };
