@@ -531,3 +531,6 @@ def prune_step_shared(ctx: Context, seqs: List[Seq], budget: int, floor: int, wi
                       select_workspace, stream)
     tri_compact_kv_counts(ctx, seqs, kept, int(budget) * ctx.n_kv_heads, kept_count,
                           compact_workspace, stream)
+
+
+from rope_aware_eviction_amd.calib_file import load_calibration, save_calibration  # noqa: E402,F401 (host-side file I/O)

@@ -100,3 +100,25 @@ def test_calib_stats_random_shapes(orc, case):
     say("calibration statistics, random", case, dtype, d, n, H)
     q, _, _ = synth.query_samples(H, d, n, seed=6000 + case, dtype=dtype, device="cuda")
     _stats_vs_oracle(orc, q, range(H))
+
+
+def test_context_from_a_saved_table_scores_identically(tmp_path):
+    """A calibration table written to disk and read back gives a context whose
+    scores equal, bit for bit, those of the context loaded from the arrays."""
+    spec = synth.workload("llama8b").replace(n_layers=2, n_kv_heads=2, lengths=(3000,))
+    cache = synth.make_cache(spec, "cuda", seed=11)
+    c = cache.calib
+    ctx_a = tri.tri_calibrate_load(2, 2, 128, c.qc_re, c.qc_im, c.q_mean_norm, c.q_mrl, c.offsets,
+                                   rope_theta=c.rope_theta, device=0)
+    path = tmp_path / "calib.npz"
+    tri.save_calibration(path, c.qc_re, c.qc_im, c.q_mean_norm, c.q_mrl, c.offsets, n_kv_heads=2,
+                         head_dim=128, rope_theta=c.rope_theta)
+    ctx_b = tri.tri_calibrate_load(**tri.load_calibration(path), device=0)
+    n = 2 * 2 * 3000
+    sa = torch.empty(n, device="cuda")
+    sb = torch.empty(n, device="cuda")
+    tri.tri_score(ctx_a, seqs_for(cache), sa)
+    tri.tri_score(ctx_b, seqs_for(cache), sb)
+    torch.cuda.synchronize()
+    say("saved calibration table: %d scores compared" % n)
+    assert torch.equal(sa, sb)
